@@ -1,0 +1,219 @@
+/*
+ * bi.h -- batch-invariant inference kernels for AMD Instinct MI355X (gfx950).
+ *
+ * A batch-invariant kernel gives each output row the same bits whatever the
+ * batch size M, whatever the other rows hold, and on every run: the
+ * floating-point reduction behind each output element runs in one fixed
+ * order that depends only on the shape of the row (N, K, head_dim, the
+ * sequence's own length), never on M or on the batch composition.
+ *
+ * The operations are those the pages name:
+ *   - mm, addmm, log_softmax, mean: the ops listed as supported by
+ *     "thinking-machines-lab/batch_invariant_ops" (catalogue page, section
+ *     "When to avoid"), which replaces standard PyTorch kernels ("What it
+ *     is"), so each op keeps PyTorch's semantics;
+ *   - RMSNorm and attention: named with matmul as the inference kernels whose
+ *     output depends on batch size (readhandoff.com, agent-run
+ *     reproducibility pinning, section "What does temperature zero actually
+ *     guarantee?", and its "Frequently asked questions");
+ *   - greedy argmax: the temperature-0 sampler picks the highest-probability
+ *     token (same section).
+ * The mechanism, fixing the reduction order, is the "TL;DR" of "How to
+ * achieve deterministic LLMs with batch invariant inference". The pages give
+ * no signatures; the ones below are this library's own.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller. The
+ *    library never allocates, frees, copies or synchronises device memory.
+ *    Host pointers appear only in bi_decode_plan().
+ *  - Row-major storage; ld* is the row stride in ELEMENTS (>= row length).
+ *  - bf16 is IEEE-style bfloat16 (the upper half of an fp32); bf16 outputs
+ *    are rounded to nearest, ties to even, once, from the fp32 result.
+ *  - Every call first validates all of its arguments on the host; on any
+ *    error it returns a non-zero bi_status and launches nothing, so an error
+ *    never leaves partial work. It never aborts and never throws.
+ *  - On success the work is enqueued on `stream` and the call returns before
+ *    the GPU finishes (stream-ordered, like any HIP launch). A HIP launch
+ *    error is returned as BI_ERR_HIP; the text is in bi_last_error_message().
+ *  - m == 0 (or batch == 0) is a valid no-op: BI_OK, nothing launched.
+ *  - Alignment: base pointers 16-byte aligned, ld* a multiple of 8 for bf16
+ *    and of 4 for fp32 operands (128-bit loads); otherwise BI_ERR_ALIGN.
+ *  - Outputs must not overlap inputs (undefined behaviour, not checked).
+ *  - The library keeps no mutable global state; calls are re-entrant and may
+ *    be issued from several host threads. Error messages are thread-local.
+ */
+#ifndef BI_H_
+#define BI_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BI_OK = 0,
+  BI_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  BI_ERR_SHAPE = 2,       /* a size is negative, or sizes disagree            */
+  BI_ERR_STRIDE = 3,      /* a leading dimension is smaller than its row      */
+  BI_ERR_ALIGN = 4,       /* pointer or leading dimension misaligned          */
+  BI_ERR_DTYPE = 5,       /* dtype code not accepted by this argument         */
+  BI_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required          */
+  BI_ERR_UNSUPPORTED = 7, /* valid but outside the supported set (see calls)  */
+  BI_ERR_HIP = 8          /* the HIP runtime reported an error                */
+} bi_status;
+
+typedef enum { BI_BF16 = 0, BI_F32 = 1 } bi_dtype;
+
+/* ------------------------------------------------------------------------
+ * bi_mm: C[m,n] = A[m,k] @ B, bf16 inputs, fp32 accumulation.
+ *   (mm, "thinking-machines-lab/batch_invariant_ops", "When to avoid")
+ *   a       bf16 [m, k], row stride lda.
+ *   b       bf16; b_is_nk == 0: B is [k, n] (row stride ldb, torch.mm's mat2);
+ *           b_is_nk != 0: B is stored [n, k] (row stride ldb, the nn.Linear
+ *           weight layout) and C = A @ B^T.
+ *   c       [m, n], row stride ldc, dtype c_dtype (BI_F32 or BI_BF16).
+ * Reduction order: for every C element, k runs in increasing order in
+ * 16-wide MFMA steps, accumulated in fp32, one chain per element; no split-K,
+ * stream-K or atomics. The tile configuration is chosen from (n, k, b_is_nk)
+ * only, never from m (bi_gemm_config reports it).
+ * Requirements: k % 8 == 0; with b_is_nk == 0 also n % 8 == 0
+ * (BI_ERR_UNSUPPORTED otherwise). k == 0 or n == 0 with m > 0: C is zero-filled.
+ * ------------------------------------------------------------------------ */
+bi_status bi_mm(const void* a, int64_t lda, const void* b, int64_t ldb, int b_is_nk,
+                void* c, int64_t ldc, bi_dtype c_dtype,
+                int64_t m, int64_t n, int64_t k, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * bi_addmm: C = beta * bias + alpha * (A @ B), bias [n] broadcast over rows
+ * (torch.addmm with a 1-D input; addmm, same page and section as bi_mm).
+ *   bias    [n], dtype bias_dtype (BI_BF16 or BI_F32), contiguous.
+ * The bias is applied once, after the whole K reduction, in fp32:
+ * t = alpha * acc; t = t + beta * bias[j]; then the single rounding to
+ * c_dtype. All other arguments and requirements as bi_mm.
+ * ------------------------------------------------------------------------ */
+bi_status bi_addmm(const void* bias, bi_dtype bias_dtype, float beta, float alpha,
+                   const void* a, int64_t lda, const void* b, int64_t ldb, int b_is_nk,
+                   void* c, int64_t ldc, bi_dtype c_dtype,
+                   int64_t m, int64_t n, int64_t k, hipStream_t stream);
+
+/* Tile configuration the GEMM uses for (n, k, b_is_nk): writes
+ * {tile_m, tile_n, tile_k, waves_per_workgroup} to out4. It takes no m: the
+ * configuration cannot depend on the batch size. Returns BI_ERR_NULL if
+ * out4 is NULL, BI_ERR_SHAPE for negative sizes. */
+bi_status bi_gemm_config(int64_t n, int64_t k, int b_is_nk, int32_t* out4);
+
+/* ------------------------------------------------------------------------
+ * bi_rmsnorm: y[i,j] = (x[i,j] * r_i) * w[j], r_i = 1 / sqrt(ss_i / n + eps),
+ * ss_i = sum_j x[i,j]^2 (RMSNorm; readhandoff.com "What does temperature
+ * zero actually guarantee?").
+ *   x  bf16 [m, n], row stride ldx.     w  bf16 [n], contiguous.
+ *   y  [m, n], row stride ldy, dtype y_dtype (BI_BF16 or BI_F32).
+ * One workgroup per row; ss_i is an fp32 sum in an order fixed by n alone.
+ * ------------------------------------------------------------------------ */
+bi_status bi_rmsnorm(const void* x, int64_t ldx, const void* w, float eps,
+                     void* y, int64_t ldy, bi_dtype y_dtype,
+                     int64_t m, int64_t n, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * bi_mean: y[i] = (sum_j x[i,j]) / n, fp32 sum in an order fixed by n
+ * (mean, "thinking-machines-lab/batch_invariant_ops", "When to avoid").
+ *   x  [m, n], dtype x_dtype (BI_BF16 or BI_F32), row stride ldx.
+ *   y  fp32 [m].
+ * n == 0 with m > 0 is BI_ERR_SHAPE (the mean of nothing is undefined).
+ * ------------------------------------------------------------------------ */
+bi_status bi_mean(const void* x, bi_dtype x_dtype, int64_t ldx, float* y,
+                  int64_t m, int64_t n, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * bi_log_softmax: y[i,j] = (x[i,j] - mx_i) - log(s_i), mx_i = max_j x[i,j],
+ * s_i = sum_j exp(x[i,j] - mx_i) (log_softmax, same page and section as
+ * bi_mean), plus the greedy choice argmax[i] = the lowest j with
+ * x[i,j] == mx_i (the temperature-0 sampler, readhandoff.com "What does
+ * temperature zero actually guarantee?").
+ *   x  fp32 [m, n], row stride ldx.   y  fp32 [m, n], row stride ldy.
+ *   argmax  int64 [m], or NULL to skip it.
+ * n must be > 0 (BI_ERR_SHAPE). The argmax is taken over the fp32 input
+ * logits, not over the rounded log-probabilities.
+ * ------------------------------------------------------------------------ */
+bi_status bi_log_softmax(const float* x, int64_t ldx, float* y, int64_t ldy,
+                         int64_t* argmax, int64_t m, int64_t n, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Decode attention over a paged KV cache, split-KV with a fixed split SIZE.
+ * (Attention is named as batch-dependent in readhandoff.com "What does
+ * temperature zero actually guarantee?"; batch-invariant attention kernels
+ * and the cost of the attention kernel are in "Batch-invariant inference
+ * kernels (Thinking Machines) -- Evidence & limits", sections "Evidence" and
+ * "Limitations".)
+ *
+ * For sequence b with L_b cached tokens and query head h (kv head
+ * g = h / (num_q_heads / num_kv_heads)):
+ *   out[b,h,:] = sum_t softmax_t(scale * q[b,h,:] . K[b,g,t,:]) V[b,g,t,:].
+ * The tokens of each sequence are cut at multiples of split_tokens of the
+ * sequence's own token index, so the split count ceil(L_b / split_tokens)
+ * depends on L_b only, never on the batch. Each split reduces its tokens in
+ * a fixed order to (m, l, o) partials; a second kernel merges the partials
+ * of each (b, h) in increasing split order. A sequence's output therefore has
+ * the same bits in any batch.
+ * ------------------------------------------------------------------------ */
+
+/* Host-side plan: split_offsets[b] = sum_{b'<b} ceil(L_b' / split_tokens),
+ * split_offsets[batch] = total. host_context_lens and host_split_offsets
+ * ([batch + 1]) are HOST pointers. Returns the total split count, or -1 on
+ * invalid input (NULL pointer, batch < 0, split_tokens <= 0, a length < 1);
+ * the message is in bi_last_error_message(). */
+int64_t bi_decode_plan(const int32_t* host_context_lens, int64_t batch, int split_tokens,
+                       int32_t* host_split_offsets);
+
+/* Bytes of device workspace bi_decode_attention needs for total_splits
+ * splits: total_splits * num_q_heads * (head_dim + 2) * 4 (fp32 partials
+ * o[head_dim], m, l per split and query head). Returns 0 for invalid sizes. */
+size_t bi_decode_workspace_bytes(int64_t total_splits, int num_q_heads, int head_dim);
+
+/* bi_decode_attention
+ *   q             bf16 [batch, num_q_heads, head_dim], contiguous.
+ *   k_pages,
+ *   v_pages       bf16 [num_pages, num_kv_heads, page_size, head_dim],
+ *                 contiguous; token t of sequence b is in physical page
+ *                 block_table[b * max_pages + t / page_size], slot
+ *                 t % page_size.
+ *   block_table   int32 [batch, max_pages], contiguous.
+ *   context_lens  int32 [batch], each >= 1 and <= max_pages * page_size.
+ *   split_offsets int32 [batch + 1] on the DEVICE, as written by
+ *                 bi_decode_plan for the same lengths and split_tokens.
+ *   total_splits  split_offsets[batch].
+ *   scale         multiplier of q . k (normally 1 / sqrt(head_dim)).
+ *   workspace     device buffer of at least bi_decode_workspace_bytes().
+ *   out           [batch, num_q_heads, head_dim], contiguous, out_dtype.
+ * Supported set (BI_ERR_UNSUPPORTED otherwise): head_dim == 128,
+ * page_size == 16, split_tokens == 256, num_q_heads == 4 * num_kv_heads,
+ * num_kv_heads >= 1. Device-side contents (lengths, table entries, offsets)
+ * are the caller's responsibility: the host cannot read them without a
+ * synchronisation, which this call never performs.
+ */
+bi_status bi_decode_attention(const void* q, const void* k_pages, const void* v_pages,
+                              const int32_t* block_table, int64_t max_pages,
+                              const int32_t* context_lens, const int32_t* split_offsets,
+                              int64_t total_splits, int64_t batch,
+                              int num_q_heads, int num_kv_heads, int head_dim,
+                              int page_size, int split_tokens, float scale,
+                              void* workspace, size_t workspace_bytes,
+                              void* out, bi_dtype out_dtype, hipStream_t stream);
+
+/* Static text for a status code (never NULL). */
+const char* bi_status_string(bi_status s);
+
+/* Thread-local detail of the last error raised on the calling thread
+ * (empty string if none); includes the hipError_t text for BI_ERR_HIP. */
+const char* bi_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BI_H_ */

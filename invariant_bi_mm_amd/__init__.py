@@ -1,0 +1,261 @@
+"""Python binding for libbi.so, the batch-invariant kernel library (gfx950).
+
+Argument marshalling only: every computation runs in the HIP kernels behind
+the C ABI declared in ``include/bi.h``; PyTorch supplies device memory and the
+current stream. The functions carry the C names (``bi_mm``, ``bi_addmm``,
+...). There is no fallback: if ``libbi.so`` is missing or cannot be loaded,
+importing this package raises ``ImportError``.
+
+The library links ``libamdhip64.so.7``. torch is imported first so that
+name resolves to the HIP runtime torch has already loaded (same soname):
+the ``hipStream_t`` handles torch hands out are only meaningful inside that
+runtime instance.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (must be loaded before libbi.so, see above)
+
+__all__ = [
+    "BiError", "LIB_PATH", "lib",
+    "bi_mm", "bi_addmm", "bi_gemm_config", "bi_rmsnorm", "bi_mean", "bi_log_softmax",
+    "bi_decode_plan", "bi_decode_workspace_bytes", "bi_decode_attention",
+    "bi_status_string", "bi_last_error_message",
+    "BI_BF16", "BI_F32", "STATUS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbi.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m invariant_bi_mm_amd._build` "
+        "(or __graft_entry__.build()). There is no fallback implementation.")
+lib = ctypes.CDLL(LIB_PATH)
+
+BI_BF16, BI_F32 = 0, 1
+STATUS = {0: "BI_OK", 1: "BI_ERR_NULL", 2: "BI_ERR_SHAPE", 3: "BI_ERR_STRIDE", 4: "BI_ERR_ALIGN",
+          5: "BI_ERR_DTYPE", 6: "BI_ERR_WORKSPACE", 7: "BI_ERR_UNSUPPORTED", 8: "BI_ERR_HIP"}
+
+_vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_st = ctypes.c_int
+
+lib.bi_mm.argtypes = [_vp, _i64, _vp, _i64, _i32, _vp, _i64, _i32, _i64, _i64, _i64, _vp]
+lib.bi_mm.restype = _st
+lib.bi_addmm.argtypes = [_vp, _i32, _f32, _f32, _vp, _i64, _vp, _i64, _i32, _vp, _i64, _i32, _i64, _i64, _i64, _vp]
+lib.bi_addmm.restype = _st
+lib.bi_gemm_config.argtypes = [_i64, _i64, _i32, ctypes.POINTER(ctypes.c_int32)]
+lib.bi_gemm_config.restype = _st
+lib.bi_rmsnorm.argtypes = [_vp, _i64, _vp, _f32, _vp, _i64, _i32, _i64, _i64, _vp]
+lib.bi_rmsnorm.restype = _st
+lib.bi_mean.argtypes = [_vp, _i32, _i64, _vp, _i64, _i64, _vp]
+lib.bi_mean.restype = _st
+lib.bi_log_softmax.argtypes = [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp]
+lib.bi_log_softmax.restype = _st
+lib.bi_decode_plan.argtypes = [_vp, _i64, _i32, _vp]
+lib.bi_decode_plan.restype = _i64
+lib.bi_decode_workspace_bytes.argtypes = [_i64, _i32, _i32]
+lib.bi_decode_workspace_bytes.restype = _sz
+lib.bi_decode_attention.argtypes = [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
+                                    _f32, _vp, _sz, _vp, _i32, _vp]
+lib.bi_decode_attention.restype = _st
+lib.bi_status_string.argtypes = [_st]
+lib.bi_status_string.restype = ctypes.c_char_p
+lib.bi_last_error_message.argtypes = []
+lib.bi_last_error_message.restype = ctypes.c_char_p
+
+
+class BiError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"{self.name}: {message}")
+
+
+def bi_status_string(s: int) -> str:
+    return lib.bi_status_string(s).decode()
+
+
+def bi_last_error_message() -> str:
+    return lib.bi_last_error_message().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise BiError(status, bi_last_error_message() or bi_status_string(status))
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return BI_BF16
+    if dt == torch.float32:
+        return BI_F32
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _mat(t: torch.Tensor, name: str):
+    """(tensor, leading dimension) for a row-major 2-D operand."""
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.stride(1) != 1 and t.size(1) > 1:
+        raise ValueError(f"{name} must have unit stride along its rows")
+    if t.size(0) > 1:
+        return t, t.stride(0)
+    # a single row: the stride is never used for addressing
+    return t, ((t.size(1) + 7) // 8) * 8
+
+
+def _need_bf16(t, name):
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16")
+
+
+def _gemm_shapes(a, b, b_is_nk):
+    _need_bf16(a, "a")
+    _need_bf16(b, "b")
+    m, k = a.shape
+    n = b.shape[0] if b_is_nk else b.shape[1]
+    kb = b.shape[1] if b_is_nk else b.shape[0]
+    if kb != k:
+        raise ValueError(f"inner dimensions differ: a is {tuple(a.shape)}, b is {tuple(b.shape)} (b_is_nk={b_is_nk})")
+    return m, n, k
+
+
+def bi_mm(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None, *, b_is_nk: bool = False,
+          out_dtype: torch.dtype = torch.float32, stream=None) -> torch.Tensor:
+    """C = a @ b (b [K, N]) or a @ b.T (b [N, K], b_is_nk=True); bf16 in, fp32 accumulate."""
+    m, n, k = _gemm_shapes(a, b, b_is_nk)
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    a, lda = _mat(a, "a")
+    b, ldb = _mat(b, "b")
+    out, ldc = _mat(out, "out")
+    _check(lib.bi_mm(_ptr(a), lda, _ptr(b), ldb, int(b_is_nk), _ptr(out), ldc, _dtype_code(out.dtype),
+                     m, n, k, _stream(stream)))
+    return out
+
+
+def bi_addmm(bias: torch.Tensor, a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None, *,
+             beta: float = 1.0, alpha: float = 1.0, b_is_nk: bool = False,
+             out_dtype: torch.dtype = torch.float32, stream=None) -> torch.Tensor:
+    """C = beta * bias[None, :] + alpha * (a @ b), bias applied after the full K reduction."""
+    m, n, k = _gemm_shapes(a, b, b_is_nk)
+    if bias.dim() != 1 or bias.shape[0] != n or not bias.is_contiguous():
+        raise ValueError("bias must be a contiguous [N] vector")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    a, lda = _mat(a, "a")
+    b, ldb = _mat(b, "b")
+    out, ldc = _mat(out, "out")
+    _check(lib.bi_addmm(_ptr(bias), _dtype_code(bias.dtype), float(beta), float(alpha), _ptr(a), lda, _ptr(b), ldb,
+                        int(b_is_nk), _ptr(out), ldc, _dtype_code(out.dtype), m, n, k, _stream(stream)))
+    return out
+
+
+def bi_gemm_config(n: int, k: int, b_is_nk: bool = False) -> tuple:
+    """(tile_m, tile_n, tile_k, waves) the GEMM uses for (n, k, layout); m is not an input."""
+    out = (ctypes.c_int32 * 4)()
+    _check(lib.bi_gemm_config(n, k, int(b_is_nk), out))
+    return tuple(out)
+
+
+def bi_rmsnorm(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, out: torch.Tensor | None = None, *,
+               out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
+    """y = (x * r) * w, r = 1/sqrt(mean(x^2) + eps) per row; x bf16 [M, N], w bf16 [N]."""
+    _need_bf16(x, "x")
+    _need_bf16(w, "w")
+    m, n = x.shape
+    if w.dim() != 1 or w.shape[0] != n or not w.is_contiguous():
+        raise ValueError("w must be a contiguous [N] vector")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    x, ldx = _mat(x, "x")
+    out, ldy = _mat(out, "out")
+    _check(lib.bi_rmsnorm(_ptr(x), ldx, _ptr(w), float(eps), _ptr(out), ldy, _dtype_code(out.dtype), m, n,
+                          _stream(stream)))
+    return out
+
+
+def bi_mean(x: torch.Tensor, out: torch.Tensor | None = None, *, stream=None) -> torch.Tensor:
+    """y[i] = mean_j x[i, j] in fp32; x bf16 or fp32 [M, N]."""
+    m, n = x.shape
+    if out is None:
+        out = torch.empty((m,), dtype=torch.float32, device=x.device)
+    x, ldx = _mat(x, "x")
+    _check(lib.bi_mean(_ptr(x), _dtype_code(x.dtype), ldx, _ptr(out), m, n, _stream(stream)))
+    return out
+
+
+def bi_log_softmax(x: torch.Tensor, out: torch.Tensor | None = None, argmax: torch.Tensor | None = None, *,
+                   want_argmax: bool = True, stream=None):
+    """(log_softmax(x) [M, N] fp32, argmax [M] int64 or None) over fp32 logits."""
+    if x.dtype != torch.float32:
+        raise TypeError("x must be float32")
+    m, n = x.shape
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    if want_argmax and argmax is None:
+        argmax = torch.empty((m,), dtype=torch.int64, device=x.device)
+    x, ldx = _mat(x, "x")
+    out, ldy = _mat(out, "out")
+    _check(lib.bi_log_softmax(_ptr(x), ldx, _ptr(out), ldy, _ptr(argmax if want_argmax else None), m, n,
+                              _stream(stream)))
+    return out, (argmax if want_argmax else None)
+
+
+def bi_decode_plan(context_lens_host: torch.Tensor, split_tokens: int = 256):
+    """Host plan: (split_offsets int32 [B+1] on the host, total splits)."""
+    lens = context_lens_host.to(torch.int32).contiguous().cpu()
+    offs = torch.empty(lens.numel() + 1, dtype=torch.int32)
+    total = lib.bi_decode_plan(_ptr(lens), lens.numel(), int(split_tokens), _ptr(offs))
+    if total < 0:
+        raise BiError(2, bi_last_error_message())
+    return offs, int(total)
+
+
+def bi_decode_workspace_bytes(total_splits: int, num_q_heads: int, head_dim: int) -> int:
+    return int(lib.bi_decode_workspace_bytes(total_splits, num_q_heads, head_dim))
+
+
+def bi_decode_attention(q, k_pages, v_pages, block_table, context_lens, split_offsets, total_splits: int, *,
+                        scale: float | None = None, split_tokens: int = 256, workspace=None, out=None,
+                        out_dtype: torch.dtype = torch.float32, stream=None):
+    """Split-KV decode attention over a paged cache.
+
+    q [B, Hq, D] bf16; k_pages/v_pages [P, Hkv, page, D] bf16; block_table
+    [B, max_pages] int32; context_lens [B] int32 and split_offsets [B+1]
+    int32 on the device (split_offsets from bi_decode_plan)."""
+    _need_bf16(q, "q")
+    _need_bf16(k_pages, "k_pages")
+    _need_bf16(v_pages, "v_pages")
+    bsz, hq, d = q.shape
+    _, hkv, page, d2 = k_pages.shape
+    if d2 != d or v_pages.shape != k_pages.shape:
+        raise ValueError("q/k/v shapes disagree")
+    for t, nm in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (block_table, "block_table"),
+                  (context_lens, "context_lens"), (split_offsets, "split_offsets")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32 or split_offsets.dtype != torch.int32:
+        raise TypeError("block_table, context_lens, split_offsets must be int32")
+    if scale is None:
+        scale = d ** -0.5
+    need = bi_decode_workspace_bytes(total_splits, hq, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((bsz, hq, d), dtype=out_dtype, device=q.device)
+    _check(lib.bi_decode_attention(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), block_table.shape[1],
+                                   _ptr(context_lens), _ptr(split_offsets), int(total_splits), bsz, hq, hkv, d,
+                                   page, int(split_tokens), float(scale), _ptr(workspace), workspace.numel(),
+                                   _ptr(out), _dtype_code(out.dtype), _stream(stream)))
+    return out

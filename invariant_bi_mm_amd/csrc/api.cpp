@@ -1,0 +1,267 @@
+// C-ABI entry points (include/bi.h): argument validation, then dispatch to
+// the HIP launchers. Every check runs on the host before any HIP call, so a
+// rejected call has launched nothing. No exceptions cross this boundary.
+#include "bi.h"
+
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "bi_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bi_status fail(bi_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+bi_status ok() {
+  g_last_error.clear();
+  return BI_OK;
+}
+
+bi_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(BI_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool valid_dtype(bi_dtype d) { return d == BI_BF16 || d == BI_F32; }
+size_t dsize(bi_dtype d) { return d == BI_BF16 ? 2 : 4; }
+
+bi_status check_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, int b_is_nk, void* c,
+                     int64_t ldc, bi_dtype c_dtype, int64_t m, int64_t n, int64_t k) {
+  if (m < 0 || n < 0 || k < 0) return fail(BI_ERR_SHAPE, "negative size (m=%lld n=%lld k=%lld)", (long long)m, (long long)n, (long long)k);
+  if (!valid_dtype(c_dtype)) return fail(BI_ERR_DTYPE, "c_dtype %d is not BI_BF16 or BI_F32", (int)c_dtype);
+  if (m == 0 || n == 0) return BI_OK;
+  if (c == nullptr) return fail(BI_ERR_NULL, "c is NULL");
+  if (k > 0 && (a == nullptr || b == nullptr)) return fail(BI_ERR_NULL, "a or b is NULL");
+  if (m > INT_MAX || n > INT_MAX || k > INT_MAX) return fail(BI_ERR_UNSUPPORTED, "a size exceeds 2^31-1");
+  if (lda < k || ldc < n || ldb < (b_is_nk ? k : n))
+    return fail(BI_ERR_STRIDE, "leading dimension smaller than its row (lda=%lld ldb=%lld ldc=%lld)",
+                (long long)lda, (long long)ldb, (long long)ldc);
+  if (k % 8 != 0) return fail(BI_ERR_UNSUPPORTED, "k=%lld is not a multiple of 8", (long long)k);
+  if (!b_is_nk && n % 8 != 0)
+    return fail(BI_ERR_UNSUPPORTED, "n=%lld is not a multiple of 8 (B stored [k, n])", (long long)n);
+  if (k > 0 && (!aligned(a, 16) || !aligned(b, 16) || lda % 8 != 0 || ldb % 8 != 0))
+    return fail(BI_ERR_ALIGN, "a/b must be 16-byte aligned with lda, ldb multiples of 8");
+  if (!aligned(c, dsize(c_dtype))) return fail(BI_ERR_ALIGN, "c is not aligned to its element size");
+  const bi::GemmConfig cfg = bi::gemm_config(n, k, b_is_nk != 0);
+  const int64_t tiles = ((m + cfg.tile_m - 1) / cfg.tile_m) * ((n + cfg.tile_n - 1) / cfg.tile_n);
+  if (tiles > INT_MAX) return fail(BI_ERR_UNSUPPORTED, "too many output tiles");
+  return BI_OK;
+}
+
+bi_status run_gemm(const void* bias, bi_dtype bias_dtype, float beta, float alpha, const void* a, int64_t lda,
+                   const void* b, int64_t ldb, int b_is_nk, void* c, int64_t ldc, bi_dtype c_dtype, int64_t m,
+                   int64_t n, int64_t k, hipStream_t stream) {
+  bi::GemmParams p;
+  p.a = a;
+  p.b = b;
+  p.c = c;
+  p.bias = bias;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldc = ldc;
+  p.m = m;
+  p.n = n;
+  p.k = k;
+  p.alpha = alpha;
+  p.beta = beta;
+  p.b_is_nk = b_is_nk != 0;
+  p.c_bf16 = c_dtype == BI_BF16;
+  p.bias_bf16 = bias_dtype == BI_BF16;
+  return hip_status(bi::launch_gemm(p, stream), "gemm launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+bi_status bi_mm(const void* a, int64_t lda, const void* b, int64_t ldb, int b_is_nk, void* c, int64_t ldc,
+                bi_dtype c_dtype, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
+  bi_status st = check_gemm(a, lda, b, ldb, b_is_nk, c, ldc, c_dtype, m, n, k);
+  if (st != BI_OK) return st;
+  if (m == 0 || n == 0) return ok();
+  return run_gemm(nullptr, BI_F32, 0.0f, 1.0f, a, lda, b, ldb, b_is_nk, c, ldc, c_dtype, m, n, k, stream);
+}
+
+bi_status bi_addmm(const void* bias, bi_dtype bias_dtype, float beta, float alpha, const void* a, int64_t lda,
+                   const void* b, int64_t ldb, int b_is_nk, void* c, int64_t ldc, bi_dtype c_dtype, int64_t m,
+                   int64_t n, int64_t k, hipStream_t stream) {
+  if (!valid_dtype(bias_dtype)) return fail(BI_ERR_DTYPE, "bias_dtype %d is not BI_BF16 or BI_F32", (int)bias_dtype);
+  bi_status st = check_gemm(a, lda, b, ldb, b_is_nk, c, ldc, c_dtype, m, n, k);
+  if (st != BI_OK) return st;
+  if (m == 0 || n == 0) return ok();
+  if (bias == nullptr) return fail(BI_ERR_NULL, "bias is NULL");
+  if (!aligned(bias, dsize(bias_dtype))) return fail(BI_ERR_ALIGN, "bias is not aligned to its element size");
+  return run_gemm(bias, bias_dtype, beta, alpha, a, lda, b, ldb, b_is_nk, c, ldc, c_dtype, m, n, k, stream);
+}
+
+bi_status bi_gemm_config(int64_t n, int64_t k, int b_is_nk, int32_t* out4) {
+  if (out4 == nullptr) return fail(BI_ERR_NULL, "out4 is NULL");
+  if (n < 0 || k < 0) return fail(BI_ERR_SHAPE, "negative size");
+  const bi::GemmConfig c = bi::gemm_config(n, k, b_is_nk != 0);
+  out4[0] = c.tile_m;
+  out4[1] = c.tile_n;
+  out4[2] = c.tile_k;
+  out4[3] = c.waves;
+  return ok();
+}
+
+bi_status bi_rmsnorm(const void* x, int64_t ldx, const void* w, float eps, void* y, int64_t ldy, bi_dtype y_dtype,
+                     int64_t m, int64_t n, hipStream_t stream) {
+  if (m < 0 || n < 0) return fail(BI_ERR_SHAPE, "negative size");
+  if (!valid_dtype(y_dtype)) return fail(BI_ERR_DTYPE, "y_dtype %d is not BI_BF16 or BI_F32", (int)y_dtype);
+  if (m == 0) return ok();
+  if (n == 0) return fail(BI_ERR_SHAPE, "n == 0: RMSNorm of an empty row is undefined");
+  if (x == nullptr || w == nullptr || y == nullptr) return fail(BI_ERR_NULL, "x, w or y is NULL");
+  if (m > INT_MAX || n > INT_MAX) return fail(BI_ERR_UNSUPPORTED, "a size exceeds 2^31-1");
+  if (ldx < n || ldy < n) return fail(BI_ERR_STRIDE, "ldx/ldy smaller than n");
+  const int64_t yq = y_dtype == BI_BF16 ? 8 : 4;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16) || ldx % 8 != 0 || ldy % yq != 0)
+    return fail(BI_ERR_ALIGN, "x, w, y must be 16-byte aligned; ldx a multiple of 8, ldy of %lld", (long long)yq);
+  return hip_status(bi::launch_rmsnorm(x, ldx, w, eps, y, ldy, y_dtype == BI_BF16, m, n, stream), "rmsnorm launch");
+}
+
+bi_status bi_mean(const void* x, bi_dtype x_dtype, int64_t ldx, float* y, int64_t m, int64_t n,
+                  hipStream_t stream) {
+  if (m < 0 || n < 0) return fail(BI_ERR_SHAPE, "negative size");
+  if (!valid_dtype(x_dtype)) return fail(BI_ERR_DTYPE, "x_dtype %d is not BI_BF16 or BI_F32", (int)x_dtype);
+  if (m == 0) return ok();
+  if (n == 0) return fail(BI_ERR_SHAPE, "n == 0: the mean of an empty row is undefined");
+  if (x == nullptr || y == nullptr) return fail(BI_ERR_NULL, "x or y is NULL");
+  if (m > INT_MAX || n > INT_MAX) return fail(BI_ERR_UNSUPPORTED, "a size exceeds 2^31-1");
+  if (ldx < n) return fail(BI_ERR_STRIDE, "ldx smaller than n");
+  const int64_t xq = x_dtype == BI_BF16 ? 8 : 4;
+  if (!aligned(x, 16) || ldx % xq != 0 || !aligned(y, 4))
+    return fail(BI_ERR_ALIGN, "x must be 16-byte aligned with ldx a multiple of %lld; y 4-byte aligned",
+                (long long)xq);
+  return hip_status(bi::launch_mean(x, x_dtype == BI_BF16, ldx, y, m, n, stream), "mean launch");
+}
+
+bi_status bi_log_softmax(const float* x, int64_t ldx, float* y, int64_t ldy, int64_t* argmax, int64_t m, int64_t n,
+                         hipStream_t stream) {
+  if (m < 0 || n < 0) return fail(BI_ERR_SHAPE, "negative size");
+  if (m == 0) return ok();
+  if (n == 0) return fail(BI_ERR_SHAPE, "n == 0: log_softmax of an empty row is undefined");
+  if (x == nullptr || y == nullptr) return fail(BI_ERR_NULL, "x or y is NULL");
+  if (m > INT_MAX || n > INT_MAX / 4) return fail(BI_ERR_UNSUPPORTED, "a size exceeds the supported range");
+  if (ldx < n || ldy < n) return fail(BI_ERR_STRIDE, "ldx/ldy smaller than n");
+  if (!aligned(x, 16) || !aligned(y, 16) || ldx % 4 != 0 || ldy % 4 != 0 || !aligned(argmax, 8))
+    return fail(BI_ERR_ALIGN, "x, y must be 16-byte aligned with ldx, ldy multiples of 4; argmax 8-byte aligned");
+  return hip_status(bi::launch_log_softmax(x, ldx, y, ldy, argmax, m, n, stream), "log_softmax launch");
+}
+
+int64_t bi_decode_plan(const int32_t* host_context_lens, int64_t batch, int split_tokens,
+                       int32_t* host_split_offsets) {
+  if (batch < 0 || split_tokens <= 0) {
+    fail(BI_ERR_SHAPE, "batch < 0 or split_tokens <= 0");
+    return -1;
+  }
+  if (host_split_offsets == nullptr || (batch > 0 && host_context_lens == nullptr)) {
+    fail(BI_ERR_NULL, "NULL host pointer");
+    return -1;
+  }
+  int64_t total = 0;
+  for (int64_t b = 0; b < batch; ++b) {
+    const int64_t L = host_context_lens[b];
+    if (L < 1) {
+      fail(BI_ERR_SHAPE, "context_lens[%lld] = %lld < 1", (long long)b, (long long)L);
+      return -1;
+    }
+    host_split_offsets[b] = (int32_t)total;
+    total += (L + split_tokens - 1) / split_tokens;
+    if (total > INT_MAX) {
+      fail(BI_ERR_UNSUPPORTED, "total split count exceeds 2^31-1");
+      return -1;
+    }
+  }
+  host_split_offsets[batch] = (int32_t)total;
+  ok();
+  return total;
+}
+
+size_t bi_decode_workspace_bytes(int64_t total_splits, int num_q_heads, int head_dim) {
+  if (total_splits < 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  return (size_t)total_splits * (size_t)num_q_heads * (size_t)(head_dim + 2) * sizeof(float);
+}
+
+bi_status bi_decode_attention(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                              int64_t max_pages, const int32_t* context_lens, const int32_t* split_offsets,
+                              int64_t total_splits, int64_t batch, int num_q_heads, int num_kv_heads, int head_dim,
+                              int page_size, int split_tokens, float scale, void* workspace, size_t workspace_bytes,
+                              void* out, bi_dtype out_dtype, hipStream_t stream) {
+  if (batch < 0 || total_splits < 0 || max_pages < 0) return fail(BI_ERR_SHAPE, "negative size");
+  if (!valid_dtype(out_dtype)) return fail(BI_ERR_DTYPE, "out_dtype %d is not BI_BF16 or BI_F32", (int)out_dtype);
+  if (head_dim != 128 || page_size != 16 || split_tokens != 256 || num_kv_heads < 1 ||
+      num_q_heads != 4 * num_kv_heads)
+    return fail(BI_ERR_UNSUPPORTED,
+                "supported: head_dim 128, page_size 16, split_tokens 256, num_q_heads = 4 * num_kv_heads "
+                "(got %d, %d, %d, %d/%d)",
+                head_dim, page_size, split_tokens, num_q_heads, num_kv_heads);
+  if (batch == 0) return ok();
+  if (q == nullptr || k_pages == nullptr || v_pages == nullptr || block_table == nullptr ||
+      context_lens == nullptr || split_offsets == nullptr || out == nullptr)
+    return fail(BI_ERR_NULL, "a required pointer is NULL");
+  if (max_pages < 1) return fail(BI_ERR_SHAPE, "max_pages must be >= 1");
+  const int64_t max_splits_per_seq = (max_pages * page_size + split_tokens - 1) / split_tokens;
+  if (total_splits < batch || total_splits > batch * max_splits_per_seq)
+    return fail(BI_ERR_SHAPE, "total_splits=%lld inconsistent with batch=%lld and max_pages=%lld",
+                (long long)total_splits, (long long)batch, (long long)max_pages);
+  if (total_splits > INT_MAX || batch > INT_MAX || num_kv_heads > 65535 || num_q_heads > 65535)
+    return fail(BI_ERR_UNSUPPORTED, "grid size out of range");
+  const size_t need = bi_decode_workspace_bytes(total_splits, num_q_heads, head_dim);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(BI_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(workspace, 16) ||
+      !aligned(out, dsize(out_dtype)) || !aligned(block_table, 4) || !aligned(context_lens, 4) ||
+      !aligned(split_offsets, 4))
+    return fail(BI_ERR_ALIGN, "q, k_pages, v_pages, workspace must be 16-byte aligned");
+  bi::DecodeParams p;
+  p.q = q;
+  p.k_pages = k_pages;
+  p.v_pages = v_pages;
+  p.block_table = block_table;
+  p.context_lens = context_lens;
+  p.split_offsets = split_offsets;
+  p.max_pages = max_pages;
+  p.total_splits = total_splits;
+  p.batch = batch;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.scale = scale;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_ml = p.ws_o + total_splits * num_q_heads * head_dim;
+  p.out = out;
+  p.out_bf16 = out_dtype == BI_BF16;
+  return hip_status(bi::launch_decode_attention(p, stream), "decode attention launch");
+}
+
+const char* bi_status_string(bi_status s) {
+  switch (s) {
+    case BI_OK: return "BI_OK";
+    case BI_ERR_NULL: return "BI_ERR_NULL: a required pointer is NULL";
+    case BI_ERR_SHAPE: return "BI_ERR_SHAPE: invalid or inconsistent sizes";
+    case BI_ERR_STRIDE: return "BI_ERR_STRIDE: leading dimension smaller than the row";
+    case BI_ERR_ALIGN: return "BI_ERR_ALIGN: pointer or leading dimension misaligned";
+    case BI_ERR_DTYPE: return "BI_ERR_DTYPE: dtype not accepted";
+    case BI_ERR_WORKSPACE: return "BI_ERR_WORKSPACE: workspace missing or too small";
+    case BI_ERR_UNSUPPORTED: return "BI_ERR_UNSUPPORTED: outside the supported set";
+    case BI_ERR_HIP: return "BI_ERR_HIP: HIP runtime error";
+  }
+  return "unknown bi_status";
+}
+
+const char* bi_last_error_message(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

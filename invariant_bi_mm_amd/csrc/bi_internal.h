@@ -1,0 +1,59 @@
+// Internal launcher interface between the host API (api.cpp) and the HIP
+// translation units. Arguments arrive here already validated.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace bi {
+
+struct GemmConfig {
+  int tile_m, tile_n, tile_k, waves;
+};
+
+// Tile configuration for (n, k, layout): a pure function of those three.
+GemmConfig gemm_config(int64_t n, int64_t k, bool b_is_nk);
+
+struct GemmParams {
+  const void* a;
+  const void* b;
+  void* c;
+  const void* bias;  // nullptr for mm
+  int64_t lda, ldb, ldc;
+  int64_t m, n, k;
+  float alpha, beta;
+  bool b_is_nk;
+  bool c_bf16;
+  bool bias_bf16;
+};
+hipError_t launch_gemm(const GemmParams& p, hipStream_t stream);
+
+hipError_t launch_rmsnorm(const void* x, int64_t ldx, const void* w, float eps, void* y,
+                          int64_t ldy, bool y_bf16, int64_t m, int64_t n, hipStream_t stream);
+hipError_t launch_mean(const void* x, bool x_bf16, int64_t ldx, float* y, int64_t m, int64_t n,
+                       hipStream_t stream);
+hipError_t launch_log_softmax(const float* x, int64_t ldx, float* y, int64_t ldy, int64_t* argmax,
+                              int64_t m, int64_t n, hipStream_t stream);
+
+struct DecodeParams {
+  const void* q;
+  const void* k_pages;
+  const void* v_pages;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  const int32_t* split_offsets;
+  int64_t max_pages;
+  int64_t total_splits;
+  int64_t batch;
+  int num_q_heads, num_kv_heads;
+  float scale;
+  float* ws_o;   // [total_splits, num_q_heads, 128]
+  float* ws_ml;  // [total_splits, num_q_heads, 2]
+  void* out;
+  bool out_bf16;
+};
+hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t stream);
+
+}  // namespace bi

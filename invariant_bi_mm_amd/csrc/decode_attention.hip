@@ -1,0 +1,260 @@
+// Batch-invariant split-KV decode attention over a paged bf16 KV cache, gfx950.
+//
+// Attention is one of the inference kernels named as batch-dependent in
+// readhandoff.com's agent-run reproducibility pinning ("What does temperature
+// zero actually guarantee?"); SGLang wrote its own batch-invariant attention
+// and an improved attention kernel recovered much of the cost ("Batch-
+// invariant inference kernels (Thinking Machines) -- Evidence & limits",
+// sections "Evidence" and "Limitations").
+//
+// Invariance: a sequence's keys are cut at fixed multiples of SPLIT of its own
+// token index, so which tokens form split s, and how many splits there are,
+// depends on the sequence's length alone -- never on the batch, on the other
+// sequences or on the occupancy of the GPU. Each split is reduced by one
+// workgroup in a fixed order; the combine kernel merges the splits of one
+// (sequence, head) in increasing split order. The position of the sequence in
+// the batch only changes WHICH workgroup does the work.
+//
+// Kernel 1, one workgroup per (split, kv head), 256 threads = 16 groups of 16
+// lanes; lane dl of a group owns head-dim slice [8*dl, 8*dl + 8).
+//   phase 1: group i handles slot i of each of the split's (<= 16) pages: the
+//            16 groups read one 4 KB head-page together. Scores for the GQA
+//            query heads sharing this kv head are 8-term fixed-order dots
+//            plus a 16-lane butterfly, kept in LDS (log2 domain: q is
+//            pre-multiplied by scale * log2(e)).
+//   phase 2: wave h (one per query head) takes the exact max over the split,
+//            writes p = 2^(s - max) back and sums it (per-lane fixed order,
+//            then butterfly).
+//   phase 3: o = sum_t p_t v_t with the same token->group assignment, groups
+//            merged by butterfly inside a wave, waves merged in wave order.
+//   output : (max, sum p, o[128]) per (split, query head), fp32.
+// Kernel 2, one workgroup per (sequence, query head), lane d:
+//   M = max_s m_s; l = sum_s 2^(m_s - M) l_s; o = sum_s 2^(m_s - M) o_s[d] in
+//   increasing s; out = o / l.
+#include "bi_internal.h"
+#include "device_common.h"
+
+namespace bi {
+namespace {
+
+constexpr int HD = 128;     // head dim
+constexpr int PAGE = 16;    // tokens per page
+constexpr int SPLIT = 256;  // tokens per split
+constexpr int GQA = 4;      // query heads per kv head
+constexpr int PPS = SPLIT / PAGE;
+constexpr float LOG2E = 1.4426950408889634f;
+
+struct SplitArgs {
+  const uint16_t* q;
+  const uint16_t* kp;
+  const uint16_t* vp;
+  const int32_t* bt;
+  const int32_t* lens;
+  const int32_t* offs;
+  int64_t max_pages;
+  int batch;
+  int hq, hkv;
+  float qscale;
+  float* ws_o;
+  float* ws_ml;
+};
+
+__global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
+  __shared__ float S[GQA][SPLIT];
+  __shared__ float O[4][GQA][HD];
+  __shared__ float ML[GQA][2];
+
+  const int w = blockIdx.x;  // global split index
+  const int g = blockIdx.y;  // kv head
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int grp = tid >> 4;  // 0..15
+  const int dl = tid & 15;   // head-dim slice
+
+  // sequence owning split w: the largest b with offs[b] <= w
+  int lo = 0, hi = a.batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.offs[mid] <= w) lo = mid; else hi = mid - 1;
+  }
+  const int b = lo;
+  const int s = w - a.offs[b];
+  const int L = a.lens[b];
+  const int t0 = s * SPLIT;
+  const int nt = min(SPLIT, L - t0);
+  const int32_t* bt = a.bt + (int64_t)b * a.max_pages + t0 / PAGE;
+
+  float qf[GQA][8];
+#pragma unroll
+  for (int h = 0; h < GQA; ++h) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * a.hq + g * GQA + h) * HD + dl * 8);
+    unpack8(v, qf[h]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[h][e] = qf[h][e] * a.qscale;
+  }
+
+  const int64_t head_stride = (int64_t)PAGE * HD;           // one head-page
+  const int64_t page_stride = (int64_t)a.hkv * head_stride;  // one physical page
+  const int64_t slot_off = (int64_t)g * head_stride + (int64_t)grp * HD + dl * 8;
+
+  // ---- phase 1: scores
+  u32x4 kv[PPS];
+#pragma unroll
+  for (int j = 0; j < PPS; ++j) {
+    kv[j] = u32x4{0u, 0u, 0u, 0u};
+    if (j * PAGE + grp < nt) {
+      const int64_t page = bt[j];
+      kv[j] = *reinterpret_cast<const u32x4*>(a.kp + page * page_stride + slot_off);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < PPS; ++j) {
+    const int i = j * PAGE + grp;
+    float kf[8];
+    unpack8(kv[j], kf);
+    float dot[GQA];
+#pragma unroll
+    for (int h = 0; h < GQA; ++h) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(qf[h][e], kf[e], acc);
+      dot[h] = group16_sum(acc);
+    }
+    if (dl < GQA) S[dl][i] = (i < nt) ? dot[dl] : -INFINITY;
+  }
+  __syncthreads();
+
+  // ---- phase 2: per query head (wave h) max, p, sum p
+  {
+    const int h = wave;
+    float v[SPLIT / 64];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < SPLIT / 64; ++r) {
+      v[r] = S[h][lane + 64 * r];
+      mx = fmaxf(mx, v[r]);
+    }
+    mx = wave_max(mx);
+    float l = 0.0f;
+#pragma unroll
+    for (int r = 0; r < SPLIT / 64; ++r) {
+      const float p = __builtin_amdgcn_exp2f(v[r] - mx);  // 2^-inf = 0 for padded slots
+      S[h][lane + 64 * r] = p;
+      l = l + p;
+    }
+    l = wave_sum(l);
+    if (lane == 0) {
+      ML[h][0] = mx;
+      ML[h][1] = l;
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 3: o = sum p v
+#pragma unroll
+  for (int j = 0; j < PPS; ++j) {
+    kv[j] = u32x4{0u, 0u, 0u, 0u};
+    if (j * PAGE + grp < nt) {
+      const int64_t page = bt[j];
+      kv[j] = *reinterpret_cast<const u32x4*>(a.vp + page * page_stride + slot_off);
+    }
+  }
+  float o[GQA][8];
+#pragma unroll
+  for (int h = 0; h < GQA; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < PPS; ++j) {
+    const int i = j * PAGE + grp;
+    float vf[8];
+    unpack8(kv[j], vf);
+#pragma unroll
+    for (int h = 0; h < GQA; ++h) {
+      const float p = S[h][i];  // 0 for padded slots, whose v is 0 too
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] = __builtin_fmaf(p, vf[e], o[h][e]);
+    }
+  }
+  // merge the 4 groups of this wave (xor 16, then xor 32)
+#pragma unroll
+  for (int h = 0; h < GQA; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float t = o[h][e];
+      t = t + xor_shfl(t, 16);
+      t = t + xor_shfl(t, 32);
+      o[h][e] = t;
+    }
+  if (lane < 16) {
+#pragma unroll
+    for (int h = 0; h < GQA; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) O[wave][h][dl * 8 + e] = o[h][e];
+  }
+  __syncthreads();
+  // merge the 4 waves in wave order; thread handles (h, d) pairs tid, tid+256
+  const int64_t base = (int64_t)w * a.hq + g * GQA;
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int idx = tid + 256 * r;
+    const int h = idx >> 7, d = idx & (HD - 1);
+    const float t = ((O[0][h][d] + O[1][h][d]) + O[2][h][d]) + O[3][h][d];
+    a.ws_o[(base + h) * HD + d] = t;
+  }
+  if (tid < GQA) {
+    a.ws_ml[(base + tid) * 2 + 0] = ML[tid][0];
+    a.ws_ml[(base + tid) * 2 + 1] = ML[tid][1];
+  }
+}
+
+__global__ __launch_bounds__(HD) void decode_combine_kernel(const int32_t* __restrict__ offs,
+                                                             const float* __restrict__ ws_o,
+                                                             const float* __restrict__ ws_ml, int hq,
+                                                             void* __restrict__ out, int out_bf16) {
+  const int b = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+  const int w0 = offs[b], ns = offs[b + 1] - w0;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, ws_ml[((int64_t)(w0 + s) * hq + h) * 2]);
+  float l = 0.0f, o = 0.0f;
+  for (int s = 0; s < ns; ++s) {
+    const int64_t ph = (int64_t)(w0 + s) * hq + h;
+    const float c = __builtin_amdgcn_exp2f(ws_ml[ph * 2] - M);
+    l = l + c * ws_ml[ph * 2 + 1];
+    o = o + c * ws_o[ph * HD + d];
+  }
+  const float r = o / l;
+  const int64_t at = ((int64_t)b * hq + h) * HD + d;
+  if (out_bf16)
+    reinterpret_cast<uint16_t*>(out)[at] = (uint16_t)f32_to_bf16_rne(r);
+  else
+    reinterpret_cast<float*>(out)[at] = r;
+}
+
+}  // namespace
+
+hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t s) {
+  SplitArgs a;
+  a.q = static_cast<const uint16_t*>(p.q);
+  a.kp = static_cast<const uint16_t*>(p.k_pages);
+  a.vp = static_cast<const uint16_t*>(p.v_pages);
+  a.bt = p.block_table;
+  a.lens = p.context_lens;
+  a.offs = p.split_offsets;
+  a.max_pages = p.max_pages;
+  a.batch = (int)p.batch;
+  a.hq = p.num_q_heads;
+  a.hkv = p.num_kv_heads;
+  a.qscale = p.scale * LOG2E;
+  a.ws_o = p.ws_o;
+  a.ws_ml = p.ws_ml;
+  hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)p.total_splits, (unsigned)p.num_kv_heads), dim3(256), 0,
+                     s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)p.batch, (unsigned)p.num_q_heads), dim3(HD), 0, s,
+                     p.split_offsets, p.ws_o, p.ws_ml, p.num_q_heads, p.out, p.out_bf16 ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace bi

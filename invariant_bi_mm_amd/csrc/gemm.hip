@@ -1,0 +1,310 @@
+// Batch-invariant bf16 GEMM (mm / addmm) for gfx950.
+//
+// mm and addmm are two of the four ops listed as supported in
+// "thinking-machines-lab/batch_invariant_ops" (catalogue page, section "When
+// to avoid"); matmul is the first kernel named as batch-dependent in
+// readhandoff.com's agent-run reproducibility pinning, section "What does
+// temperature zero actually guarantee?". The fix is a fixed reduction order
+// ("How to achieve deterministic LLMs with batch invariant inference",
+// "TL;DR"); split-K and shape-aware tiling are the optimisations given up
+// (wiki page "Thinking Machines", section on why it is not the main answer,
+// point 3).
+//
+// What fixes the bits of C[i][j]
+//   acc = 0; for kc = 0, 16, 32, ... (increasing): acc = MFMA16(A[i][kc..kc+15],
+//   B[kc..kc+15][j], acc). One v_mfma_f32_32x32x16_bf16 step per 16 k, fp32
+//   accumulator, a single chain per element. Nothing in that chain depends on
+//   M, on the row's position, on the other rows or on the tile shape: rows
+//   past M and k past K are loaded as zeros, and every tile -- full or
+//   partial -- runs the same instruction stream. There is no split-K,
+//   stream-K or atomic anywhere.
+//
+// Structure (one workgroup per TM x TN output tile)
+//   * global -> registers: 128-bit loads of the next k-tile (TK = 64) while
+//     the current one is multiplied;
+//   * registers -> LDS: double-buffered, rows of 64 bf16 (128 bytes) made of
+//     eight 16-byte chunks whose position is XOR-swizzled by the row, so the
+//     MFMA fragment reads (ds_read_b128) and the tile writes are free of bank
+//     conflicts without padding;
+//   * B stored [K, N] (N contiguous) is transposed on its way into LDS: each
+//     thread loads a 4(k) x 8(n) block and writes eight 4(k) x 1(n) pieces,
+//     so both operands sit k-contiguous in LDS, as the MFMA wants them;
+//   * epilogue straight from the accumulators: alpha, then + beta * bias in
+//     fp32 after the full K loop, one rounding to the output dtype.
+//   * workgroup -> tile order is XCD-aware: consecutive workgroup ids land on
+//     different XCDs (round robin), so ids are remapped to give each XCD a
+//     contiguous band of tiles that share A rows / B columns in its own L2.
+//     This only permutes which workgroup computes which tile.
+#include "bi_internal.h"
+#include "device_common.h"
+
+namespace bi {
+namespace {
+
+constexpr int TK = 64;  // k per stage: 8 chunks of 8 bf16
+
+struct GemmArgs {
+  const uint16_t* a;
+  const uint16_t* b;
+  void* c;
+  const void* bias;
+  int64_t lda, ldb, ldc;
+  int m, n, k;
+  float alpha, beta;
+  int out_bf16;
+  int bias_mode;  // 0 none, 1 bf16, 2 fp32
+  int tiles_m, tiles_n;
+};
+
+// Index (in 16-byte units) of chunk `ch` of LDS row `row`.
+__device__ __forceinline__ int swz(int row, int ch) {
+  return row * 8 + (ch ^ ((row ^ (row >> 3)) & 7));
+}
+
+// Workgroup id -> (tile_m, tile_n). Bijective on [0, tiles).
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int tiles = tiles_m * tiles_n;
+  // XCD-aware: ids are dealt round-robin to 8 XCDs; give XCD x the contiguous
+  // logical range it would own in a blocked distribution.
+  const int x = bid & 7, idx = bid >> 3;
+  const int q = tiles >> 3, r = tiles & 7;
+  const int logical = x * q + (x < r ? x : r) + idx;
+  // Grouped order: bands of GM tile-rows, column-major inside a band.
+  constexpr int GM = 8;
+  const int band = logical / (GM * tiles_n);
+  const int first = band * GM;
+  const int rows = min(tiles_m - first, GM);
+  const int in = logical - band * GM * tiles_n;
+  tm = first + in % rows;
+  tn = in / rows;
+}
+
+template <int TM, int TN, int WM, int WN, bool B_NK>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int WTM = TM / WM, WTN = TN / WN;  // wave tile
+  constexpr int FM = WTM / 32, FN = WTN / 32;  // 32x32 MFMA tiles per wave
+  constexpr int A_CH = TM * 8 / NT;            // A chunks per thread
+  constexpr int B_CH = TN * 8 / NT;            // B chunks per thread ([N,K] layout)
+  constexpr int B_UN = 2 * TN / NT;            // 4x8 units per thread ([K,N] layout)
+  static_assert(A_CH * NT == TM * 8, "A tile not evenly split");
+  static_assert(B_NK ? (B_CH * NT == TN * 8) : (B_UN * NT == 2 * TN), "B tile not evenly split");
+  static_assert(FM >= 1 && FN >= 1, "wave tile smaller than one MFMA");
+
+  __shared__ u32x4 As[2][TM * 8];
+  __shared__ u32x4 Bs[2][TN * 8];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  int tm, tn;
+  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+  const int m0 = tm * TM, n0 = tn * TN;
+  const int M = g.m, N = g.n, K = g.k;
+  const int nk = (K + TK - 1) / TK;
+
+  u32x4 ra[A_CH];
+  u32x4 rb[B_NK ? B_CH : 4 * B_UN];
+
+  auto load_tile = [&](int kt) {
+    const int k0 = kt * TK;
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int c = tid + i * NT;
+      const int row = c >> 3, ch = c & 7;
+      const int gm = m0 + row, gk = k0 + ch * 8;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (gm < M && gk < K) v = *reinterpret_cast<const u32x4*>(g.a + (int64_t)gm * g.lda + gk);
+      ra[i] = v;
+    }
+    if constexpr (B_NK) {
+#pragma unroll
+      for (int i = 0; i < B_CH; ++i) {
+        const int c = tid + i * NT;
+        const int row = c >> 3, ch = c & 7;
+        const int gn = n0 + row, gk = k0 + ch * 8;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (gn < N && gk < K) v = *reinterpret_cast<const u32x4*>(g.b + (int64_t)gn * g.ldb + gk);
+        rb[i] = v;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < B_UN; ++i) {
+        const int u = tid + i * NT;
+        const int kb = ((u >> 1) / (TN / 8)) * 2 + (u & 1);
+        const int nb = (u >> 1) % (TN / 8);
+        const int gn = n0 + nb * 8;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int gk = k0 + kb * 4 + r;
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (gn < N && gk < K) v = *reinterpret_cast<const u32x4*>(g.b + (int64_t)gk * g.ldb + gn);
+          rb[i * 4 + r] = v;
+        }
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      const int c = tid + i * NT;
+      As[buf][swz(c >> 3, c & 7)] = ra[i];
+    }
+    if constexpr (B_NK) {
+#pragma unroll
+      for (int i = 0; i < B_CH; ++i) {
+        const int c = tid + i * NT;
+        Bs[buf][swz(c >> 3, c & 7)] = rb[i];
+      }
+    } else {
+      uint32_t* bs32 = reinterpret_cast<uint32_t*>(&Bs[buf][0]);
+#pragma unroll
+      for (int i = 0; i < B_UN; ++i) {
+        const int u = tid + i * NT;
+        const int kb = ((u >> 1) / (TN / 8)) * 2 + (u & 1);
+        const int nb = (u >> 1) % (TN / 8);
+        const u32x4 w0 = rb[i * 4 + 0], w1 = rb[i * 4 + 1], w2 = rb[i * 4 + 2], w3 = rb[i * 4 + 3];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = e >> 1;
+          uint32_t x0 = w0[j], x1 = w1[j], x2 = w2[j], x3 = w3[j];
+          uint32_t d0, d1;
+          if ((e & 1) == 0) {
+            d0 = (x0 & 0xffffu) | (x1 << 16);
+            d1 = (x2 & 0xffffu) | (x3 << 16);
+          } else {
+            d0 = (x0 >> 16) | (x1 & 0xffff0000u);
+            d1 = (x2 >> 16) | (x3 & 0xffff0000u);
+          }
+          const int row = nb * 8 + e;
+          // 16-byte chunk kb>>1 of the row, 8-byte half kb&1.
+          const int at = swz(row, kb >> 1) * 4 + (kb & 1) * 2;
+          *reinterpret_cast<u32x2*>(bs32 + at) = u32x2{d0, d1};
+        }
+      }
+    }
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  if (nk > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  const int arow0 = wm * WTM + (lane & 31);
+  const int brow0 = wn * WTN + (lane & 31);
+  const int khalf = lane >> 5;
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_tile(kt + 1);
+#pragma unroll
+    for (int kk = 0; kk < TK / 16; ++kk) {
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const u32x4 v = As[cur][swz(arow0 + i * 32, kk * 2 + khalf)];
+        af[i] = __builtin_bit_cast(bf16x8, v);
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const u32x4 v = Bs[cur][swz(brow0 + j * 32, kk * 2 + khalf)];
+        bfr[j] = __builtin_bit_cast(bf16x8, v);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: lane holds C[8*(r/4) + 4*(lane/32) + r%4][lane%32] of each
+  // 32x32 tile, r = 0..15.
+  const int col_in = lane & 31;
+  const int row_in = 4 * (lane >> 5);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int gn = n0 + wn * WTN + j * 32 + col_in;
+    if (gn >= N) continue;
+    float bterm = 0.0f;
+    if (g.bias_mode == 1) {
+      bterm = g.beta * __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(g.bias)[gn]) << 16);
+    } else if (g.bias_mode == 2) {
+      bterm = g.beta * reinterpret_cast<const float*>(g.bias)[gn];
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int gm = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + row_in + (r & 3);
+        if (gm >= M) continue;
+        float t = g.alpha * acc[i][j][r];
+        if (g.bias_mode != 0) t = t + bterm;
+        const int64_t off = (int64_t)gm * g.ldc + gn;
+        if (g.out_bf16)
+          reinterpret_cast<uint16_t*>(g.c)[off] = (uint16_t)f32_to_bf16_rne(t);
+        else
+          reinterpret_cast<float*>(g.c)[off] = t;
+      }
+    }
+  }
+}
+
+template <int TM, int TN, int WM, int WN, bool B_NK>
+hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
+  const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+  hipLaunchKernelGGL((gemm_kernel<TM, TN, WM, WN, B_NK>), dim3((unsigned)tiles), dim3(WM * WN * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// The configuration table. It is keyed by (n, k, layout) only; m is not an
+// input, so no batch size can select a different tile or instruction.
+GemmConfig gemm_config(int64_t n, int64_t k, bool b_is_nk) {
+  (void)n;
+  (void)k;
+  (void)b_is_nk;
+  return GemmConfig{128, 128, TK, 4};
+}
+
+hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
+  const GemmConfig cfg = gemm_config(p.n, p.k, p.b_is_nk);
+  GemmArgs a;
+  a.a = static_cast<const uint16_t*>(p.a);
+  a.b = static_cast<const uint16_t*>(p.b);
+  a.c = p.c;
+  a.bias = p.bias;
+  a.lda = p.lda;
+  a.ldb = p.ldb;
+  a.ldc = p.ldc;
+  a.m = (int)p.m;
+  a.n = (int)p.n;
+  a.k = (int)p.k;
+  a.alpha = p.alpha;
+  a.beta = p.beta;
+  a.out_bf16 = p.c_bf16 ? 1 : 0;
+  a.bias_mode = p.bias == nullptr ? 0 : (p.bias_bf16 ? 1 : 2);
+  a.tiles_m = (int)((p.m + cfg.tile_m - 1) / cfg.tile_m);
+  a.tiles_n = (int)((p.n + cfg.tile_n - 1) / cfg.tile_n);
+  if (cfg.tile_m == 128 && cfg.tile_n == 128 && cfg.waves == 4) {
+    return p.b_is_nk ? launch_cfg<128, 128, 2, 2, true>(a, s) : launch_cfg<128, 128, 2, 2, false>(a, s);
+  }
+  return hipErrorInvalidConfiguration;
+}
+
+}  // namespace bi

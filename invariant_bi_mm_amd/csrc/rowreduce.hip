@@ -1,0 +1,360 @@
+// Batch-invariant row reductions for gfx950: RMSNorm, mean, log_softmax with
+// the greedy argmax.
+//
+// mean and log_softmax are supported ops of
+// "thinking-machines-lab/batch_invariant_ops" (section "When to avoid");
+// SGLang took over its mean and log-softmax kernels ("Batch-invariant
+// inference kernels (Thinking Machines) -- Evidence & limits", section
+// "Evidence"). RMSNorm is named as batch-dependent in readhandoff.com's
+// agent-run reproducibility pinning, section "What does temperature zero
+// actually guarantee?"; the greedy sampler "picks the highest-probability
+// token" (same section).
+//
+// Invariance: one workgroup owns one row and nothing else. The lane that
+// reads an element, the order each lane folds its elements, the butterfly
+// and the fixed-order merge of the waves' partials are all functions of n
+// (and the compiled kernel) only, so row i gets the same bits for any m and
+// any content of the other rows. No atomics, no cross-workgroup traffic.
+#include "bi_internal.h"
+#include "device_common.h"
+
+namespace bi {
+namespace {
+
+// ---------------------------------------------------------------------------
+// RMSNorm and mean over bf16 rows: one 64-lane wave per row. Lane l owns the
+// 16-byte chunks l, l + 64, l + 128, ... of its row (coalesced 128-bit loads),
+// keeps up to CPT of them in registers, folds them in increasing order, then
+// a wave butterfly gives every lane the row total. Elements past the last
+// full chunk (n % 8) are folded last, by lanes 0..n%8-1.
+// CPT == 0 selects the streaming variant (no register cache; chunks are read
+// again for the output pass) used for rows longer than 64 * 16 chunks.
+// ---------------------------------------------------------------------------
+template <int CPT>
+__global__ __launch_bounds__(64) void rmsnorm_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                      const uint16_t* __restrict__ w, float eps,
+                                                      void* __restrict__ y, int64_t ldy, int y_bf16,
+                                                      int n) {
+  const int row = blockIdx.x;
+  const int lane = threadIdx.x;
+  const uint16_t* xr = x + (int64_t)row * ldx;
+  const int nch = n >> 3;
+  const int tail = n & 7;
+
+  u32x4 cache[CPT > 0 ? CPT : 1];
+  float ss = 0.0f;
+  if constexpr (CPT > 0) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = lane + 64 * i;
+      cache[i] = c < nch ? reinterpret_cast<const u32x4*>(xr)[c] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      float f[8];
+      unpack8(cache[i], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(f[e], f[e], ss);
+    }
+  } else {
+    for (int c = lane; c < nch; c += 64) {
+      float f[8];
+      unpack8(reinterpret_cast<const u32x4*>(xr)[c], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(f[e], f[e], ss);
+    }
+  }
+  if (lane < tail) {
+    const float t = __uint_as_float(uint32_t(xr[nch * 8 + lane]) << 16);
+    ss = __builtin_fmaf(t, t, ss);
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)n + eps);
+
+  auto emit = [&](int c, const u32x4& xv) {
+    float f[8], wf[8];
+    unpack8(xv, f);
+    unpack8(reinterpret_cast<const u32x4*>(w)[c], wf);
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (f[e] * r) * wf[e];
+    if (y_bf16) {
+      u32x4 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                  pack_bf16x2(o[6], o[7])};
+      reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(y) + (int64_t)row * ldy)[c] = pk;
+    } else {
+      f32x4* yr = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(y) + (int64_t)row * ldy);
+      yr[2 * c] = f32x4{o[0], o[1], o[2], o[3]};
+      yr[2 * c + 1] = f32x4{o[4], o[5], o[6], o[7]};
+    }
+  };
+  if constexpr (CPT > 0) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nch) emit(c, cache[i]);
+    }
+  } else {
+    for (int c = lane; c < nch; c += 64) emit(c, reinterpret_cast<const u32x4*>(xr)[c]);
+  }
+  if (lane < tail) {
+    const int j = nch * 8 + lane;
+    const float t = __uint_as_float(uint32_t(xr[j]) << 16);
+    const float wj = __uint_as_float(uint32_t(w[j]) << 16);
+    const float o = (t * r) * wj;
+    if (y_bf16)
+      (reinterpret_cast<uint16_t*>(y) + (int64_t)row * ldy)[j] = (uint16_t)f32_to_bf16_rne(o);
+    else
+      (reinterpret_cast<float*>(y) + (int64_t)row * ldy)[j] = o;
+  }
+}
+
+// mean over bf16 (8 per chunk) or fp32 (4 per chunk) rows; same shape as above.
+template <bool BF16, int CPT>
+__global__ __launch_bounds__(64) void mean_kernel(const void* __restrict__ x, int64_t ldx,
+                                                   float* __restrict__ y, int n) {
+  const int row = blockIdx.x;
+  const int lane = threadIdx.x;
+  constexpr int PER = BF16 ? 8 : 4;
+  const int nch = n / PER;
+  const int tail = n - nch * PER;
+  float s = 0.0f;
+  if constexpr (BF16) {
+    const uint16_t* xr = reinterpret_cast<const uint16_t*>(x) + (int64_t)row * ldx;
+    if constexpr (CPT > 0) {
+      u32x4 cache[CPT];
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int c = lane + 64 * i;
+        cache[i] = c < nch ? reinterpret_cast<const u32x4*>(xr)[c] : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        float f[8];
+        unpack8(cache[i], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s = s + f[e];
+      }
+    } else {
+      for (int c = lane; c < nch; c += 64) {
+        float f[8];
+        unpack8(reinterpret_cast<const u32x4*>(xr)[c], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s = s + f[e];
+      }
+    }
+    if (lane < tail) s = s + __uint_as_float(uint32_t(xr[nch * 8 + lane]) << 16);
+  } else {
+    const float* xr = reinterpret_cast<const float*>(x) + (int64_t)row * ldx;
+    if constexpr (CPT > 0) {
+      f32x4 cache[CPT];
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int c = lane + 64 * i;
+        cache[i] = c < nch ? reinterpret_cast<const f32x4*>(xr)[c] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) s = s + cache[i].x + cache[i].y + cache[i].z + cache[i].w;
+    } else {
+      for (int c = lane; c < nch; c += 64) {
+        const f32x4 v = reinterpret_cast<const f32x4*>(xr)[c];
+        s = s + v.x + v.y + v.z + v.w;
+      }
+    }
+    if (lane < tail) s = s + xr[nch * 4 + lane];
+  }
+  s = wave_sum(s);
+  if (lane == 0) y[row] = s / (float)n;
+}
+
+// ---------------------------------------------------------------------------
+// log_softmax + argmax over fp32 rows: one workgroup of LS_NT threads per row.
+// Pass 1: thread t reads the 16-byte chunks t, t + LS_NT, ... in increasing
+// order and keeps a running (max, sum of exp(x - max)) pair, rescaled when
+// the max grows, plus the (value, lowest index) of its largest element.
+// The pairs are merged by a wave butterfly and then across waves in wave
+// order. Pass 2 re-reads the row and writes (x - max) - log(sum).
+// ---------------------------------------------------------------------------
+constexpr int LS_NT = 1024;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float exp_dev(float v) { return __builtin_amdgcn_exp2f(v * LOG2E); }
+
+struct MS {
+  float m, s;
+};
+__device__ __forceinline__ MS ms_merge(MS a, MS b) {
+  const float M = fmaxf(a.m, b.m);
+  if (M == -INFINITY) return MS{M, 0.0f};
+  return MS{M, a.s * exp_dev(a.m - M) + b.s * exp_dev(b.m - M)};
+}
+struct AM {
+  float v;
+  int i;
+};
+__device__ __forceinline__ AM am_merge(AM a, AM b) {
+  const bool take_b = (b.v > a.v) || (b.v == a.v && b.i < a.i);
+  return take_b ? b : a;
+}
+
+__global__ __launch_bounds__(LS_NT) void log_softmax_kernel(const float* __restrict__ x, int64_t ldx,
+                                                             float* __restrict__ y, int64_t ldy,
+                                                             int64_t* __restrict__ amax, int n) {
+  __shared__ float sm_m[LS_NT / 64], sm_s[LS_NT / 64], sm_v[LS_NT / 64];
+  __shared__ int sm_i[LS_NT / 64];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const float* xr = x + (int64_t)row * ldx;
+  float* yr = y + (int64_t)row * ldy;
+  const int nch = n >> 2;
+  const int tail = n & 3;
+
+  float m = -INFINITY, s = 0.0f;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  auto fold = [&](float v, int j) {
+    // argmax: strictly greater keeps the lowest index within this thread.
+    if (v > bv) {
+      bv = v;
+      bi = j;
+    }
+  };
+  auto fold4 = [&](const f32x4 v, int j0) {
+    const float cm = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+    if (cm > m) {
+      s = s * exp_dev(m - cm);
+      m = cm;
+    }
+    s = s + exp_dev(v.x - m);
+    s = s + exp_dev(v.y - m);
+    s = s + exp_dev(v.z - m);
+    s = s + exp_dev(v.w - m);
+    fold(v.x, j0);
+    fold(v.y, j0 + 1);
+    fold(v.z, j0 + 2);
+    fold(v.w, j0 + 3);
+  };
+
+  int c = tid;
+  for (; c + 3 * LS_NT < nch; c += 4 * LS_NT) {
+    const f32x4 v0 = reinterpret_cast<const f32x4*>(xr)[c];
+    const f32x4 v1 = reinterpret_cast<const f32x4*>(xr)[c + LS_NT];
+    const f32x4 v2 = reinterpret_cast<const f32x4*>(xr)[c + 2 * LS_NT];
+    const f32x4 v3 = reinterpret_cast<const f32x4*>(xr)[c + 3 * LS_NT];
+    fold4(v0, 4 * c);
+    fold4(v1, 4 * (c + LS_NT));
+    fold4(v2, 4 * (c + 2 * LS_NT));
+    fold4(v3, 4 * (c + 3 * LS_NT));
+  }
+  for (; c < nch; c += LS_NT) fold4(reinterpret_cast<const f32x4*>(xr)[c], 4 * c);
+  if (tid < tail) {
+    const float v = xr[nch * 4 + tid];
+    if (v > m) {
+      s = s * exp_dev(m - v);
+      m = v;
+    }
+    s = s + exp_dev(v - m);
+    fold(v, nch * 4 + tid);
+  }
+
+  MS ms{m, s};
+  AM am{bv, bi};
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    ms = ms_merge(ms, MS{xor_shfl(ms.m, d), xor_shfl(ms.s, d)});
+    am = am_merge(am, AM{xor_shfl(am.v, d), __shfl_xor(am.i, d, 64)});
+  }
+  if (lane == 0) {
+    sm_m[wave] = ms.m;
+    sm_s[wave] = ms.s;
+    sm_v[wave] = am.v;
+    sm_i[wave] = am.i;
+  }
+  __syncthreads();
+  MS tot = MS{sm_m[0], sm_s[0]};
+  AM best = AM{sm_v[0], sm_i[0]};
+#pragma unroll
+  for (int w = 1; w < LS_NT / 64; ++w) {
+    tot = ms_merge(tot, MS{sm_m[w], sm_s[w]});
+    best = am_merge(best, AM{sm_v[w], sm_i[w]});
+  }
+  if (tid == 0 && amax != nullptr) amax[row] = (int64_t)(best.i == 0x7fffffff ? 0 : best.i);
+
+  const float mx = tot.m;
+  const float lg = __builtin_amdgcn_logf(tot.s) * LN2;  // log2 -> ln
+  for (c = tid; c < nch; c += LS_NT) {
+    const f32x4 v = reinterpret_cast<const f32x4*>(xr)[c];
+    reinterpret_cast<f32x4*>(yr)[c] = f32x4{(v.x - mx) - lg, (v.y - mx) - lg, (v.z - mx) - lg, (v.w - mx) - lg};
+  }
+  if (tid < tail) yr[nch * 4 + tid] = (xr[nch * 4 + tid] - mx) - lg;
+}
+
+// Chunks-per-lane template choice for one-wave-per-row kernels: a function
+// of n only.
+int pick_cpt(int64_t nch) {
+  const int64_t per = (nch + 63) / 64;
+  if (per <= 1) return 1;
+  if (per <= 2) return 2;
+  if (per <= 4) return 4;
+  if (per <= 8) return 8;
+  if (per <= 16) return 16;
+  return 0;
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm(const void* x, int64_t ldx, const void* w, float eps, void* y, int64_t ldy,
+                          bool y_bf16, int64_t m, int64_t n, hipStream_t s) {
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  const uint16_t* wp = static_cast<const uint16_t*>(w);
+  const int yb = y_bf16 ? 1 : 0;
+  const dim3 grid((unsigned)m), block(64);
+  switch (pick_cpt(n / 8)) {
+    case 1: hipLaunchKernelGGL(rmsnorm_kernel<1>, grid, block, 0, s, xp, ldx, wp, eps, y, ldy, yb, (int)n); break;
+    case 2: hipLaunchKernelGGL(rmsnorm_kernel<2>, grid, block, 0, s, xp, ldx, wp, eps, y, ldy, yb, (int)n); break;
+    case 4: hipLaunchKernelGGL(rmsnorm_kernel<4>, grid, block, 0, s, xp, ldx, wp, eps, y, ldy, yb, (int)n); break;
+    case 8: hipLaunchKernelGGL(rmsnorm_kernel<8>, grid, block, 0, s, xp, ldx, wp, eps, y, ldy, yb, (int)n); break;
+    case 16: hipLaunchKernelGGL(rmsnorm_kernel<16>, grid, block, 0, s, xp, ldx, wp, eps, y, ldy, yb, (int)n); break;
+    default: hipLaunchKernelGGL(rmsnorm_kernel<0>, grid, block, 0, s, xp, ldx, wp, eps, y, ldy, yb, (int)n); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mean(const void* x, bool x_bf16, int64_t ldx, float* y, int64_t m, int64_t n,
+                       hipStream_t s) {
+  const dim3 grid((unsigned)m), block(64);
+  const int cpt = pick_cpt(x_bf16 ? n / 8 : n / 4);
+  const int ni = (int)n;
+#define BI_MEAN_CASE(B, C) hipLaunchKernelGGL((mean_kernel<B, C>), grid, block, 0, s, x, ldx, y, ni)
+  if (x_bf16) {
+    switch (cpt) {
+      case 1: BI_MEAN_CASE(true, 1); break;
+      case 2: BI_MEAN_CASE(true, 2); break;
+      case 4: BI_MEAN_CASE(true, 4); break;
+      case 8: BI_MEAN_CASE(true, 8); break;
+      case 16: BI_MEAN_CASE(true, 16); break;
+      default: BI_MEAN_CASE(true, 0); break;
+    }
+  } else {
+    switch (cpt) {
+      case 1: BI_MEAN_CASE(false, 1); break;
+      case 2: BI_MEAN_CASE(false, 2); break;
+      case 4: BI_MEAN_CASE(false, 4); break;
+      case 8: BI_MEAN_CASE(false, 8); break;
+      case 16: BI_MEAN_CASE(false, 16); break;
+      default: BI_MEAN_CASE(false, 0); break;
+    }
+  }
+#undef BI_MEAN_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_log_softmax(const float* x, int64_t ldx, float* y, int64_t ldy, int64_t* argmax,
+                              int64_t m, int64_t n, hipStream_t s) {
+  hipLaunchKernelGGL(log_softmax_kernel, dim3((unsigned)m), dim3(LS_NT), 0, s, x, ldx, y, ldy, argmax, (int)n);
+  return hipGetLastError();
+}
+
+}  // namespace bi

@@ -1,0 +1,279 @@
+"""Batch invariance, bit for bit, through the C ABI.
+
+The property ("their numerical output for a given sequence depends on the
+total batch size" is what the pages call the defect; readhandoff.com,
+agent-run reproducibility pinning, "What does temperature zero actually
+guarantee?") is checked directly by memcmp, with no oracle: a fixed row
+computed alone (M = 1) must have the same bytes inside every batch size, at
+every position, whatever the other rows hold (random, zeros, huge, NaN/Inf),
+and on every repeated run. A negative control runs the same harness on
+torch's own kernels and reports how many rows change.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synthetic as S
+from helpers import digest, same_bits
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def with_row(m, k, row, pos, seed, fill="random", dtype=torch.bfloat16):
+    """[m, k] on the GPU with `row` at `pos` and the other rows per `fill`."""
+    if fill == "random":
+        x = S.normal_f32((m, k), 1.0, seed=seed, device=DEV)
+    elif fill == "zeros":
+        x = torch.zeros((m, k), device=DEV)
+    elif fill == "huge":
+        x = torch.full((m, k), 3.0e38, device=DEV)
+    elif fill == "nan":
+        x = torch.full((m, k), float("nan"), device=DEV)
+        x[:, ::3] = float("inf")
+    x = x.to(dtype)
+    x[pos] = row
+    return x
+
+
+# ------------------------------------------------------------------ GEMM
+def gemm_sweep(lib, k, n, ms, b_is_nk=False, out_dtype=torch.float32, var=0.02, positions=None):
+    w = S.normal_bf16((n, k) if b_is_nk else (k, n), var, seed=7 + n + k, device=DEV)
+    row = S.normal_bf16((1, k), 1.0, seed=11, device=DEV)[0]
+    ref = lib.bi_mm(row[None], w, b_is_nk=b_is_nk, out_dtype=out_dtype)[0].clone()
+    bad = []
+    for m in ms:
+        for pos in (positions(m) if positions else sorted({0, m - 1, (m * 5) // 7})):
+            x = with_row(m, k, row, pos, seed=1000 + m)
+            c = lib.bi_mm(x, w, b_is_nk=b_is_nk, out_dtype=out_dtype)
+            if not same_bits(c[pos], ref):
+                bad.append((m, pos))
+    return bad
+
+
+def test_mm_smoke_every_m_up_to_4096(lib):
+    """K = N = 512 smoke shape, every M = 1..4096: row 0 fixed, others random."""
+    w = S.normal_bf16((512, 512), 1 / 512, seed=2, device=DEV)
+    row = S.normal_bf16((1, 512), 1.0, seed=1, device=DEV)[0]
+    ref = lib.bi_mm(row[None], w)[0].clone()
+    refb = lib.bi_mm(row[None], w, out_dtype=torch.bfloat16)[0].clone()
+    say("mm every M 1..4096")
+    # one big random block; each M uses its first M rows (row 0 fixed)
+    big = S.normal_bf16((4096, 512), 1.0, seed=3, device=DEV)
+    big[0] = row
+    outs = torch.empty((4096, 512), device=DEV)
+    bad = []
+    for m in range(1, 4097):
+        c = lib.bi_mm(big[:m], w, out=outs[:m])
+        if m % 512 == 0 or m < 4:
+            torch.cuda.synchronize()
+        if not torch.equal(c[0].view(torch.int32), ref.view(torch.int32)):
+            bad.append(m)
+    assert not bad, f"row 0 changed at M = {bad[:20]}"
+    cb = lib.bi_mm(big, w, out_dtype=torch.bfloat16)
+    assert same_bits(cb[0], refb)
+
+
+def test_mm_smoke_every_position_in_tile(lib):
+    """The fixed row at every position 0..TM-1 of a tile (and in the next
+    tile): MFMA lane placement must not change its bits."""
+    tm = lib.bi_gemm_config(512, 512)[0]
+    w = S.normal_bf16((512, 512), 1 / 512, seed=2, device=DEV)
+    row = S.normal_bf16((1, 512), 1.0, seed=1, device=DEV)[0]
+    ref = lib.bi_mm(row[None], w)[0].clone()
+    m = 2 * tm + 3
+    base = S.normal_bf16((m, 512), 1.0, seed=4, device=DEV)
+    bad = []
+    for pos in range(m):
+        x = base.clone()
+        x[pos] = row
+        c = lib.bi_mm(x, w)
+        if not same_bits(c[pos], ref):
+            bad.append(pos)
+    assert not bad, f"row changed at positions {bad[:20]}"
+
+
+@pytest.mark.parametrize("fill", ["zeros", "huge", "nan"])
+def test_mm_adversarial_other_rows(lib, fill):
+    w = S.normal_bf16((512, 512), 1 / 512, seed=2, device=DEV)
+    row = S.normal_bf16((1, 512), 1.0, seed=1, device=DEV)[0]
+    ref = lib.bi_mm(row[None], w)[0].clone()
+    for m in (2, 33, 200):
+        for pos in (0, m - 1):
+            x = with_row(m, 512, row, pos, seed=0, fill=fill)
+            assert same_bits(lib.bi_mm(x, w)[pos], ref), (fill, m, pos)
+
+
+QWEN = [(4096, 6144), (4096, 4096), (4096, 24576), (12288, 4096)]
+
+
+@pytest.mark.parametrize("k,n", QWEN)
+def test_mm_qwen_shapes_invariant(lib, k, n):
+    """Qwen3-8B projection shapes: config Ms, tile boundaries, random Ms."""
+    tm = lib.bi_gemm_config(n, k)[0]
+    rng = np.random.default_rng(k + n)
+    ms = sorted({1, 2, 8, 64, 512, 4096, tm - 1, tm, tm + 1, 2 * tm + 1,
+                 *rng.integers(2, 4097, size=4).tolist()})
+    say(f"qwen invariance k={k} n={n} ms={ms}")
+    bad = gemm_sweep(lib, k, n, ms)
+    assert not bad, bad
+
+
+def test_mm_nk_layout_and_bf16_invariant(lib):
+    bad = gemm_sweep(lib, 4096, 4096, [1, 7, 129, 1000], b_is_nk=True)
+    assert not bad, bad
+    bad = gemm_sweep(lib, 4096, 4096, [1, 7, 129, 1000], out_dtype=torch.bfloat16)
+    assert not bad, bad
+
+
+def test_addmm_lm_head_invariant(lib):
+    k, n = 4096, 151936
+    w = S.normal_bf16((k, n), 0.02, seed=51, device=DEV)
+    bias = S.normal_bf16((n,), 0.1, seed=52, device=DEV)
+    row = S.normal_bf16((1, k), 1.0, seed=53, device=DEV)[0]
+    ref = lib.bi_addmm(bias, row[None], w)[0].clone()
+    lp_ref, am_ref = lib.bi_log_softmax(ref[None].contiguous())
+    for m in (32, 256):
+        say(f"lm head invariance m={m}")
+        x = with_row(m, k, row, m // 3, seed=54 + m)
+        logits = lib.bi_addmm(bias, x, w)
+        assert same_bits(logits[m // 3], ref)
+        lp, am = lib.bi_log_softmax(logits)
+        assert same_bits(lp[m // 3], lp_ref[0]) and am[m // 3].item() == am_ref[0].item()
+
+
+def test_mm_repeat_100(lib):
+    x = S.normal_bf16((512, 4096), 1.0, seed=60, device=DEV)
+    w = S.normal_bf16((4096, 4096), 0.02, seed=61, device=DEV)
+    first = lib.bi_mm(x, w)
+    h = digest(first)
+    for _ in range(99):
+        assert same_bits(lib.bi_mm(x, w), first)
+    say("mm sha256", h)
+
+
+# ------------------------------------------------------------------ reductions
+def test_rows_reductions_invariant(lib):
+    n = 4096
+    w = S.uniform_bf16((n,), 0.5, 1.5, seed=61, device=DEV)
+    row = S.normal_bf16((1, n), 1.0, seed=62, device=DEV)[0]
+    ref_y = lib.bi_rmsnorm(row[None], w, 1e-6)[0].clone()
+    ref_yf = lib.bi_rmsnorm(row[None], w, 1e-6, out_dtype=torch.float32)[0].clone()
+    ref_mean = lib.bi_mean(row[None])[0].clone()
+    for m in (1, 2, 7, 64, 513, 2048):
+        for fill in ("random", "zeros", "huge", "nan"):
+            for pos in sorted({0, m - 1, m // 2}):
+                x = with_row(m, n, row, pos, seed=63 + m, fill=fill)
+                assert same_bits(lib.bi_rmsnorm(x, w, 1e-6)[pos], ref_y), ("rmsnorm", m, fill, pos)
+                assert same_bits(lib.bi_rmsnorm(x, w, 1e-6, out_dtype=torch.float32)[pos], ref_yf)
+                assert same_bits(lib.bi_mean(x)[pos], ref_mean), ("mean", m, fill, pos)
+
+
+def test_log_softmax_invariant(lib):
+    n = 151936
+    row = S.normal_f32((1, n), 4.0, seed=70, device=DEV)[0]
+    ref_y, ref_a = lib.bi_log_softmax(row[None].contiguous())
+    for m in (1, 7, 64, 513):
+        for fill in ("random", "zeros", "nan"):
+            pos = (m * 3) // 5
+            x = with_row(m, n, row, pos, seed=71 + m, fill=fill, dtype=torch.float32)
+            y, a = lib.bi_log_softmax(x)
+            assert same_bits(y[pos], ref_y[0]), (m, fill)
+            assert a[pos].item() == ref_a[0].item()
+
+
+def test_reductions_repeat_100(lib):
+    x = S.normal_bf16((2048, 4096), 1.0, seed=80, device=DEV)
+    w = S.uniform_bf16((4096,), 0.5, 1.5, seed=81, device=DEV)
+    lg = S.normal_f32((64, 151936), 4.0, seed=82, device=DEV)
+    y0, m0 = lib.bi_rmsnorm(x, w, 1e-6), lib.bi_mean(x)
+    l0, a0 = lib.bi_log_softmax(lg)
+    for _ in range(99):
+        assert same_bits(lib.bi_rmsnorm(x, w, 1e-6), y0)
+        assert same_bits(lib.bi_mean(x), m0)
+        l1, a1 = lib.bi_log_softmax(lg)
+        assert same_bits(l1, l0) and same_bits(a1, a0)
+
+
+# ------------------------------------------------------------------ decode attention
+def test_decode_batch_composition_invariant(lib):
+    """A sequence's output is the same bytes alone, in batches of other
+    sequences, at other batch positions and with other page placements."""
+    hq, hkv, d, page = 32, 8, 128, 16
+    target_len = 5000
+    qx = S.normal_bf16((hq, d), 1.0, seed=90)
+    kx = S.normal_bf16((target_len, hkv, d), 1.0, seed=91)   # the target's tokens
+    vx = S.normal_bf16((target_len, hkv, d), 1.0, seed=92)
+
+    def batch(other_lens, pos, seed):
+        lens = list(other_lens)
+        lens.insert(pos, target_len)
+        lens_t = torch.tensor(lens, dtype=torch.int32)
+        table, npages = S.paged_kv_layout(lens_t, page, seed=seed)
+        kp = S.normal_bf16((npages, hkv, page, d), 1.0, seed=seed + 1)
+        vp = S.normal_bf16((npages, hkv, page, d), 1.0, seed=seed + 2)
+        for t in range(target_len):              # place the target's tokens
+            p = table[pos, t // page]
+            kp[p, :, t % page] = kx[t]
+            vp[p, :, t % page] = vx[t]
+        q = S.normal_bf16((len(lens), hq, d), 1.0, seed=seed + 3)
+        q[pos] = qx
+        offs, total = lib.bi_decode_plan(lens_t)
+        out = lib.bi_decode_attention(q.to(DEV), kp.to(DEV), vp.to(DEV), table.to(DEV), lens_t.to(DEV),
+                                      offs.to(DEV), total)
+        return out[pos].cpu()
+
+    ref = batch([], 0, seed=200)
+    cases = [([1], 1, 210), ([300, 7, 32768], 2, 220), (S.context_lens(63, seed=5).tolist(), 40, 230),
+             ([5000] * 3, 0, 240)]
+    for others, pos, seed in cases:
+        say(f"decode composition B={len(others) + 1} pos={pos}")
+        assert same_bits(batch(others, pos, seed), ref), (len(others), pos)
+
+
+def test_decode_repeat_100(lib):
+    lens_t = S.context_lens(32, seed=300)
+    table, npages = S.paged_kv_layout(lens_t, 16, seed=301)
+    q = S.normal_bf16((32, 32, 128), 1.0, seed=302, device=DEV)
+    kp = S.normal_bf16((npages, 8, 16, 128), 1.0, seed=303, device=DEV)
+    vp = S.normal_bf16((npages, 8, 16, 128), 1.0, seed=304, device=DEV)
+    offs, total = lib.bi_decode_plan(lens_t)
+    args = (q, kp, vp, table.to(DEV), lens_t.to(DEV), offs.to(DEV), total)
+    first = lib.bi_decode_attention(*args)
+    for _ in range(99):
+        assert same_bits(lib.bi_decode_attention(*args), first)
+
+
+# ------------------------------------------------------------------ negative control
+def test_harness_detects_one_flipped_bit():
+    a = torch.randn(64)
+    b = a.clone()
+    b.view(torch.int32)[17] ^= 1
+    assert not same_bits(a, b) and same_bits(a, a.clone())
+
+
+def test_negative_control_torch_kernels(lib):
+    """The same harness on torch's own (non-invariant) kernels. The count is
+    reported, not asserted: whether a vendor library changes its reduction
+    with M is its own business; the test only shows the harness can see it."""
+    k, n = 4096, 4096
+    w = S.normal_bf16((k, n), 0.02, seed=7, device=DEV)
+    row = S.normal_bf16((1, k), 1.0, seed=11, device=DEV)[0]
+    ref = (row[None] @ w)[0].float()
+    changed = []
+    for m in (2, 8, 64, 512, 4096):
+        x = with_row(m, k, row, 0, seed=m)
+        if not same_bits((x @ w)[0].float(), ref):
+            changed.append(m)
+    lg = S.normal_f32((1, 151936), 4.0, seed=3, device=DEV)
+    ref_l = torch.log_softmax(lg, dim=-1)[0]
+    lchanged = []
+    for m in (2, 64, 513):
+        x = with_row(m, 151936, lg[0], 0, seed=m, dtype=torch.float32)
+        if not same_bits(torch.log_softmax(x, dim=-1)[0], ref_l):
+            lchanged.append(m)
+    say(f"negative control: torch.mm row 0 changed at M={changed}; log_softmax at M={lchanged}")

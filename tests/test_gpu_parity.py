@@ -1,0 +1,303 @@
+"""GPU parity: every kernel against the fp64 oracle, through the C ABI.
+
+fp32 outputs must meet relative Frobenius <= 1e-3 and elementwise
+|err| <= 4e-3 (|ref| + 1). bf16 outputs cannot meet the Frobenius bound
+against an unrounded oracle (a single round-to-nearest of N(0,1) data to bf16
+alone gives ~1.7e-3), so they are checked as bitwise equal to torch's
+round-to-nearest-even of the same kernel's fp32 output, plus the elementwise
+bound against the unrounded oracle. Argmax indices are compared exactly on
+the same fp32 logits.
+
+Small cases are compared element by element; the full-size shapes are
+compared on sampled rows/columns the oracle can afford, in the launch
+configuration the benchmark times.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synthetic as S
+from helpers import assert_close, bits, f32, rne_bf16, same_bits
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------ GEMM
+@pytest.mark.parametrize("m", [1, 2, 3, 8, 16])
+def test_mm_smoke_config(lib, m):
+    """X[M,512] ~ N(0,1), W[512,512] ~ N(0,1/512): the small smoke case."""
+    say(f"mm smoke m={m}")
+    x = S.rows_with_fixed_row(m, 512, 1.0, fixed_seed=1, other_seed=100 + m).to(DEV)
+    w = S.normal_bf16((512, 512), 1 / 512, seed=2).to(DEV)
+    c = lib.bi_mm(x, w)
+    ref = O.mm(bits(x), bits(w))
+    assert_close(f32(c), ref, f"mm m={m}")
+    cb = lib.bi_mm(x, w, out_dtype=torch.bfloat16)
+    assert same_bits(cb, rne_bf16(c)), "bf16 output is not RNE of the fp32 output"
+    assert O.elementwise_ratio(f32(cb.float()), ref) <= 4e-3
+
+
+@pytest.mark.parametrize("b_is_nk", [False, True])
+@pytest.mark.parametrize("m,n,k", [(300, 200, 264), (129, 136, 520), (1, 8, 8), (257, 384, 64), (77, 1000, 1032)])
+def test_mm_ragged_tiles(lib, m, n, k, b_is_nk):
+    """Sizes that span several tiles with ragged M, N and K tails."""
+    if not b_is_nk and n % 8:
+        pytest.skip("B [k, n] needs n % 8 == 0")
+    say(f"mm ragged m={m} n={n} k={k} nk={b_is_nk}")
+    a = S.normal_bf16((m, k), 1.0, seed=m * 7 + k).to(DEV)
+    b = S.normal_bf16((n, k) if b_is_nk else (k, n), 1.0 / k, seed=n * 13 + k).to(DEV)
+    c = lib.bi_mm(a, b, b_is_nk=b_is_nk)
+    assert_close(f32(c), O.mm(bits(a), bits(b), b_is_nk=b_is_nk), "mm ragged")
+
+
+def test_mm_layouts_agree_bitwise(lib):
+    """B stored [K,N] and the same B stored [N,K] give identical bits: the
+    layout changes only how B reaches LDS, not the arithmetic."""
+    say("mm layouts")
+    a = S.normal_bf16((200, 512), 1.0, seed=5).to(DEV)
+    b = S.normal_bf16((512, 384), 1 / 512, seed=6).to(DEV)
+    c1 = lib.bi_mm(a, b)
+    c2 = lib.bi_mm(a, b.t().contiguous(), b_is_nk=True)
+    assert same_bits(c1, c2)
+
+
+def test_mm_strided_operands(lib):
+    """Row strides larger than the rows (sub-views of wider buffers)."""
+    say("mm strided")
+    big_a = S.normal_bf16((70, 520), 1.0, seed=8).to(DEV)
+    big_b = S.normal_bf16((264, 208), 1 / 256, seed=9).to(DEV)
+    a = big_a[:, :256]
+    b = big_b[:256, :200]
+    out_big = torch.full((70, 216), 7.0, device=DEV)
+    out = out_big[:, :200]
+    lib.bi_mm(a, b, out=out)
+    assert_close(f32(out), O.mm(bits(a), bits(b)), "mm strided")
+    assert torch.all(out_big[:, 200:] == 7.0), "wrote outside the output view"
+
+
+def test_mm_identity_and_ones_exact(lib):
+    say("mm identity")
+    a = S.normal_bf16((130, 256), 1.0, seed=10).to(DEV)
+    eye = torch.eye(256, dtype=torch.bfloat16, device=DEV)
+    assert same_bits(lib.bi_mm(a, eye), a.float())
+    assert same_bits(lib.bi_mm(a, eye, out_dtype=torch.bfloat16), a)
+    ones_a = torch.ones((5, 4096), dtype=torch.bfloat16, device=DEV)
+    ones_b = torch.ones((4096, 64), dtype=torch.bfloat16, device=DEV)
+    assert torch.all(lib.bi_mm(ones_a, ones_b) == 4096.0)
+
+
+def test_mm_k_zero_and_empty(lib):
+    say("mm empty")
+    a = torch.empty((5, 0), dtype=torch.bfloat16, device=DEV)
+    b = torch.empty((0, 16), dtype=torch.bfloat16, device=DEV)
+    c = torch.full((5, 16), 3.0, device=DEV)
+    lib.bi_mm(a, b, out=c)
+    assert torch.all(c == 0)
+    e = lib.bi_mm(torch.empty((0, 64), dtype=torch.bfloat16, device=DEV),
+                  torch.ones((64, 8), dtype=torch.bfloat16, device=DEV))
+    assert e.shape == (0, 8)
+
+
+QWEN = [(4096, 6144), (4096, 4096), (4096, 24576), (12288, 4096)]
+
+
+@pytest.mark.parametrize("k,n", QWEN)
+@pytest.mark.parametrize("m", [1, 512, 4096])
+def test_mm_qwen_shapes_sampled(lib, k, n, m):
+    """Full-size projection GEMMs (weights ~N(0,0.02)), sampled rows."""
+    say(f"mm qwen k={k} n={n} m={m}")
+    a = S.normal_bf16((m, k), 1.0, seed=20 + m, device=DEV)
+    w = S.normal_bf16((k, n), 0.02, seed=30 + n + k, device=DEV)
+    c = lib.bi_mm(a, w)
+    rows = sorted({0, m - 1, m // 2, (m * 7) // 11})
+    ref = O.mm(bits(a[rows]), bits(w))
+    assert_close(f32(c[rows]), ref, f"qwen k={k} n={n} m={m}")
+
+
+def test_addmm_small_and_alpha_beta(lib):
+    say("addmm small")
+    a = S.normal_bf16((70, 256), 1.0, seed=40).to(DEV)
+    b = S.normal_bf16((256, 136), 1 / 256, seed=41).to(DEV)
+    bias = S.normal_bf16((136,), 0.1, seed=42).to(DEV)
+    c = lib.bi_addmm(bias, a, b)
+    assert_close(f32(c), O.addmm(bits(bias), bits(a), bits(b)), "addmm")
+    c2 = lib.bi_addmm(bias.float(), a, b, beta=0.5, alpha=2.0)
+    assert_close(f32(c2), O.addmm(f32(bias.float()), bits(a), bits(b), beta=0.5, alpha=2.0), "addmm a/b")
+    cb = lib.bi_addmm(bias, a, b, out_dtype=torch.bfloat16)
+    assert same_bits(cb, rne_bf16(c))
+    # A = 0 gives beta * bias exactly
+    z = lib.bi_addmm(bias, torch.zeros_like(a), b)
+    assert same_bits(z, bias.float().expand(70, 136).contiguous())
+
+
+def test_addmm_lm_head_then_log_softmax(lib):
+    """LM head (X[M,4096], W[4096,151936] ~N(0,0.02), bias ~N(0,0.1)) then
+    log_softmax + argmax, sampled columns/rows."""
+    m, k, n = 32, 4096, 151936
+    say("lm head chain")
+    x = S.normal_bf16((m, k), 1.0, seed=50, device=DEV)
+    w = S.normal_bf16((k, n), 0.02, seed=51, device=DEV)
+    bias = S.normal_bf16((n,), 0.1, seed=52, device=DEV)
+    logits = lib.bi_addmm(bias, x, w)
+    rows = [0, 13, 31]
+    cols = np.sort(np.random.default_rng(0).choice(n, 2048, replace=False))
+    colst = torch.from_numpy(cols).to(DEV)
+    ref = O.addmm(bits(bias[colst]), bits(x[rows]), bits(w[:, colst]))
+    assert_close(f32(logits[rows][:, colst]), ref, "lm head")
+    lp, am = lib.bi_log_softmax(logits)
+    # op-level: log_softmax and argmax on the GPU logits against the oracle
+    lg = f32(logits[rows])
+    assert_close(f32(lp[rows]), O.log_softmax(lg), "log_softmax of lm head")
+    assert am[rows].cpu().tolist() == O.argmax(lg).tolist()
+
+
+# ------------------------------------------------------------------ reductions
+@pytest.mark.parametrize("m", [1, 7, 64, 513])
+def test_rmsnorm(lib, m):
+    say(f"rmsnorm m={m}")
+    x = S.normal_bf16((m, 4096), 1.0, seed=60 + m).to(DEV)
+    w = S.uniform_bf16((4096,), 0.5, 1.5, seed=61).to(DEV)
+    y = lib.bi_rmsnorm(x, w, 1e-6, out_dtype=torch.float32)
+    ref = O.rmsnorm(bits(x), bits(w), 1e-6)
+    assert_close(f32(y), ref, f"rmsnorm m={m}")
+    yb = lib.bi_rmsnorm(x, w, 1e-6, out_dtype=torch.bfloat16)
+    assert same_bits(yb, rne_bf16(y)), "bf16 RMSNorm is not RNE of its fp32 output"
+    assert O.elementwise_ratio(f32(yb.float()), ref) <= 4e-3
+
+
+@pytest.mark.parametrize("n", [4100, 8, 13, 20000, 4096 * 5])
+def test_rmsnorm_other_widths(lib, n):
+    """Widths with a tail (n % 8 != 0), tiny rows and rows past the register
+    cache (streaming variant)."""
+    say(f"rmsnorm n={n}")
+    ld = (n + 7) // 8 * 8
+    buf = S.normal_bf16((9, ld), 1.0, seed=n).to(DEV)
+    x = buf[:, :n]
+    w = S.uniform_bf16((ld,), 0.5, 1.5, seed=n + 1).to(DEV)[:n]
+    y = lib.bi_rmsnorm(x, w, 1e-6, out_dtype=torch.float32, out=torch.empty((9, ld), device=DEV)[:, :n])
+    assert_close(f32(y), O.rmsnorm(bits(x), bits(w), 1e-6), f"rmsnorm n={n}")
+
+
+def test_rmsnorm_constant_rows(lib):
+    say("rmsnorm const")
+    n = 4096
+    x = torch.tensor([0.0, 1.0, -0.5, 3.0], dtype=torch.bfloat16).repeat_interleave(n).view(4, n).to(DEV)
+    w = S.uniform_bf16((n,), 0.5, 1.5, seed=62).to(DEV)
+    y = lib.bi_rmsnorm(x, w, 1e-6, out_dtype=torch.float32)
+    assert torch.all(y[0] == 0)
+    assert_close(f32(y), O.rmsnorm(bits(x), bits(w), 1e-6), "rmsnorm const")
+
+
+@pytest.mark.parametrize("m", [1, 7, 64, 513])
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_mean(lib, m, dt):
+    say(f"mean m={m} {dt}")
+    x = S.normal_f32((m, 4096), 1.0, seed=70 + m).to(dt).to(DEV)
+    y = lib.bi_mean(x)
+    ref = O.mean(bits(x) if dt == torch.bfloat16 else f32(x))
+    assert_close(f32(y), ref, "mean")
+
+
+def test_mean_constant_rows_exact_and_tails(lib):
+    say("mean const")
+    vals = [1.5, -3.25, 0.0, 7.0]
+    x = torch.tensor(vals, dtype=torch.bfloat16).repeat_interleave(4096).view(4, 4096).to(DEV)
+    assert lib.bi_mean(x).cpu().tolist() == vals
+    for n in (1, 5, 4099, 30000):
+        ld = (n + 7) // 8 * 8
+        xb = S.normal_bf16((3, ld), 1.0, seed=n).to(DEV)[:, :n]
+        assert_close(f32(lib.bi_mean(xb)), O.mean(bits(xb)), f"mean n={n}")
+
+
+@pytest.mark.parametrize("m", [1, 7, 64])
+def test_log_softmax(lib, m):
+    say(f"log_softmax m={m}")
+    x = S.normal_f32((m, 151936), 4.0, seed=80 + m).to(DEV)
+    y, am = lib.bi_log_softmax(x)
+    xc = f32(x)
+    assert_close(f32(y), O.log_softmax(xc), f"log_softmax m={m}")
+    assert am.cpu().tolist() == O.argmax(xc).tolist()
+    # sum exp(y) = 1 per row (fp64 sum of the fp32 outputs)
+    s = np.exp(f32(y).astype(np.float64)).sum(axis=1)
+    assert np.all(np.abs(s - 1.0) < 1e-4)
+
+
+def test_log_softmax_edges(lib):
+    say("log_softmax edges")
+    n = 1003
+    ld = 1004
+    buf = S.normal_f32((6, ld), 1.0, seed=90).to(DEV)
+    x = buf[:, :n]
+    x[0] = 0.7                              # constant row: -log n
+    x[1, 10] = 50.0                         # unique max
+    x[2, 5] = 9.0
+    x[2, 900] = 9.0                         # tie: lowest index
+    x[3, n - 1] = 80.0                      # max in the tail (n % 4 != 0)
+    y, am = lib.bi_log_softmax(x, out=torch.empty((6, ld), device=DEV)[:, :n])
+    xc = f32(x)
+    assert_close(f32(y), O.log_softmax(xc), "log_softmax edges")
+    assert am.cpu().tolist() == O.argmax(xc).tolist()
+    assert am[2].item() == 5 and am[3].item() == n - 1
+    assert abs(y[0, 0].item() + math.log(n)) < 1e-5
+    y1, none = lib.bi_log_softmax(x[:1].contiguous(), want_argmax=False)
+    assert none is None and same_bits(y1, y[:1])
+
+
+# ------------------------------------------------------------------ decode attention
+def make_decode(lens, seed, hkv=8, hq=32, d=128, page=16):
+    lens_t = torch.tensor(lens, dtype=torch.int32)
+    table, npages = S.paged_kv_layout(lens_t, page, seed=seed)
+    q = S.normal_bf16((len(lens), hq, d), 1.0, seed=seed + 1)
+    kp = S.normal_bf16((npages, hkv, page, d), 1.0, seed=seed + 2)
+    vp = S.normal_bf16((npages, hkv, page, d), 1.0, seed=seed + 3)
+    return lens_t, table, q, kp, vp
+
+
+def run_decode(lib, lens_t, table, q, kp, vp, out_dtype=torch.float32):
+    offs, total = lib.bi_decode_plan(lens_t)
+    return lib.bi_decode_attention(q.to(DEV), kp.to(DEV), vp.to(DEV), table.to(DEV), lens_t.to(DEV),
+                                   offs.to(DEV), total, out_dtype=out_dtype)
+
+
+def test_decode_attention_lengths(lib):
+    lens = [1, 15, 16, 17, 255, 256, 257, 1000, 4097]
+    say("decode lengths", lens)
+    lens_t, table, q, kp, vp = make_decode(lens, seed=100)
+    out = run_decode(lib, lens_t, table, q, kp, vp)
+    ref = O.decode_attention(bits(q), bits(kp), bits(vp), table.numpy(), lens, 128 ** -0.5)
+    assert_close(f32(out), ref, "decode")
+    outb = run_decode(lib, lens_t, table, q, kp, vp, torch.bfloat16)
+    assert same_bits(outb, rne_bf16(out))
+
+
+def test_decode_attention_single_token_is_v0(lib):
+    say("decode L=1")
+    lens_t, table, q, kp, vp = make_decode([1, 1, 1], seed=110)
+    out = run_decode(lib, lens_t, table, q, kp, vp)
+    for b in range(3):
+        for h in range(32):
+            v0 = vp[table[b, 0], h // 4, 0].float()
+            assert same_bits(out[b, h].cpu(), v0)
+
+
+def test_decode_attention_config_batch(lib):
+    """A log-uniform batch (lengths in [1, 32768]), sampled sequences."""
+    lens_t = S.context_lens(64, seed=120)
+    say("decode batch64 total tokens", int(lens_t.sum()))
+    table, npages = S.paged_kv_layout(lens_t, 16, seed=121)
+    q = S.normal_bf16((64, 32, 128), 1.0, seed=122, device=DEV)
+    kp = S.normal_bf16((npages, 8, 16, 128), 1.0, seed=123, device=DEV)
+    vp = S.normal_bf16((npages, 8, 16, 128), 1.0, seed=124, device=DEV)
+    offs, total = lib.bi_decode_plan(lens_t)
+    out = lib.bi_decode_attention(q, kp, vp, table.to(DEV), lens_t.to(DEV), offs.to(DEV), total)
+    seqs = [0, 1, int(torch.argmax(lens_t)), int(torch.argmin(lens_t)), 63]
+    ref = O.decode_attention(bits(q), bits(kp), bits(vp), table.numpy(), lens_t.numpy(), 128 ** -0.5, seqs=seqs)
+    assert_close(f32(out[seqs]), ref[seqs], "decode batch")
