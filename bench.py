@@ -1,0 +1,335 @@
+#!/usr/bin/env python3
+"""Benchmark of the batch-invariant hot path on one MI355X.
+
+One step runs every kernel of the path once, on synthetic Qwen3-8B-shaped
+inputs already resident in HBM:
+  gemm_qkv     bi_mm  A[4096,4096] @ W[4096,6144]     -> fp32
+  gemm_o       bi_mm  A[4096,4096] @ W[4096,4096]     -> fp32
+  gemm_gateup  bi_mm  A[4096,4096] @ W[4096,24576]    -> fp32
+  gemm_down    bi_mm  A[4096,12288] @ W[12288,4096]   -> fp32
+  lm_head      bi_addmm X[256,4096] @ W[4096,151936] + bias -> fp32 logits
+  lm_logsm     bi_log_softmax + argmax over those logits [256,151936]
+  rmsnorm      bi_rmsnorm x[2048,4096] bf16 -> bf16
+  mean         bi_mean x[2048,4096] bf16 -> fp32
+  logsm        bi_log_softmax + argmax x[2048,151936] fp32
+  decode_attn  bi_decode_attention, B=256, lengths log-uniform in [1,32768]
+Each kernel has a roofline time t_min = max(flops / 2.5 PFLOP/s, bytes /
+8 TB/s) from its algorithmic flops and bytes. ``value`` is the whole step's
+roofline fraction: sum of t_min over the step / measured step time, in %.
+
+Prints ONE JSON line on stdout; a human-readable table goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5e15   # MI355X dense bf16 MFMA, FLOP/s (published)
+PEAK_HBM = 8.0e12    # MI355X HBM3E, B/s (published)
+METRIC = "invariant bf16 GEMM TFLOP/s & reduction GB/s (% roofline), M=1..4096, 1 GPU"
+
+GEMMS = [("gemm_qkv", 4096, 6144), ("gemm_o", 4096, 4096), ("gemm_gateup", 4096, 24576), ("gemm_down", 12288, 4096)]
+M_GEMM = 4096
+M_LM = 256
+M_ROWS = 2048
+HIDDEN = 4096
+VOCAB = 151936
+B_DECODE = 256
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_work(m, n, k, out_bytes=4, bias=False):
+    flops = 2.0 * m * n * k
+    byts = 2.0 * (m * k + k * n) + out_bytes * m * n + (2.0 * n if bias else 0.0)
+    return flops, byts
+
+
+def t_min(flops, byts):
+    return max(flops / PEAK_BF16, byts / PEAK_HBM)
+
+
+class Workload:
+    """All inputs and outputs of one step, generated on the GPU from seeds."""
+
+    def __init__(self, torch, S, bi, dev):
+        self.torch, self.bi = torch, bi
+        t0 = time.time()
+        self.gemm = []
+        for i, (name, k, n) in enumerate(GEMMS):
+            a = S.normal_bf16((M_GEMM, k), 1.0, seed=3000 + i, device=dev)
+            w = S.normal_bf16((k, n), 0.02, seed=3100 + i, device=dev)
+            c = torch.empty((M_GEMM, n), dtype=torch.float32, device=dev)
+            self.gemm.append((name, a, w, c, k, n))
+        self.lm_x = S.normal_bf16((M_LM, HIDDEN), 1.0, seed=4000, device=dev)
+        self.lm_w = S.normal_bf16((HIDDEN, VOCAB), 0.02, seed=4001, device=dev)
+        self.lm_b = S.normal_bf16((VOCAB,), 0.1, seed=4002, device=dev)
+        self.lm_logits = torch.empty((M_LM, VOCAB), dtype=torch.float32, device=dev)
+        self.lm_lp = torch.empty_like(self.lm_logits)
+        self.lm_am = torch.empty((M_LM,), dtype=torch.int64, device=dev)
+        self.rx = S.normal_bf16((M_ROWS, HIDDEN), 1.0, seed=1000, device=dev)
+        self.rw = S.uniform_bf16((HIDDEN,), 0.5, 1.5, seed=1001, device=dev)
+        self.ry = torch.empty_like(self.rx)
+        self.rmean = torch.empty((M_ROWS,), dtype=torch.float32, device=dev)
+        self.lx = S.normal_f32((M_ROWS, VOCAB), 4.0, seed=1002, device=dev)
+        self.ly = torch.empty_like(self.lx)
+        self.lam = torch.empty((M_ROWS,), dtype=torch.int64, device=dev)
+        self.lens = S.context_lens(B_DECODE, seed=5000)
+        table, npages = S.paged_kv_layout(self.lens, 16, seed=5001)
+        self.q = S.normal_bf16((B_DECODE, 32, 128), 1.0, seed=5002, device=dev)
+        self.kp = S.normal_bf16((npages, 8, 16, 128), 1.0, seed=5003, device=dev)
+        self.vp = S.normal_bf16((npages, 8, 16, 128), 1.0, seed=5004, device=dev)
+        self.table = table.to(dev)
+        self.table_host = table
+        self.lens_dev = self.lens.to(dev)
+        offs, self.total_splits = bi.bi_decode_plan(self.lens)
+        self.offs = offs.to(dev)
+        self.ws = torch.empty(bi.bi_decode_workspace_bytes(self.total_splits, 32, 128), dtype=torch.uint8, device=dev)
+        self.attn_out = torch.empty((B_DECODE, 32, 128), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        log(f"inputs generated in {time.time() - t0:.1f}s; decode tokens={int(self.lens.sum())} "
+            f"splits={self.total_splits}")
+
+    def ops(self):
+        """(name, callable, flops, bytes) for every kernel launch group of a step."""
+        bi = self.bi
+        out = []
+        for name, a, w, c, k, n in self.gemm:
+            f, b = gemm_work(M_GEMM, n, k)
+            out.append((name, (lambda a=a, w=w, c=c: bi.bi_mm(a, w, out=c)), f, b))
+        f, b = gemm_work(M_LM, VOCAB, HIDDEN, bias=True)
+        out.append(("lm_head", lambda: bi.bi_addmm(self.lm_b, self.lm_x, self.lm_w, out=self.lm_logits), f, b))
+        out.append(("lm_logsm", lambda: bi.bi_log_softmax(self.lm_logits, out=self.lm_lp, argmax=self.lm_am),
+                    5.0 * M_LM * VOCAB, 8.0 * M_LM * VOCAB + 8 * M_LM))
+        out.append(("rmsnorm", lambda: bi.bi_rmsnorm(self.rx, self.rw, 1e-6, out=self.ry),
+                    4.0 * M_ROWS * HIDDEN, 4.0 * M_ROWS * HIDDEN + 2 * HIDDEN))
+        out.append(("mean", lambda: bi.bi_mean(self.rx, out=self.rmean),
+                    1.0 * M_ROWS * HIDDEN, 2.0 * M_ROWS * HIDDEN + 4 * M_ROWS))
+        out.append(("logsm", lambda: bi.bi_log_softmax(self.lx, out=self.ly, argmax=self.lam),
+                    5.0 * M_ROWS * VOCAB, 8.0 * M_ROWS * VOCAB + 8 * M_ROWS))
+        tokens = int(self.lens.sum())
+        pages = int(((self.lens + 15) // 16).sum())
+        attn_bytes = 4096.0 * tokens + B_DECODE * 32 * 128 * (2 + 4) + 4.0 * pages
+        attn_flops = 4.0 * 32 * 128 * tokens
+        out.append(("decode_attn", lambda: bi.bi_decode_attention(
+            self.q, self.kp, self.vp, self.table, self.lens_dev, self.offs, self.total_splits,
+            workspace=self.ws, out=self.attn_out), attn_flops, attn_bytes))
+        return out
+
+    def torch_ops(self):
+        """The same work through torch's own (non-invariant) kernels."""
+        torch = self.torch
+        F = torch.nn.functional
+        out = []
+        for name, a, w, c, k, n in self.gemm:
+            out.append((name, (lambda a=a, w=w: torch.mm(a, w, out_dtype=torch.float32))))
+        out.append(("lm_head", lambda: torch.addmm(self.lm_b, self.lm_x, self.lm_w, out_dtype=torch.float32)))
+        out.append(("lm_logsm", lambda: (torch.log_softmax(self.lm_logits, -1), torch.argmax(self.lm_logits, -1))))
+        out.append(("rmsnorm", lambda: F.rms_norm(self.rx, (HIDDEN,), self.rw, 1e-6)))
+        out.append(("mean", lambda: torch.mean(self.rx, dim=1, dtype=torch.float32)))
+        out.append(("logsm", lambda: (torch.log_softmax(self.lx, -1), torch.argmax(self.lx, -1))))
+        return out
+
+
+def time_step(torch, ops, steps, warmup):
+    """Run `warmup` untimed steps, then `steps` timed steps bracketed by
+    synchronize; every launch group is also bracketed by HIP events on the
+    stream the kernels run on. Returns (ms per step, {name: avg ms})."""
+    for _ in range(warmup):
+        for _, fn, *_ in ops:
+            fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        for (name, fn, *_), (e0, e1) in zip(ops, evs[s]):
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    per = {}
+    for i, (name, *_) in enumerate(ops):
+        per[name] = sum(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(steps)) / steps
+    return wall, per
+
+
+def cpu_baseline(wl, S):
+    """The fp64 oracle on a bounded sample of the same step, extrapolated by
+    the work ratio of each kernel."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        ncores = len(os.sched_getaffinity(0))
+        threadpool_limits(ncores)
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    bits = S.bf16_bits_numpy
+    total = 0.0
+    parts = {}
+
+    def timed(fn):
+        t = time.perf_counter()
+        fn()
+        return time.perf_counter() - t
+
+    # GEMMs: 128 rows x 2048 columns of each projection, scaled by flops
+    for name, a, w, c, k, n in wl.gemm:
+        ab, wb = bits(a[:128]), bits(w[:, :2048])
+        t = timed(lambda: O.mm(ab, wb)) * (M_GEMM * n) / (128 * 2048)
+        parts[name] = t
+    xb, wb, bb = bits(wl.lm_x[:32]), bits(wl.lm_w[:, :4096]), bits(wl.lm_b[:4096])
+    parts["lm_head"] = timed(lambda: O.addmm(bb, xb, wb)) * (M_LM * VOCAB) / (32 * 4096)
+    lg = S.f32_numpy(wl.lm_logits[:16])
+    parts["lm_logsm"] = timed(lambda: (O.log_softmax(lg), O.argmax(lg))) * M_LM / 16
+    rx, rw = bits(wl.rx[:256]), bits(wl.rw)
+    parts["rmsnorm"] = timed(lambda: O.rmsnorm(rx, rw, 1e-6)) * M_ROWS / 256
+    parts["mean"] = timed(lambda: O.mean(rx)) * M_ROWS / 256
+    lx = S.f32_numpy(wl.lx[:32])
+    parts["logsm"] = timed(lambda: (O.log_softmax(lx), O.argmax(lx))) * M_ROWS / 32
+    # decode attention: 3 sequences (their pages only), scaled by tokens
+    lens = wl.lens.numpy()
+    seqs = [int(np.argsort(lens)[len(lens) // 2]), 0, 1]
+    kp = bits(wl.kp)
+    vp = bits(wl.vp)
+    q = bits(wl.q)
+    tb = wl.table_host.numpy()
+    ta = timed(lambda: O.decode_attention(q, kp, vp, tb, lens, 128 ** -0.5, seqs=seqs))
+    parts["decode_attn"] = ta * float(lens.sum()) / float(lens[seqs].sum())
+    total = sum(parts.values())
+    sample = ("oracle (numpy fp64) on: 128 rows x 2048 cols per projection GEMM, 32 rows x 4096 cols of the "
+              "LM head, 16 rows of LM-head log_softmax, 256 rows of RMSNorm/mean, 32 rows of the 2048-row "
+              "log_softmax, 3 decode sequences; each extrapolated to the full step by its work ratio")
+    return total, parts, threads, sample
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
+    ap.add_argument("--no-torch", action="store_true", help="skip the non-invariant torch baseline")
+    ap.add_argument("--traffic", default=None, help="JSON with measured HBM traffic of the dominant kernel")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(see the sharding paragraph in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import invariant_bi_mm_amd as bi
+    import synthetic as S
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    wl = Workload(torch, S, bi, dev)
+    ops = wl.ops()
+    ms_step, per = time_step(torch, ops, args.steps, args.warmup)
+    tmin = {name: t_min(f, b) for name, _, f, b in ops}
+    work = {name: (f, b) for name, _, f, b in ops}
+    sum_tmin_ms = sum(tmin.values()) * 1e3
+    value = 100.0 * sum_tmin_ms / ms_step
+
+    log(f"{'kernel':12s} {'ms':>9s} {'t_min ms':>9s} {'frac':>6s} {'TFLOP/s':>9s} {'GB/s':>9s}")
+    for name, *_ in ops:
+        f, b = work[name]
+        log(f"{name:12s} {per[name]:9.4f} {tmin[name] * 1e3:9.4f} {tmin[name] * 1e3 / per[name]:6.3f} "
+            f"{f / per[name] / 1e9:9.1f} {b / per[name] / 1e6:9.1f}")
+    log(f"step: {ms_step:.3f} ms (sum of kernel events {sum(per.values()):.3f} ms), "
+        f"sum t_min {sum_tmin_ms:.3f} ms -> {value:.1f}% of roofline")
+
+    gemm_names = [g[0] for g in GEMMS] + ["lm_head"]
+    red_names = ["rmsnorm", "mean", "logsm", "lm_logsm"]
+
+    def group(names, use_flops):
+        t = sum(per[n] for n in names) / 1e3
+        amount = sum(work[n][0 if use_flops else 1] for n in names)
+        frac = sum(tmin[n] for n in names) / t
+        return amount / t, frac
+
+    g_tf, g_frac = group(gemm_names, True)
+    r_bw, r_frac = group(red_names, False)
+    a_bw, a_frac = group(["decode_attn"], False)
+
+    dom = max(per, key=lambda n: per[n])
+    f, b = work[dom]
+    is_mfma = f / PEAK_BF16 >= b / PEAK_HBM
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as fh:
+            traffic = json.load(fh).get(dom)
+    if is_mfma:
+        roof = {"bound": "mfma", "achieved": f / (per[dom] / 1e3) / 1e12, "peak": PEAK_BF16 / 1e12,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": b / (per[dom] / 1e3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic
+    roof["kernel"] = dom
+    roof["algorithmic_per_launch"] = {"flops": f, "bytes": b}
+    roof["avg_launch_ms"] = per[dom]
+
+    torch_base = None
+    if not args.no_torch:
+        tops = [(n, fn, *work[n]) for n, fn in wl.torch_ops()]
+        t_ms, t_per = time_step(torch, tops, max(5, args.steps // 2), 2)
+        bi_same = sum(per[n] for n in t_per)
+        torch_base = {"ms_per_step_without_decode": t_ms, "per_kernel_ms": {k: round(v, 4) for k, v in t_per.items()},
+                      "invariance_tax": bi_same / sum(t_per.values()),
+                      "note": "torch.mm/addmm with out_dtype=float32 (hipBLASLt/rocBLAS as dispatched), F.rms_norm, torch.mean, "
+                              "torch.log_softmax+argmax on the same tensors; decode attention has no torch "
+                              "counterpart here"}
+        log(f"torch baseline: {t_ms:.3f} ms/step (no decode); tax bi/torch on the same kernels "
+            f"{torch_base['invariance_tax']:.3f}x")
+
+    cpu = None
+    if not args.no_cpu:
+        t_cpu, parts, threads, sample = cpu_baseline(wl, S)
+        cpu = {"value": 100.0 * sum_tmin_ms / (t_cpu * 1e3), "unit": "% of MI355X roofline (same step)",
+               "cores": threads, "kind": "oracle", "sample": sample,
+               "step_seconds_extrapolated": t_cpu,
+               "per_kernel_seconds": {k: round(v, 3) for k, v in parts.items()}}
+        log(f"cpu oracle: {t_cpu:.1f} s per step (extrapolated), threads={threads}")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "% roofline (sum of per-kernel roofline times / measured step time)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Qwen3-8B-shaped invariant step: 4 projection GEMMs at M=4096 (fp32 out), "
+                               "LM-head addmm M=256 + log_softmax/argmax, RMSNorm+mean 2048x4096, "
+                               "log_softmax+argmax 2048x151936, decode attention B=256 (split 256)",
+                   "gemm_m": M_GEMM, "lm_head_m": M_LM, "row_m": M_ROWS, "decode_batch": B_DECODE,
+                   "decode_tokens": int(wl.lens.sum()), "accumulate": "fp32"},
+        "components": {
+            "gemm": {"TFLOP/s": round(g_tf / 1e12, 2), "frac": round(g_frac, 4)},
+            "reductions": {"GB/s": round(r_bw / 1e9, 1), "frac": round(r_frac, 4)},
+            "decode_attention": {"GB/s": round(a_bw / 1e9, 1), "frac": round(a_frac, 4)},
+        },
+        "per_kernel_ms": {k: round(v, 4) for k, v in per.items()},
+        "roofline": roof,
+        "torch_baseline": torch_base,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
