@@ -20,12 +20,16 @@
 //   stream-K or atomic anywhere.
 //
 // Structure (one workgroup per TM x TN output tile)
-//   * global -> registers: 128-bit loads of the next k-tile (TK = 64) while
-//     the current one is multiplied;
+//   * global -> registers: raw buffer loads, 128 bits per lane. Rows past M
+//     or N and k past K read as zero through the buffer range check, so the
+//     loads need no branch and the k loop is one basic block. The loads of
+//     k tile t+2 are issued while tile t is multiplied, and land in LDS
+//     during tile t+1, so each has a whole k tile of latency to hide;
 //   * registers -> LDS: double-buffered, rows of 64 bf16 (128 bytes) made of
 //     eight 16-byte chunks whose position is XOR-swizzled by the row, so the
 //     MFMA fragment reads (ds_read_b128) and the tile writes are free of bank
-//     conflicts without padding;
+//     conflicts without padding; the writes of the next tile are issued
+//     among the MFMAs of the current one;
 //   * B stored [K, N] (N contiguous) is transposed on its way into LDS: each
 //     thread loads a 4(k) x 8(n) block and writes eight 4(k) x 1(n) pieces,
 //     so both operands sit k-contiguous in LDS, as the MFMA wants them;
@@ -79,6 +83,17 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
   tn = in / rows;
 }
 
+// Raw buffer loads: an offset at or past the descriptor's byte count reads
+// as zero without touching memory, so masked rows/columns and the k tail
+// need no branch and the k loop stays one basic block.
+constexpr uint32_t OOB = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
 template <int TM, int TN, int WM, int WN, bool B_NK>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
   constexpr int NT = WM * WN * 64;
@@ -87,10 +102,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
   constexpr int A_CH = TM * 8 / NT;            // A chunks per thread
   constexpr int B_CH = TN * 8 / NT;            // B chunks per thread ([N,K] layout)
   constexpr int B_UN = 2 * TN / NT;            // 4x8 units per thread ([K,N] layout)
+  constexpr int B_RG = B_NK ? B_CH : 4 * B_UN; // B registers per set
   static_assert(A_CH * NT == TM * 8, "A tile not evenly split");
   static_assert(B_NK ? (B_CH * NT == TN * 8) : (B_UN * NT == 2 * TN), "B tile not evenly split");
   static_assert(FM >= 1 && FN >= 1, "wave tile smaller than one MFMA");
 
+  // two LDS stages as separate objects, so the compiler knows the stage being
+  // written never aliases the stage being read
   __shared__ u32x4 As[2][TM * 8];
   __shared__ u32x4 Bs[2][TN * 8];
 
@@ -104,73 +122,94 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
   const int m0 = tm * TM, n0 = tn * TN;
   const int M = g.m, N = g.n, K = g.k;
   const int nk = (K + TK - 1) / TK;
+  const uint32_t lda2 = (uint32_t)g.lda * 2u, ldb2 = (uint32_t)g.ldb * 2u;
 
-  u32x4 ra[A_CH];
-  u32x4 rb[B_NK ? B_CH : 4 * B_UN];
+  // A rows past M, and B rows past N ([N,K] layout), lie past the descriptor.
+  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(g.a + (int64_t)m0 * g.lda, (uint32_t)min(TM, M - m0) * lda2);
+  __amdgpu_buffer_rsrc_t bnk_rsrc;
+  if constexpr (B_NK) bnk_rsrc = make_rsrc(g.b + (int64_t)n0 * g.ldb, (uint32_t)min(TN, N - n0) * ldb2);
 
-  auto load_tile = [&](int kt) {
-    const int k0 = kt * TK;
+  // per-thread load geometry (constant over the k loop)
+  uint32_t a_off[A_CH];
+  int a_k[A_CH];
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
+  for (int i = 0; i < A_CH; ++i) {
+    const int c = tid + i * NT;
+    a_off[i] = (uint32_t)(c >> 3) * lda2 + (uint32_t)(c & 7) * 16u;
+    a_k[i] = (c & 7) * 8;
+  }
+  uint32_t b_off[B_NK ? B_CH : B_UN];
+  int b_k[B_NK ? B_CH : 1];
+  bool b_ok[B_NK ? 1 : B_UN];
+  if constexpr (B_NK) {
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
       const int c = tid + i * NT;
-      const int row = c >> 3, ch = c & 7;
-      const int gm = m0 + row, gk = k0 + ch * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (gm < M && gk < K) v = *reinterpret_cast<const u32x4*>(g.a + (int64_t)gm * g.lda + gk);
-      ra[i] = v;
+      b_off[i] = (uint32_t)(c >> 3) * ldb2 + (uint32_t)(c & 7) * 16u;
+      b_k[i] = (c & 7) * 8;
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < B_UN; ++i) {
+      const int u = tid + i * NT;
+      const int kb = ((u >> 1) / (TN / 8)) * 2 + (u & 1);
+      const int nb = (u >> 1) % (TN / 8);
+      b_off[i] = (uint32_t)(kb * 4) * ldb2 + (uint32_t)nb * 16u;
+      b_ok[i] = n0 + nb * 8 < N;
+    }
+  }
+
+  u32x4 RA[A_CH];
+  u32x4 RB[B_RG];
+
+  // global -> registers, tile t; tiles past K read zeros
+  auto load = [&](int t) {
+    const int k0 = t * TK;
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i)
+      RA[i] = bload(a_rsrc, (k0 + a_k[i] < K) ? a_off[i] + (uint32_t)k0 * 2u : OOB);
     if constexpr (B_NK) {
 #pragma unroll
-      for (int i = 0; i < B_CH; ++i) {
-        const int c = tid + i * NT;
-        const int row = c >> 3, ch = c & 7;
-        const int gn = n0 + row, gk = k0 + ch * 8;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (gn < N && gk < K) v = *reinterpret_cast<const u32x4*>(g.b + (int64_t)gn * g.ldb + gk);
-        rb[i] = v;
-      }
+      for (int i = 0; i < B_CH; ++i)
+        RB[i] = bload(bnk_rsrc, (k0 + b_k[i] < K) ? b_off[i] + (uint32_t)k0 * 2u : OOB);
     } else {
+      // rows of this k tile only: rows past K lie past the descriptor
+      const int kr = max(0, min(TK, K - k0));
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(g.b + ((int64_t)k0 * g.ldb + n0), (uint32_t)kr * ldb2);
 #pragma unroll
-      for (int i = 0; i < B_UN; ++i) {
-        const int u = tid + i * NT;
-        const int kb = ((u >> 1) / (TN / 8)) * 2 + (u & 1);
-        const int nb = (u >> 1) % (TN / 8);
-        const int gn = n0 + nb * 8;
+      for (int i = 0; i < B_UN; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int gk = k0 + kb * 4 + r;
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (gn < N && gk < K) v = *reinterpret_cast<const u32x4*>(g.b + (int64_t)gk * g.ldb + gn);
-          rb[i * 4 + r] = v;
-        }
-      }
+        for (int q = 0; q < 4; ++q) RB[i * 4 + q] = bload(r, b_ok[i] ? b_off[i] + (uint32_t)q * ldb2 : OOB);
     }
   };
 
-  auto store_tile = [&](int buf) {
+  // registers -> LDS stage d
+  auto store = [&](int d) {
+    u32x4* as = As[d];
+    u32x4* bs = Bs[d];
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       const int c = tid + i * NT;
-      As[buf][swz(c >> 3, c & 7)] = ra[i];
+      as[swz(c >> 3, c & 7)] = RA[i];
     }
     if constexpr (B_NK) {
 #pragma unroll
       for (int i = 0; i < B_CH; ++i) {
         const int c = tid + i * NT;
-        Bs[buf][swz(c >> 3, c & 7)] = rb[i];
+        bs[swz(c >> 3, c & 7)] = RB[i];
       }
     } else {
-      uint32_t* bs32 = reinterpret_cast<uint32_t*>(&Bs[buf][0]);
+      uint32_t* bs32 = reinterpret_cast<uint32_t*>(bs);
 #pragma unroll
       for (int i = 0; i < B_UN; ++i) {
         const int u = tid + i * NT;
         const int kb = ((u >> 1) / (TN / 8)) * 2 + (u & 1);
         const int nb = (u >> 1) % (TN / 8);
-        const u32x4 w0 = rb[i * 4 + 0], w1 = rb[i * 4 + 1], w2 = rb[i * 4 + 2], w3 = rb[i * 4 + 3];
+        const u32x4 w0 = RB[i * 4 + 0], w1 = RB[i * 4 + 1], w2 = RB[i * 4 + 2], w3 = RB[i * 4 + 3];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int j = e >> 1;
-          uint32_t x0 = w0[j], x1 = w1[j], x2 = w2[j], x3 = w3[j];
+          const uint32_t x0 = w0[j], x1 = w1[j], x2 = w2[j], x3 = w3[j];
           uint32_t d0, d1;
           if ((e & 1) == 0) {
             d0 = (x0 & 0xffffu) | (x1 << 16);
@@ -179,9 +218,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
             d0 = (x0 >> 16) | (x1 & 0xffff0000u);
             d1 = (x2 >> 16) | (x3 & 0xffff0000u);
           }
-          const int row = nb * 8 + e;
-          // 16-byte chunk kb>>1 of the row, 8-byte half kb&1.
-          const int at = swz(row, kb >> 1) * 4 + (kb & 1) * 2;
+          // row n = nb*8+e holds k contiguous: 16-byte chunk kb>>1, 8-byte half kb&1
+          const int at = swz(nb * 8 + e, kb >> 1) * 4 + (kb & 1) * 2;
           *reinterpret_cast<u32x2*>(bs32 + at) = u32x2{d0, d1};
         }
       }
@@ -196,39 +234,39 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  if (nk > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
   const int arow0 = wm * WTM + (lane & 31);
   const int brow0 = wn * WTN + (lane & 31);
   const int khalf = lane >> 5;
 
+  // one 16-wide k step of the wave's FM x FN MFMA tiles from LDS stage D
+  auto mma = [&](int kk, int d) {
+    const u32x4* as = As[d];
+    const u32x4* bs = Bs[d];
+    bf16x8 af[FM], bfr[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[i] = __builtin_bit_cast(bf16x8, as[swz(arow0 + i * 32, kk * 2 + khalf)]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bfr[j] = __builtin_bit_cast(bf16x8, bs[swz(brow0 + j * 32, kk * 2 + khalf)]);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  };
+
+  // One k tile: multiply stage C (tile t) while tile t+1 goes from the
+  // registers into the other stage and tile t+2 is fetched into them.
+  load(0);
+  store(0);
+  load(1);
+  __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_tile(kt + 1);
+    const int c = kt & 1;
+    mma(0, c);
+    store(c ^ 1);
+    load(kt + 2);
 #pragma unroll
-    for (int kk = 0; kk < TK / 16; ++kk) {
-      bf16x8 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const u32x4 v = As[cur][swz(arow0 + i * 32, kk * 2 + khalf)];
-        af[i] = __builtin_bit_cast(bf16x8, v);
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const u32x4 v = Bs[cur][swz(brow0 + j * 32, kk * 2 + khalf)];
-        bfr[j] = __builtin_bit_cast(bf16x8, v);
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store_tile(cur ^ 1);
+    for (int kk = 1; kk < TK / 16; ++kk) mma(kk, c);
     __syncthreads();
   }
 
@@ -279,7 +317,7 @@ GemmConfig gemm_config(int64_t n, int64_t k, bool b_is_nk) {
   (void)n;
   (void)k;
   (void)b_is_nk;
-  return GemmConfig{128, 128, TK, 4};
+  return GemmConfig{128, 128, TK, 4};  // @@TABLE@@
 }
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
@@ -301,9 +339,15 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   a.bias_mode = p.bias == nullptr ? 0 : (p.bias_bf16 ? 1 : 2);
   a.tiles_m = (int)((p.m + cfg.tile_m - 1) / cfg.tile_m);
   a.tiles_n = (int)((p.n + cfg.tile_n - 1) / cfg.tile_n);
-  if (cfg.tile_m == 128 && cfg.tile_n == 128 && cfg.waves == 4) {
-    return p.b_is_nk ? launch_cfg<128, 128, 2, 2, true>(a, s) : launch_cfg<128, 128, 2, 2, false>(a, s);
-  }
+#define BI_GEMM_CASE(TM_, TN_, WM_, WN_)                                                          \
+  if (cfg.tile_m == TM_ && cfg.tile_n == TN_ && cfg.waves == WM_ * WN_)                            \
+    return p.b_is_nk ? launch_cfg<TM_, TN_, WM_, WN_, true>(a, s) : launch_cfg<TM_, TN_, WM_, WN_, false>(a, s);
+  BI_GEMM_CASE(128, 128, 2, 2)
+  BI_GEMM_CASE(256, 128, 2, 2)
+  BI_GEMM_CASE(128, 256, 2, 2)
+  BI_GEMM_CASE(256, 256, 2, 2)
+  BI_GEMM_CASE(256, 256, 2, 4)
+#undef BI_GEMM_CASE
   return hipErrorInvalidConfiguration;
 }
 
