@@ -23,8 +23,9 @@
 //   * global -> registers: raw buffer loads, 128 bits per lane. Rows past M
 //     or N and k past K read as zero through the buffer range check, so the
 //     loads need no branch and the k loop is one basic block. The loads of
-//     k tile t+2 are issued while tile t is multiplied, and land in LDS
-//     during tile t+1, so each has a whole k tile of latency to hide;
+//     k tile t+1 are issued at the start of tile t and written to LDS after
+//     three of its four k steps, so they land behind most of a tile of
+//     MFMA work;
 //   * registers -> LDS: double-buffered, rows of 64 bf16 (128 bytes) made of
 //     eight 16-byte chunks whose position is XOR-swizzled by the row, so the
 //     MFMA fragment reads (ds_read_b128) and the tile writes are free of bank
@@ -173,9 +174,16 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
       for (int i = 0; i < B_CH; ++i)
         RB[i] = bload(bnk_rsrc, (k0 + b_k[i] < K) ? b_off[i] + (uint32_t)k0 * 2u : OOB);
     } else {
-      // rows of this k tile only: rows past K lie past the descriptor
+      // rows of this k tile only: rows past K lie past the descriptor. The
+      // base and size are workgroup-uniform; readfirstlane lets the compiler
+      // see that (a divergent descriptor would need a waterfall loop).
       const int kr = max(0, min(TK, K - k0));
-      const __amdgpu_buffer_rsrc_t r = make_rsrc(g.b + ((int64_t)k0 * g.ldb + n0), (uint32_t)kr * ldb2);
+      const uint64_t base = reinterpret_cast<uint64_t>(g.b + ((int64_t)k0 * g.ldb + n0));
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+      const uint32_t nbytes = __builtin_amdgcn_readfirstlane((uint32_t)kr * ldb2);
+      const __amdgpu_buffer_rsrc_t r =
+          make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), nbytes);
 #pragma unroll
       for (int i = 0; i < B_UN; ++i)
 #pragma unroll
@@ -238,15 +246,18 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
   const int brow0 = wn * WTN + (lane & 31);
   const int khalf = lane >> 5;
 
-  // one 16-wide k step of the wave's FM x FN MFMA tiles from LDS stage D
-  auto mma = [&](int kk, int d) {
+  // Fragments of one 16-wide k step from LDS stage d, and the FM x FN MFMAs
+  // that consume them. The k loop below keeps two fragment sets so the LDS
+  // reads of step kk+1 are in flight while the MFMAs of step kk run.
+  auto frags = [&](int kk, int d, bf16x8* af, bf16x8* bfr) {
     const u32x4* as = As[d];
     const u32x4* bs = Bs[d];
-    bf16x8 af[FM], bfr[FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i) af[i] = __builtin_bit_cast(bf16x8, as[swz(arow0 + i * 32, kk * 2 + khalf)]);
 #pragma unroll
     for (int j = 0; j < FN; ++j) bfr[j] = __builtin_bit_cast(bf16x8, bs[swz(brow0 + j * 32, kk * 2 + khalf)]);
+  };
+  auto mma = [&](const bf16x8* af, const bf16x8* bfr) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -254,19 +265,26 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
   };
 
-  // One k tile: multiply stage C (tile t) while tile t+1 goes from the
-  // registers into the other stage and tile t+2 is fetched into them.
   load(0);
   store(0);
-  load(1);
   __syncthreads();
+  static_assert(TK / 16 == 4, "the k step pipeline below assumes four 16-wide steps per tile");
+  bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
   for (int kt = 0; kt < nk; ++kt) {
     const int c = kt & 1;
-    mma(0, c);
+    // Fetch tile kt+1 now; it is written to the other LDS stage after three
+    // of this tile's four k steps, so the loads have most of a tile of MFMA
+    // work to land behind.
+    load(kt + 1);
+    frags(0, c, fa0, fb0);
+    frags(1, c, fa1, fb1);
+    mma(fa0, fb0);
+    frags(2, c, fa0, fb0);
+    mma(fa1, fb1);
+    frags(3, c, fa1, fb1);
+    mma(fa0, fb0);
     store(c ^ 1);
-    load(kt + 2);
-#pragma unroll
-    for (int kk = 1; kk < TK / 16; ++kk) mma(kk, c);
+    mma(fa1, fb1);
     __syncthreads();
   }
 
@@ -312,11 +330,22 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 }  // namespace
 
 // The configuration table. It is keyed by (n, k, layout) only; m is not an
-// input, so no batch size can select a different tile or instruction.
+// input, so no batch size can select a different tile or instruction. (Every
+// configuration also runs the same per-element chain -- one 32x32x16 MFMA
+// per 16 k, in increasing k -- so the choice moves work between workgroups
+// without changing any output bit.)
+//
+// Choice, measured on MI355X for the Qwen3-8B projection shapes: a 256x256
+// tile with 8 waves (each 128x64) is fastest at M >= 512 but gives only
+// ceil(M/256) * ceil(N/256) workgroups, so for N <= 6144 it leaves most of
+// the 256 CUs idle at M = 512; there, and for the wide LM head where small M
+// dominates, the 128x128 tile (4 waves, 64x64 each, two workgroups per CU)
+// wins on the geometric mean over M = 512 and 4096. Wide-N GEMMs with
+// moderate K (gate+up, N = 24576) have enough 256-wide column tiles at every
+// M >= 512 and take the big tile.
 GemmConfig gemm_config(int64_t n, int64_t k, bool b_is_nk) {
-  (void)n;
-  (void)k;
   (void)b_is_nk;
+  if (n >= 16384 && n <= 65536 && k <= 8192) return GemmConfig{256, 256, TK, 8};
   return GemmConfig{128, 128, TK, 4};  // @@TABLE@@
 }
 
