@@ -81,8 +81,10 @@ typedef enum { BI_BF16 = 0, BI_F32 = 1 } bi_dtype;
  * 16-wide MFMA steps, accumulated in fp32, one chain per element; no split-K,
  * stream-K or atomics. The tile configuration is chosen from (n, k, b_is_nk)
  * only, never from m (bi_gemm_config reports it).
- * Requirements: k % 8 == 0; with b_is_nk == 0 also n % 8 == 0
- * (BI_ERR_UNSUPPORTED otherwise). k == 0 or n == 0 with m > 0: C is zero-filled.
+ * Requirements: k % 8 == 0; with b_is_nk == 0 also n % 8 == 0; one tile's
+ * rows of A (tile_m * lda * 2 bytes) and of B (tile_n * ldb * 2 bytes when
+ * b_is_nk, else tile_k * ldb * 2) below 2^31 bytes (BI_ERR_UNSUPPORTED
+ * otherwise). k == 0 with m, n > 0: C = beta * bias (addmm) or zeros (mm).
  * ------------------------------------------------------------------------ */
 bi_status bi_mm(const void* a, int64_t lda, const void* b, int64_t ldb, int b_is_nk,
                 void* c, int64_t ldc, bi_dtype c_dtype,

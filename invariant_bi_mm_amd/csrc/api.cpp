@@ -58,6 +58,11 @@ bi_status check_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, int
   const bi::GemmConfig cfg = bi::gemm_config(n, k, b_is_nk != 0);
   const int64_t tiles = ((m + cfg.tile_m - 1) / cfg.tile_m) * ((n + cfg.tile_n - 1) / cfg.tile_n);
   if (tiles > INT_MAX) return fail(BI_ERR_UNSUPPORTED, "too many output tiles");
+  // the kernels address one tile's rows of A and B through 32-bit buffer
+  // descriptors: a tile's byte extent must stay below 2^31
+  const int64_t lim = int64_t(1) << 31;
+  if (2 * cfg.tile_m * lda >= lim || 2 * (b_is_nk ? cfg.tile_n : cfg.tile_k) * ldb >= lim)
+    return fail(BI_ERR_UNSUPPORTED, "leading dimension too large for one tile's 32-bit byte range");
   return BI_OK;
 }
 
@@ -218,7 +223,7 @@ bi_status bi_decode_attention(const void* q, const void* k_pages, const void* v_
   if (total_splits < batch || total_splits > batch * max_splits_per_seq)
     return fail(BI_ERR_SHAPE, "total_splits=%lld inconsistent with batch=%lld and max_pages=%lld",
                 (long long)total_splits, (long long)batch, (long long)max_pages);
-  if (total_splits > INT_MAX || batch > INT_MAX || num_kv_heads > 65535 || num_q_heads > 65535)
+  if (total_splits * num_kv_heads > INT_MAX || batch > INT_MAX || num_kv_heads > 65535 || num_q_heads > 65535)
     return fail(BI_ERR_UNSUPPORTED, "grid size out of range");
   const size_t need = bi_decode_workspace_bytes(total_splits, num_q_heads, head_dim);
   if (workspace == nullptr || workspace_bytes < need)

@@ -28,9 +28,10 @@
 //   phase 3: o = sum_t p_t v_t with the same token->group assignment, groups
 //            merged by butterfly inside a wave, waves merged in wave order.
 //   output : (max, sum p, o[128]) per (split, query head), fp32.
-// Kernel 2, one workgroup per (sequence, query head), lane d:
-//   M = max_s m_s; l = sum_s 2^(m_s - M) l_s; o = sum_s 2^(m_s - M) o_s[d] in
-//   increasing s; out = o / l.
+// Kernel 2, one workgroup per (sequence, query head):
+//   M = max_s m_s; l = sum_s 2^(m_s - M) l_s; o = sum_s 2^(m_s - M) o_s[d],
+//   each sum taken as (even splits in increasing s) + (odd splits in
+//   increasing s); out = o / l.
 #include "bi_internal.h"
 #include "device_common.h"
 
@@ -64,20 +65,28 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
   __shared__ float O[4][GQA][HD];
   __shared__ float ML[GQA][2];
 
-  const int w = blockIdx.x;  // global split index
-  const int g = blockIdx.y;  // kv head
+  // The kv heads of one split are adjacent in dispatch order, so the 4 KB
+  // head slices of a physical page (all heads, 32 KB at 8 heads) are read at
+  // about the same time.
+  const int w = blockIdx.x / a.hkv;  // global split index
+  const int g = blockIdx.x % a.hkv;  // kv head
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int grp = tid >> 4;  // 0..15
   const int dl = tid & 15;   // head-dim slice
 
-  // sequence owning split w: the largest b with offs[b] <= w
-  int lo = 0, hi = a.batch - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.offs[mid] <= w) lo = mid; else hi = mid - 1;
+  // sequence owning split w: the b with offs[b] <= w < offs[b+1]. The
+  // offsets are read with coalesced loads and compared in parallel (one
+  // memory round trip per 256 sequences instead of a dependent binary search).
+  __shared__ int sb;
+  if (tid == 0) sb = 0;
+  __syncthreads();
+  for (int base = 0; base < a.batch; base += 256) {
+    const int t = base + tid;
+    if (t < a.batch && a.offs[t] <= w && w < a.offs[t + 1]) sb = t;
   }
-  const int b = lo;
+  __syncthreads();
+  const int b = sb;
   const int s = w - a.offs[b];
   const int L = a.lens[b];
   const int t0 = s * SPLIT;
@@ -208,27 +217,63 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
   }
 }
 
-__global__ __launch_bounds__(HD) void decode_combine_kernel(const int32_t* __restrict__ offs,
-                                                             const float* __restrict__ ws_o,
-                                                             const float* __restrict__ ws_ml, int hq,
-                                                             void* __restrict__ out, int out_bf16) {
-  const int b = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+// Combine: one workgroup of 2 * HD threads per (sequence, query head). Thread
+// (half, d) folds the splits s = half, half + 2, half + 4, ... in increasing
+// order; the two halves are then added, half 0 first. The order depends only
+// on the sequence's split count.
+__global__ __launch_bounds__(2 * HD) void decode_combine_kernel(const int32_t* __restrict__ offs,
+                                                                 const float* __restrict__ ws_o,
+                                                                 const float* __restrict__ ws_ml, int hq,
+                                                                 void* __restrict__ out, int out_bf16) {
+  __shared__ float red[4];
+  __shared__ float part_o[HD], part_l;
+  const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int d = tid & (HD - 1), half = tid >> 7;
   const int w0 = offs[b], ns = offs[b + 1] - w0;
+  // exact max of the split maxima (max is order-free)
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, ws_ml[((int64_t)(w0 + s) * hq + h) * 2]);
+  for (int s = tid; s < ns; s += 2 * HD) M = fmaxf(M, ws_ml[((int64_t)(w0 + s) * hq + h) * 2]);
+  M = wave_max(M);
+  if ((tid & 63) == 0) red[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   float l = 0.0f, o = 0.0f;
-  for (int s = 0; s < ns; ++s) {
+  int s = half;
+  for (; s + 6 < ns; s += 8) {
+    float mv[4], lv[4], ov[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t ph = (int64_t)(w0 + s + 2 * u) * hq + h;
+      mv[u] = ws_ml[ph * 2];
+      lv[u] = ws_ml[ph * 2 + 1];
+      ov[u] = ws_o[ph * HD + d];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float c = __builtin_amdgcn_exp2f(mv[u] - M);
+      l = l + c * lv[u];
+      o = o + c * ov[u];
+    }
+  }
+  for (; s < ns; s += 2) {
     const int64_t ph = (int64_t)(w0 + s) * hq + h;
     const float c = __builtin_amdgcn_exp2f(ws_ml[ph * 2] - M);
     l = l + c * ws_ml[ph * 2 + 1];
     o = o + c * ws_o[ph * HD + d];
   }
-  const float r = o / l;
-  const int64_t at = ((int64_t)b * hq + h) * HD + d;
-  if (out_bf16)
-    reinterpret_cast<uint16_t*>(out)[at] = (uint16_t)f32_to_bf16_rne(r);
-  else
-    reinterpret_cast<float*>(out)[at] = r;
+  if (half == 1) {
+    part_o[d] = o;
+    if (d == 0) part_l = l;
+  }
+  __syncthreads();
+  if (half == 0) {
+    const float r = (o + part_o[d]) / (l + part_l);
+    const int64_t at = ((int64_t)b * hq + h) * HD + d;
+    if (out_bf16)
+      reinterpret_cast<uint16_t*>(out)[at] = (uint16_t)f32_to_bf16_rne(r);
+    else
+      reinterpret_cast<float*>(out)[at] = r;
+  }
 }
 
 }  // namespace
@@ -248,11 +293,10 @@ hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t s) {
   a.qscale = p.scale * LOG2E;
   a.ws_o = p.ws_o;
   a.ws_ml = p.ws_ml;
-  hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)p.total_splits, (unsigned)p.num_kv_heads), dim3(256), 0,
-                     s, a);
+  hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)(p.total_splits * p.num_kv_heads)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)p.batch, (unsigned)p.num_q_heads), dim3(HD), 0, s,
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)p.batch, (unsigned)p.num_q_heads), dim3(2 * HD), 0, s,
                      p.split_offsets, p.ws_o, p.ws_ml, p.num_q_heads, p.out, p.out_bf16 ? 1 : 0);
   return hipGetLastError();
 }

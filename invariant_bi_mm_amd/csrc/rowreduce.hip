@@ -198,11 +198,19 @@ __device__ __forceinline__ AM am_merge(AM a, AM b) {
   return take_b ? b : a;
 }
 
+// At most one workgroup per CU: the workgroup reserves more than half of the
+// 160 KB LDS, so 256 rows (~155 MB at n = 151936) are in flight at a time and
+// stay inside the 256 MB Infinity Cache; pass 2's re-read of a row is then
+// served from there instead of HBM.
+constexpr int LS_LDS_FLOATS = 22 * 1024;
 __global__ __launch_bounds__(LS_NT) void log_softmax_kernel(const float* __restrict__ x, int64_t ldx,
                                                              float* __restrict__ y, int64_t ldy,
                                                              int64_t* __restrict__ amax, int n) {
-  __shared__ float sm_m[LS_NT / 64], sm_s[LS_NT / 64], sm_v[LS_NT / 64];
-  __shared__ int sm_i[LS_NT / 64];
+  __shared__ float lds[LS_LDS_FLOATS];  // only the first 4 * 16 words are used (see above)
+  float* sm_m = lds;
+  float* sm_s = lds + LS_NT / 64;
+  float* sm_v = lds + 2 * (LS_NT / 64);
+  int* sm_i = reinterpret_cast<int*>(lds + 3 * (LS_NT / 64));
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
