@@ -140,6 +140,18 @@ class Workload:
         return out
 
 
+def source_digest():
+    """sha256 over the HIP sources; measured traffic is tied to it."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "invariant_bi_mm_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as fh:
+                h.update(name.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
 def time_step(torch, ops, steps, warmup):
     """Run `warmup` untimed steps, then `steps` timed steps bracketed by
     synchronize; every launch group is also bracketed by HIP events on the
@@ -224,8 +236,21 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--no-torch", action="store_true", help="skip the non-invariant torch baseline")
-    ap.add_argument("--traffic", default=None, help="JSON with measured HBM traffic of the dominant kernel")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
+                    help="measured HBM traffic per kernel (written from rocprofv3 FETCH_SIZE/WRITE_SIZE runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (for scaling the HBM counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        nbytes = 256 << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 5}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(see the sharding paragraph in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
@@ -271,7 +296,10 @@ def main():
     traffic = None
     if args.traffic and os.path.exists(args.traffic):
         with open(args.traffic) as fh:
-            traffic = json.load(fh).get(dom)
+            rec = json.load(fh)
+        # counters are only valid for the kernel sources they were taken on
+        if rec.get("source_sha256") == source_digest():
+            traffic = rec.get("kernels", {}).get(dom, {}).get("hbm_bytes_per_launch")
     if is_mfma:
         roof = {"bound": "mfma", "achieved": f / (per[dom] / 1e3) / 1e12, "peak": PEAK_BF16 / 1e12,
                 "unit": "TFLOP/s"}
