@@ -31,9 +31,10 @@
 //     MFMA fragment reads (ds_read_b128) and the tile writes are free of bank
 //     conflicts without padding; the writes of the next tile are issued
 //     among the MFMAs of the current one;
-//   * B stored [K, N] (N contiguous) is transposed on its way into LDS: each
-//     thread loads a 4(k) x 8(n) block and writes eight 4(k) x 1(n) pieces,
-//     so both operands sit k-contiguous in LDS, as the MFMA wants them;
+//   * B stored [K, N] (N contiguous) goes into LDS as it is, k rows of n,
+//     padded by 64 bytes; its MFMA fragments (8 consecutive k of one column
+//     per lane) come out through gfx950's transposing LDS read,
+//     ds_read_b64_tr_b16, two per fragment. B stored [N, K] is staged like A;
 //   * epilogue straight from the accumulators: alpha, then + beta * bias in
 //     fp32 after the full K loop, one rounding to the output dtype.
 //   * workgroup -> tile order is XCD-aware: consecutive workgroup ids land on
@@ -101,17 +102,21 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
   constexpr int WTM = TM / WM, WTN = TN / WN;  // wave tile
   constexpr int FM = WTM / 32, FN = WTN / 32;  // 32x32 MFMA tiles per wave
   constexpr int A_CH = TM * 8 / NT;            // A chunks per thread
-  constexpr int B_CH = TN * 8 / NT;            // B chunks per thread ([N,K] layout)
-  constexpr int B_UN = 2 * TN / NT;            // 4x8 units per thread ([K,N] layout)
-  constexpr int B_RG = B_NK ? B_CH : 4 * B_UN; // B registers per set
+  // B chunks per thread: [N,K] layout TN rows of 8 k-chunks; [K,N] layout TK
+  // rows of TN/8 n-chunks (the same count)
+  constexpr int B_CH = TN * 8 / NT;
+  // [K,N] layout in LDS: TK rows of TN bf16, padded by 64 bytes so the four
+  // rows one transposing read touches land on disjoint banks
+  constexpr int BROW = TN / 8 + 4;  // 16-byte units per padded row
+  constexpr int BS_UNITS = B_NK ? TN * 8 : TK * BROW;
   static_assert(A_CH * NT == TM * 8, "A tile not evenly split");
-  static_assert(B_NK ? (B_CH * NT == TN * 8) : (B_UN * NT == 2 * TN), "B tile not evenly split");
+  static_assert(B_CH * NT == TN * 8, "B tile not evenly split");
   static_assert(FM >= 1 && FN >= 1, "wave tile smaller than one MFMA");
 
   // two LDS stages as separate objects, so the compiler knows the stage being
   // written never aliases the stage being read
   __shared__ u32x4 As[2][TM * 8];
-  __shared__ u32x4 Bs[2][TN * 8];
+  __shared__ u32x4 Bs[2][BS_UNITS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -139,29 +144,24 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
     a_off[i] = (uint32_t)(c >> 3) * lda2 + (uint32_t)(c & 7) * 16u;
     a_k[i] = (c & 7) * 8;
   }
-  uint32_t b_off[B_NK ? B_CH : B_UN];
+  uint32_t b_off[B_CH];
   int b_k[B_NK ? B_CH : 1];
-  bool b_ok[B_NK ? 1 : B_UN];
-  if constexpr (B_NK) {
+  bool b_ok[B_NK ? 1 : B_CH];
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      const int c = tid + i * NT;
+  for (int i = 0; i < B_CH; ++i) {
+    const int c = tid + i * NT;
+    if constexpr (B_NK) {
       b_off[i] = (uint32_t)(c >> 3) * ldb2 + (uint32_t)(c & 7) * 16u;
       b_k[i] = (c & 7) * 8;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < B_UN; ++i) {
-      const int u = tid + i * NT;
-      const int kb = ((u >> 1) / (TN / 8)) * 2 + (u & 1);
-      const int nb = (u >> 1) % (TN / 8);
-      b_off[i] = (uint32_t)(kb * 4) * ldb2 + (uint32_t)nb * 16u;
-      b_ok[i] = n0 + nb * 8 < N;
+    } else {
+      const int kr = c / (TN / 8), cc = c % (TN / 8);
+      b_off[i] = (uint32_t)kr * ldb2 + (uint32_t)cc * 16u;
+      b_ok[i] = n0 + cc * 8 < N;
     }
   }
 
   u32x4 RA[A_CH];
-  u32x4 RB[B_RG];
+  u32x4 RB[B_CH];
 
   // global -> registers, tile t; tiles past K read zeros
   auto load = [&](int t) {
@@ -185,9 +185,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
       const __amdgpu_buffer_rsrc_t r =
           make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), nbytes);
 #pragma unroll
-      for (int i = 0; i < B_UN; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) RB[i * 4 + q] = bload(r, b_ok[i] ? b_off[i] + (uint32_t)q * ldb2 : OOB);
+      for (int i = 0; i < B_CH; ++i) RB[i] = bload(r, b_ok[i] ? b_off[i] : OOB);
     }
   };
 
@@ -207,29 +205,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
         bs[swz(c >> 3, c & 7)] = RB[i];
       }
     } else {
-      uint32_t* bs32 = reinterpret_cast<uint32_t*>(bs);
 #pragma unroll
-      for (int i = 0; i < B_UN; ++i) {
-        const int u = tid + i * NT;
-        const int kb = ((u >> 1) / (TN / 8)) * 2 + (u & 1);
-        const int nb = (u >> 1) % (TN / 8);
-        const u32x4 w0 = RB[i * 4 + 0], w1 = RB[i * 4 + 1], w2 = RB[i * 4 + 2], w3 = RB[i * 4 + 3];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = e >> 1;
-          const uint32_t x0 = w0[j], x1 = w1[j], x2 = w2[j], x3 = w3[j];
-          uint32_t d0, d1;
-          if ((e & 1) == 0) {
-            d0 = (x0 & 0xffffu) | (x1 << 16);
-            d1 = (x2 & 0xffffu) | (x3 << 16);
-          } else {
-            d0 = (x0 >> 16) | (x1 & 0xffff0000u);
-            d1 = (x2 >> 16) | (x3 & 0xffff0000u);
-          }
-          // row n = nb*8+e holds k contiguous: 16-byte chunk kb>>1, 8-byte half kb&1
-          const int at = swz(nb * 8 + e, kb >> 1) * 4 + (kb & 1) * 2;
-          *reinterpret_cast<u32x2*>(bs32 + at) = u32x2{d0, d1};
-        }
+      for (int i = 0; i < B_CH; ++i) {
+        const int c = tid + i * NT;
+        bs[(c / (TN / 8)) * BROW + c % (TN / 8)] = RB[i];
       }
     }
   };
@@ -245,6 +224,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
   const int arow0 = wm * WTM + (lane & 31);
   const int brow0 = wn * WTN + (lane & 31);
   const int khalf = lane >> 5;
+  // [K,N] layout: a B fragment (8 consecutive k of one column n per lane) is
+  // two ds_read_b64_tr_b16. Within each 16-lane group that instruction hands
+  // lane i column i of the 4 x 16 block whose row r, 4-element piece q is
+  // addressed by lane 4r + q. Lanes 0..31 take columns n0..n0+31 and k rows
+  // 0..7 of the step; lanes 32..63 the same columns, k rows 8..15.
+  const int tr_g = lane >> 4, tr_l = lane & 15;
+  const int tr_base = (8 * (tr_g >> 1) + (tr_l >> 2)) * (BROW * 8) + wn * WTN + 16 * (tr_g & 1) + 4 * (tr_l & 3);
 
   // Fragments of one 16-wide k step from LDS stage d, and the FM x FN MFMAs
   // that consume them. The k loop below keeps two fragment sets so the LDS
@@ -254,8 +240,21 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
     const u32x4* bs = Bs[d];
 #pragma unroll
     for (int i = 0; i < FM; ++i) af[i] = __builtin_bit_cast(bf16x8, as[swz(arow0 + i * 32, kk * 2 + khalf)]);
+    if constexpr (B_NK) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) bfr[j] = __builtin_bit_cast(bf16x8, bs[swz(brow0 + j * 32, kk * 2 + khalf)]);
+      for (int j = 0; j < FN; ++j) bfr[j] = __builtin_bit_cast(bf16x8, bs[swz(brow0 + j * 32, kk * 2 + khalf)]);
+    } else {
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+      const __attribute__((address_space(3))) short* bl = (const __attribute__((address_space(3))) short*)bs;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int e = tr_base + kk * 16 * (BROW * 8) + j * 32;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(bl + e));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(bl + e + 4 * (BROW * 8)));
+        bfr[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
   };
   auto mma = [&](const bf16x8* af, const bf16x8* bfr) {
 #pragma unroll

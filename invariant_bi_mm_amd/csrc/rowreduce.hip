@@ -245,16 +245,15 @@ __global__ __launch_bounds__(LS_NT) void log_softmax_kernel(const float* __restr
     fold(v.w, j0 + 3);
   };
 
+  // eight 16-byte loads in flight per thread, folded in increasing chunk order
+  constexpr int U = 8;
   int c = tid;
-  for (; c + 3 * LS_NT < nch; c += 4 * LS_NT) {
-    const f32x4 v0 = reinterpret_cast<const f32x4*>(xr)[c];
-    const f32x4 v1 = reinterpret_cast<const f32x4*>(xr)[c + LS_NT];
-    const f32x4 v2 = reinterpret_cast<const f32x4*>(xr)[c + 2 * LS_NT];
-    const f32x4 v3 = reinterpret_cast<const f32x4*>(xr)[c + 3 * LS_NT];
-    fold4(v0, 4 * c);
-    fold4(v1, 4 * (c + LS_NT));
-    fold4(v2, 4 * (c + 2 * LS_NT));
-    fold4(v3, 4 * (c + 3 * LS_NT));
+  for (; c + (U - 1) * LS_NT < nch; c += U * LS_NT) {
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = reinterpret_cast<const f32x4*>(xr)[c + u * LS_NT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) fold4(v[u], 4 * (c + u * LS_NT));
   }
   for (; c < nch; c += LS_NT) fold4(reinterpret_cast<const f32x4*>(xr)[c], 4 * c);
   if (tid < tail) {
@@ -292,10 +291,18 @@ __global__ __launch_bounds__(LS_NT) void log_softmax_kernel(const float* __restr
 
   const float mx = tot.m;
   const float lg = __builtin_amdgcn_logf(tot.s) * LN2;  // log2 -> ln
-  for (c = tid; c < nch; c += LS_NT) {
-    const f32x4 v = reinterpret_cast<const f32x4*>(xr)[c];
-    reinterpret_cast<f32x4*>(yr)[c] = f32x4{(v.x - mx) - lg, (v.y - mx) - lg, (v.z - mx) - lg, (v.w - mx) - lg};
+  auto out4 = [&](int cc, const f32x4 v) {
+    reinterpret_cast<f32x4*>(yr)[cc] = f32x4{(v.x - mx) - lg, (v.y - mx) - lg, (v.z - mx) - lg, (v.w - mx) - lg};
+  };
+  constexpr int U2 = 4;
+  for (c = tid; c + (U2 - 1) * LS_NT < nch; c += U2 * LS_NT) {
+    f32x4 v[U2];
+#pragma unroll
+    for (int u = 0; u < U2; ++u) v[u] = reinterpret_cast<const f32x4*>(xr)[c + u * LS_NT];
+#pragma unroll
+    for (int u = 0; u < U2; ++u) out4(c + u * LS_NT, v[u]);
   }
+  for (; c < nch; c += LS_NT) out4(c, reinterpret_cast<const f32x4*>(xr)[c]);
   if (tid < tail) yr[nch * 4 + tid] = (xr[nch * 4 + tid] - mx) - lg;
 }
 
