@@ -1,6 +1,8 @@
 """Build libbi.so (the C-ABI library) in-tree with hipcc for gfx950.
 
-Usage: python -m invariant_bi_mm_amd._build   (or __graft_entry__.build()).
+Usage: python invariant_bi_mm_amd/_build.py   (or __graft_entry__.build()).
+Run it by path, not with -m: importing the package loads libbi.so, which is
+the file this script (re)builds.
 Objects go to ``_build/`` at the repository root; the library is written to
 ``invariant_bi_mm_amd/libbi.so``.
 """

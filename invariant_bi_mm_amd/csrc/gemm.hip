@@ -20,21 +20,23 @@
 //   stream-K or atomic anywhere.
 //
 // Structure (one workgroup per TM x TN output tile)
-//   * global -> registers: raw buffer loads, 128 bits per lane. Rows past M
-//     or N and k past K read as zero through the buffer range check, so the
-//     loads need no branch and the k loop is one basic block. The loads of
-//     k tile t+1 are issued at the start of tile t and written to LDS after
-//     three of its four k steps, so they land behind most of a tile of
-//     MFMA work;
-//   * registers -> LDS: double-buffered, rows of 64 bf16 (128 bytes) made of
-//     eight 16-byte chunks whose position is XOR-swizzled by the row, so the
-//     MFMA fragment reads (ds_read_b128) and the tile writes are free of bank
-//     conflicts without padding; the writes of the next tile are issued
-//     among the MFMAs of the current one;
-//   * B stored [K, N] (N contiguous) goes into LDS as it is, k rows of n,
-//     padded by 64 bytes; its MFMA fragments (8 consecutive k of one column
-//     per lane) come out through gfx950's transposing LDS read,
-//     ds_read_b64_tr_b16, two per fragment. B stored [N, K] is staged like A;
+//   * global -> LDS directly (buffer_load ... lds, 16 bytes per lane): no
+//     register staging and no LDS write instructions. Rows past M or N and k
+//     past K read as zero through the buffer range check, so no load needs a
+//     branch. The loads of k tile t+1 are issued at the start of tile t into
+//     the other of two LDS stages and waited for at the barrier that ends
+//     tile t, so they land behind a whole tile of MFMA work;
+//   * LDS layout: A (and B stored [N,K]) as rows of 64 bf16 made of eight
+//     16-byte chunks whose position is XOR-swizzled by the row, so the MFMA
+//     fragment reads (ds_read_b128) are free of bank conflicts; each lane of
+//     a direct load fetches the global chunk that belongs at its swizzled
+//     LDS position;
+//   * B stored [K, N] (N contiguous) goes into LDS as it is, k rows of n
+//     with 16-byte chunks XOR-swizzled by row % 4; its MFMA fragments (8
+//     consecutive k of one column per lane) come out through gfx950's
+//     transposing LDS read, ds_read_b64_tr_b16, two per fragment;
+//   * fragments are double-buffered in registers across the four 16-wide k
+//     steps of a tile;
 //   * epilogue straight from the accumulators: alpha, then + beta * bias in
 //     fp32 after the full K loop, one rounding to the output dtype.
 //   * workgroup -> tile order is XCD-aware: consecutive workgroup ids land on
@@ -92,8 +94,12 @@ constexpr uint32_t OOB = 0x80000000u;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+// 16 bytes per lane straight into LDS: lane l of the wave writes the 16
+// bytes at lds + 16 * l (lds is wave-uniform). Kept as a plain device
+// function: called directly inside the kernel template's lambdas, the
+// builtin made the host compilation pass drop the kernels' launch stubs.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, const void* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
 }
 
 template <int TM, int TN, int WM, int WN, bool B_NK>
@@ -101,26 +107,24 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
   constexpr int NT = WM * WN * 64;
   constexpr int WTM = TM / WM, WTN = TN / WN;  // wave tile
   constexpr int FM = WTM / 32, FN = WTN / 32;  // 32x32 MFMA tiles per wave
-  constexpr int A_CH = TM * 8 / NT;            // A chunks per thread
-  // B chunks per thread: [N,K] layout TN rows of 8 k-chunks; [K,N] layout TK
-  // rows of TN/8 n-chunks (the same count)
-  constexpr int B_CH = TN * 8 / NT;
-  // [K,N] layout in LDS: TK rows of TN bf16, padded by 64 bytes so the four
-  // rows one transposing read touches land on disjoint banks
-  constexpr int BROW = TN / 8 + 4;  // 16-byte units per padded row
-  constexpr int BS_UNITS = B_NK ? TN * 8 : TK * BROW;
-  static_assert(A_CH * NT == TM * 8, "A tile not evenly split");
-  static_assert(B_CH * NT == TN * 8, "B tile not evenly split");
+  // LDS stages. A (and B stored [N,K]): rows of 64 bf16 = eight 16-byte
+  // chunks, chunk position XOR-swizzled by the row (swz). B stored [K,N]:
+  // TK rows of TN bf16, 16-byte chunk c of row r stored at c ^ (4 * (r % 4)),
+  // so the four rows one transposing read touches sit on disjoint banks.
+  constexpr int NW = WM * WN;
+  constexpr int A_I = TM * 8 / 64 / NW;  // 1 KB direct-to-LDS loads per wave per k tile (A)
+  constexpr int B_I = TN * 8 / 64 / NW;  // ... (B; TK * TN / 8 == TN * 8 chunks either layout)
+  static_assert(A_I * 64 * NW == TM * 8 && B_I * 64 * NW == TN * 8, "tile not evenly split across waves");
   static_assert(FM >= 1 && FN >= 1, "wave tile smaller than one MFMA");
+  static_assert(B_NK || TN % 128 == 0, "[K,N] swizzle needs at least 16 chunks per row");
 
-  // two LDS stages as separate objects, so the compiler knows the stage being
-  // written never aliases the stage being read
-  __shared__ u32x4 As[2][TM * 8];
-  __shared__ u32x4 Bs[2][BS_UNITS];
+  // two stages, each its own LDS object
+  __shared__ u32x4 As0[TM * 8], As1[TM * 8];
+  __shared__ u32x4 Bs0[TN * 8], Bs1[TN * 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
   int tm, tn;
@@ -135,44 +139,44 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
   __amdgpu_buffer_rsrc_t bnk_rsrc;
   if constexpr (B_NK) bnk_rsrc = make_rsrc(g.b + (int64_t)n0 * g.ldb, (uint32_t)min(TN, N - n0) * ldb2);
 
-  // per-thread load geometry (constant over the k loop)
-  uint32_t a_off[A_CH];
-  int a_k[A_CH];
+  // Direct-to-LDS loads: lane l of a wave's load writes the 16 bytes at
+  // LDS unit base + l, so each lane fetches the global chunk that belongs at
+  // that (swizzled) position. Per-lane geometry is fixed over the k loop.
+  uint32_t a_off[A_I];
+  int a_k[A_I];
 #pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int c = tid + i * NT;
-    a_off[i] = (uint32_t)(c >> 3) * lda2 + (uint32_t)(c & 7) * 16u;
-    a_k[i] = (c & 7) * 8;
+  for (int i = 0; i < A_I; ++i) {
+    const int p = (i * NW + wave) * 64 + lane;
+    const int row = p >> 3, ch = (p & 7) ^ ((row ^ (row >> 3)) & 7);
+    a_off[i] = (uint32_t)row * lda2 + (uint32_t)ch * 16u;
+    a_k[i] = ch * 8;
   }
-  uint32_t b_off[B_CH];
-  int b_k[B_NK ? B_CH : 1];
-  bool b_ok[B_NK ? 1 : B_CH];
+  uint32_t b_off[B_I];
+  int b_k[B_I];  // [N,K]: k of the chunk; [K,N]: n of the chunk, relative to n0
 #pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int c = tid + i * NT;
+  for (int i = 0; i < B_I; ++i) {
+    const int p = (i * NW + wave) * 64 + lane;
     if constexpr (B_NK) {
-      b_off[i] = (uint32_t)(c >> 3) * ldb2 + (uint32_t)(c & 7) * 16u;
-      b_k[i] = (c & 7) * 8;
+      const int row = p >> 3, ch = (p & 7) ^ ((row ^ (row >> 3)) & 7);
+      b_off[i] = (uint32_t)row * ldb2 + (uint32_t)ch * 16u;
+      b_k[i] = ch * 8;
     } else {
-      const int kr = c / (TN / 8), cc = c % (TN / 8);
-      b_off[i] = (uint32_t)kr * ldb2 + (uint32_t)cc * 16u;
-      b_ok[i] = n0 + cc * 8 < N;
+      const int row = p / (TN / 8), ch = (p % (TN / 8)) ^ (4 * (row & 3));
+      b_off[i] = (uint32_t)row * ldb2 + (uint32_t)ch * 16u;
+      b_k[i] = ch * 8;
     }
   }
 
-  u32x4 RA[A_CH];
-  u32x4 RB[B_CH];
-
-  // global -> registers, tile t; tiles past K read zeros
-  auto load = [&](int t) {
+  // global -> LDS stage (as, bs), k tile t; tiles past K read zeros
+  auto load = [&](int t, u32x4* as, u32x4* bs) {
     const int k0 = t * TK;
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i)
-      RA[i] = bload(a_rsrc, (k0 + a_k[i] < K) ? a_off[i] + (uint32_t)k0 * 2u : OOB);
+    for (int i = 0; i < A_I; ++i)
+      lds_load16(a_rsrc, &as[(i * NW + wave) * 64], (k0 + a_k[i] < K) ? a_off[i] + (uint32_t)k0 * 2u : OOB);
     if constexpr (B_NK) {
 #pragma unroll
-      for (int i = 0; i < B_CH; ++i)
-        RB[i] = bload(bnk_rsrc, (k0 + b_k[i] < K) ? b_off[i] + (uint32_t)k0 * 2u : OOB);
+      for (int i = 0; i < B_I; ++i)
+        lds_load16(bnk_rsrc, &bs[(i * NW + wave) * 64], (k0 + b_k[i] < K) ? b_off[i] + (uint32_t)k0 * 2u : OOB);
     } else {
       // rows of this k tile only: rows past K lie past the descriptor. The
       // base and size are workgroup-uniform; readfirstlane lets the compiler
@@ -185,31 +189,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
       const __amdgpu_buffer_rsrc_t r =
           make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), nbytes);
 #pragma unroll
-      for (int i = 0; i < B_CH; ++i) RB[i] = bload(r, b_ok[i] ? b_off[i] : OOB);
-    }
-  };
-
-  // registers -> LDS stage d
-  auto store = [&](int d) {
-    u32x4* as = As[d];
-    u32x4* bs = Bs[d];
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      const int c = tid + i * NT;
-      as[swz(c >> 3, c & 7)] = RA[i];
-    }
-    if constexpr (B_NK) {
-#pragma unroll
-      for (int i = 0; i < B_CH; ++i) {
-        const int c = tid + i * NT;
-        bs[swz(c >> 3, c & 7)] = RB[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < B_CH; ++i) {
-        const int c = tid + i * NT;
-        bs[(c / (TN / 8)) * BROW + c % (TN / 8)] = RB[i];
-      }
+      for (int i = 0; i < B_I; ++i)
+        lds_load16(r, &bs[(i * NW + wave) * 64], (n0 + b_k[i] < N) ? b_off[i] : OOB);
     }
   };
 
@@ -228,16 +209,18 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
   // two ds_read_b64_tr_b16. Within each 16-lane group that instruction hands
   // lane i column i of the 4 x 16 block whose row r, 4-element piece q is
   // addressed by lane 4r + q. Lanes 0..31 take columns n0..n0+31 and k rows
-  // 0..7 of the step; lanes 32..63 the same columns, k rows 8..15.
+  // 0..7 of the step; lanes 32..63 the same columns, k rows 8..15. Every row
+  // a lane touches has row % 4 == tr_l / 4, so its swizzle is fixed per lane.
   const int tr_g = lane >> 4, tr_l = lane & 15;
-  const int tr_base = (8 * (tr_g >> 1) + (tr_l >> 2)) * (BROW * 8) + wn * WTN + 16 * (tr_g & 1) + 4 * (tr_l & 3);
+  const int tr_row = 8 * (tr_g >> 1) + (tr_l >> 2);
+  const int tr_sw = 4 * (tr_l >> 2);
+  const int tr_lo = 2 * (tr_g & 1) + ((tr_l & 3) >> 1);  // chunk within the 4-chunk group
+  const int tr_in = 4 * (tr_l & 1);                      // element within the chunk
 
   // Fragments of one 16-wide k step from LDS stage d, and the FM x FN MFMAs
   // that consume them. The k loop below keeps two fragment sets so the LDS
   // reads of step kk+1 are in flight while the MFMAs of step kk run.
-  auto frags = [&](int kk, int d, bf16x8* af, bf16x8* bfr) {
-    const u32x4* as = As[d];
-    const u32x4* bs = Bs[d];
+  auto frags = [&](int kk, const u32x4* as, const u32x4* bs, bf16x8* af, bf16x8* bfr) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) af[i] = __builtin_bit_cast(bf16x8, as[swz(arow0 + i * 32, kk * 2 + khalf)]);
     if constexpr (B_NK) {
@@ -249,9 +232,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
       const __attribute__((address_space(3))) short* bl = (const __attribute__((address_space(3))) short*)bs;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int e = tr_base + kk * 16 * (BROW * 8) + j * 32;
+        const int chunk = (((wn * WTN + j * 32) >> 3) ^ tr_sw) + tr_lo;
+        const int e = (kk * 16 + tr_row) * TN + chunk * 8 + tr_in;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(bl + e));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(bl + e + 4 * (BROW * 8)));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(bl + e + 4 * TN));
         bfr[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
@@ -264,28 +248,39 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
   };
 
-  load(0);
-  store(0);
-  __syncthreads();
+  // The loads of k tile kt+1 go straight into the other stage while tile kt
+  // is multiplied; the barrier that ends the tile waits for them (vmcnt) and
+  // publishes them to all waves. The stages reach `step` as __restrict__
+  // pointers: once inlined, that gives the loads and the fragment reads
+  // disjoint alias scopes, so the compiler does not make the reads of one
+  // stage wait for the loads still landing in the other. A load past the
+  // last tile reads zeros into the unused stage.
   static_assert(TK / 16 == 4, "the k step pipeline below assumes four 16-wide steps per tile");
   bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-  for (int kt = 0; kt < nk; ++kt) {
-    const int c = kt & 1;
-    // Fetch tile kt+1 now; it is written to the other LDS stage after three
-    // of this tile's four k steps, so the loads have most of a tile of MFMA
-    // work to land behind.
-    load(kt + 1);
-    frags(0, c, fa0, fb0);
-    frags(1, c, fa1, fb1);
+  auto step = [&](int kt, const u32x4* __restrict__ as, const u32x4* __restrict__ bs, u32x4* __restrict__ as_w,
+                  u32x4* __restrict__ bs_w) {
+    load(kt + 1, as_w, bs_w);
+    // keep the loads at the head of the tile: nothing in this block consumes
+    // them, and the scheduler would otherwise sink them to the barrier
+    __builtin_amdgcn_sched_barrier(0);
+    frags(0, as, bs, fa0, fb0);
+    frags(1, as, bs, fa1, fb1);
     mma(fa0, fb0);
-    frags(2, c, fa0, fb0);
+    frags(2, as, bs, fa0, fb0);
     mma(fa1, fb1);
-    frags(3, c, fa1, fb1);
+    frags(3, as, bs, fa1, fb1);
     mma(fa0, fb0);
-    store(c ^ 1);
     mma(fa1, fb1);
     __syncthreads();
+  };
+  load(0, As0, Bs0);
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, As0, Bs0, As1, Bs1);
+    step(kt + 1, As1, Bs1, As0, Bs0);
   }
+  if (kt < nk) step(kt, As0, Bs0, As1, Bs1);
 
   // Epilogue: lane holds C[8*(r/4) + 4*(lane/32) + r%4][lane%32] of each
   // 32x32 tile, r = 0..15.
