@@ -229,6 +229,107 @@ def cpu_baseline(wl, S):
     return total, parts, threads, sample
 
 
+def sweep(torch, S, bi):
+    """Per-config sweep (the workloads' M values), each line beside torch's
+    non-invariant kernel on the same tensors. Prints a markdown table."""
+    def timed(f, it=None):
+        """Mean device time per call. The calls are captured once into a
+        HIP graph and the graph is replayed, so short kernels are timed
+        without the Python/ctypes launch overhead between them."""
+        n = it or 20
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            f()  # warm the side stream (allocations made by torch ops)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=side):
+                for _ in range(n):
+                    f()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n / 1e3
+
+    rows = ["| op | shape | M | bi us | bi rate | bi % roofline | torch us | tax (bi/torch) |",
+            "|---|---|---|---|---|---|---|---|"]
+
+    def line(op, shape, m, t, f, b, tt):
+        tm = t_min(f, b)
+        bound_mfma = f / PEAK_BF16 >= b / PEAK_HBM
+        rate = f"{f / t / 1e12:.1f} TFLOP/s" if bound_mfma else f"{b / t / 1e12:.2f} TB/s"
+        rows.append(f"| {op} | {shape} | {m} | {t * 1e6:.1f} | {rate} | {100 * tm / t:.1f} | "
+                    f"{'' if tt is None else f'{tt * 1e6:.1f}'} | {'' if tt is None else f'{t / tt:.2f}'} |")
+        log(rows[-1])
+
+    dev = "cuda:0"
+    for (k, n), ms in [((512, 512), (1, 2, 3, 8, 16)), ((4096, 6144), (1, 8, 64, 512, 4096)),
+                       ((4096, 4096), (1, 8, 64, 512, 4096)), ((4096, 24576), (1, 8, 64, 512, 4096)),
+                       ((12288, 4096), (1, 8, 64, 512, 4096))]:
+        w = S.normal_bf16((k, n), 0.02, seed=7, device=dev)
+        for m in ms:
+            a = S.normal_bf16((m, k), 1.0, seed=m, device=dev)
+            c = torch.empty((m, n), device=dev)
+            t = timed(lambda: bi.bi_mm(a, w, out=c))
+            tt = timed(lambda: torch.mm(a, w, out_dtype=torch.float32))
+            line("bi_mm", f"K={k} N={n}", m, t, *gemm_work(m, n, k), tt)
+    k, n = HIDDEN, VOCAB
+    w = S.normal_bf16((k, n), 0.02, seed=8, device=dev)
+    bias = S.normal_bf16((n,), 0.1, seed=9, device=dev)
+    for m in (1, 32, 256):
+        x = S.normal_bf16((m, k), 1.0, seed=m, device=dev)
+        c = torch.empty((m, n), device=dev)
+        t = timed(lambda: bi.bi_addmm(bias, x, w, out=c), 10)
+        tt = timed(lambda: torch.addmm(bias, x, w, out_dtype=torch.float32), 10)
+        line("bi_addmm (LM head)", f"K={k} N={n}", m, t, *gemm_work(m, n, k, bias=True), tt)
+        lp = torch.empty_like(c)
+        am = torch.empty((m,), dtype=torch.int64, device=dev)
+        t = timed(lambda: bi.bi_log_softmax(c, out=lp, argmax=am))
+        tt = timed(lambda: (torch.log_softmax(c, -1), torch.argmax(c, -1)))
+        line("bi_log_softmax+argmax (LM head)", f"N={n}", m, t, 5.0 * m * n, 8.0 * m * n + 8 * m, tt)
+    F = torch.nn.functional
+    wr = S.uniform_bf16((HIDDEN,), 0.5, 1.5, seed=10, device=dev)
+    for m in (1, 7, 64, 513, 2048):
+        x = S.normal_bf16((m, HIDDEN), 1.0, seed=m, device=dev)
+        y = torch.empty_like(x)
+        t = timed(lambda: bi.bi_rmsnorm(x, wr, 1e-6, out=y))
+        tt = timed(lambda: F.rms_norm(x, (HIDDEN,), wr, 1e-6))
+        line("bi_rmsnorm", f"N={HIDDEN}", m, t, 4.0 * m * HIDDEN, 4.0 * m * HIDDEN + 2 * HIDDEN, tt)
+        ym = torch.empty((m,), device=dev)
+        t = timed(lambda: bi.bi_mean(x, out=ym))
+        tt = timed(lambda: torch.mean(x, dim=1, dtype=torch.float32))
+        line("bi_mean", f"N={HIDDEN}", m, t, 1.0 * m * HIDDEN, 2.0 * m * HIDDEN + 4 * m, tt)
+        lx = S.normal_f32((m, VOCAB), 4.0, seed=m, device=dev)
+        ly = torch.empty_like(lx)
+        am = torch.empty((m,), dtype=torch.int64, device=dev)
+        t = timed(lambda: bi.bi_log_softmax(lx, out=ly, argmax=am))
+        tt = timed(lambda: (torch.log_softmax(lx, -1), torch.argmax(lx, -1)))
+        line("bi_log_softmax+argmax", f"N={VOCAB}", m, t, 5.0 * m * VOCAB, 8.0 * m * VOCAB + 8 * m, tt)
+    for bsz in (1, 8, 64, 256):
+        lens = S.context_lens(bsz, seed=6000 + bsz)
+        table, npages = S.paged_kv_layout(lens, 16, seed=6001)
+        q = S.normal_bf16((bsz, 32, 128), 1.0, seed=6002, device=dev)
+        kp = S.normal_bf16((npages, 8, 16, 128), 1.0, seed=6003, device=dev)
+        vp = S.normal_bf16((npages, 8, 16, 128), 1.0, seed=6004, device=dev)
+        offs, total = bi.bi_decode_plan(lens)
+        ws = torch.empty(bi.bi_decode_workspace_bytes(total, 32, 128), dtype=torch.uint8, device=dev)
+        out = torch.empty((bsz, 32, 128), device=dev)
+        tb, ld, of = table.to(dev), lens.to(dev), offs.to(dev)
+        t = timed(lambda: bi.bi_decode_attention(q, kp, vp, tb, ld, of, total, workspace=ws, out=out), 10)
+        tok = int(lens.sum())
+        byts = 4096.0 * tok + bsz * 32 * 128 * 6 + 4.0 * int(((lens + 15) // 16).sum())
+        line("bi_decode_attention", f"B={bsz}, {tok} tokens", bsz, t, 4.0 * 32 * 128 * tok, byts, None)
+    print("\n".join(rows))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,6 +339,8 @@ def main():
     ap.add_argument("--no-torch", action="store_true", help="skip the non-invariant torch baseline")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
                     help="measured HBM traffic per kernel (written from rocprofv3 FETCH_SIZE/WRITE_SIZE runs)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="per-config sweep over the workloads' M values (markdown table), then exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for scaling the HBM counters) and exit")
     args = ap.parse_args()
@@ -261,6 +364,9 @@ def main():
     import synthetic as S
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.sweep:
+        sweep(torch, S, bi)
+        return
     wl = Workload(torch, S, bi, dev)
     ops = wl.ops()
     ms_step, per = time_step(torch, ops, args.steps, args.warmup)

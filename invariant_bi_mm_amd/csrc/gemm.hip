@@ -370,6 +370,7 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   BI_GEMM_CASE(128, 256, 2, 2)
   BI_GEMM_CASE(256, 256, 2, 2)
   BI_GEMM_CASE(256, 256, 2, 4)
+  BI_GEMM_CASE(256, 128, 4, 2)
 #undef BI_GEMM_CASE
   return hipErrorInvalidConfiguration;
 }

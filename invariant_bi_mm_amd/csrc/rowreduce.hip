@@ -42,12 +42,14 @@ __global__ __launch_bounds__(64) void rmsnorm_kernel(const uint16_t* __restrict_
   const int tail = n & 7;
 
   u32x4 cache[CPT > 0 ? CPT : 1];
+  u32x4 wcache[CPT > 0 ? CPT : 1];  // the weight chunks, fetched with x (no second round trip)
   float ss = 0.0f;
   if constexpr (CPT > 0) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = lane + 64 * i;
       cache[i] = c < nch ? reinterpret_cast<const u32x4*>(xr)[c] : u32x4{0u, 0u, 0u, 0u};
+      wcache[i] = c < nch ? reinterpret_cast<const u32x4*>(w)[c] : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
@@ -71,10 +73,10 @@ __global__ __launch_bounds__(64) void rmsnorm_kernel(const uint16_t* __restrict_
   ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / (float)n + eps);
 
-  auto emit = [&](int c, const u32x4& xv) {
+  auto emit = [&](int c, const u32x4& xv, const u32x4& wv) {
     float f[8], wf[8];
     unpack8(xv, f);
-    unpack8(reinterpret_cast<const u32x4*>(w)[c], wf);
+    unpack8(wv, wf);
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = (f[e] * r) * wf[e];
@@ -92,10 +94,11 @@ __global__ __launch_bounds__(64) void rmsnorm_kernel(const uint16_t* __restrict_
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = lane + 64 * i;
-      if (c < nch) emit(c, cache[i]);
+      if (c < nch) emit(c, cache[i], wcache[i]);
     }
   } else {
-    for (int c = lane; c < nch; c += 64) emit(c, reinterpret_cast<const u32x4*>(xr)[c]);
+    for (int c = lane; c < nch; c += 64)
+      emit(c, reinterpret_cast<const u32x4*>(xr)[c], reinterpret_cast<const u32x4*>(w)[c]);
   }
   if (lane < tail) {
     const int j = nch * 8 + lane;
