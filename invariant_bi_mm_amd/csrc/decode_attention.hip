@@ -30,8 +30,8 @@
 //   output : (max, sum p, o[128]) per (split, query head), fp32.
 // Kernel 2, one workgroup per (sequence, query head):
 //   M = max_s m_s; l = sum_s 2^(m_s - M) l_s; o = sum_s 2^(m_s - M) o_s[d],
-//   each sum taken as (even splits in increasing s) + (odd splits in
-//   increasing s); out = o / l.
+//   each sum taken as 8 chains (splits s = r mod 8, increasing s) added in a
+//   fixed tree; out = o / l.
 #include "bi_internal.h"
 #include "device_common.h"
 
@@ -217,62 +217,81 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
   }
 }
 
-// Combine: one workgroup of 2 * HD threads per (sequence, query head). Thread
-// (half, d) folds the splits s = half, half + 2, half + 4, ... in increasing
-// order; the two halves are then added, half 0 first. The order depends only
-// on the sequence's split count.
-__global__ __launch_bounds__(2 * HD) void decode_combine_kernel(const int32_t* __restrict__ offs,
-                                                                 const float* __restrict__ ws_o,
-                                                                 const float* __restrict__ ws_ml, int hq,
-                                                                 void* __restrict__ out, int out_bf16) {
+// Combine: one workgroup of 256 threads per (sequence, query head), as 8
+// groups of 32 lanes; lane c of a group owns o[4c .. 4c+3]. Group r folds the
+// splits s = r, r + 8, r + 16, ... in increasing order (m, l, o weighted by
+// 2^(m_s - M)); the 8 group sums are then added as
+// ((g0 + g1) + (g2 + g3)) + ((g4 + g5) + (g6 + g7)). The order depends only on
+// the sequence's split count, and the 8 chains cut the dependent-load chain of
+// a 128-split sequence to 16 steps.
+__global__ __launch_bounds__(256) void decode_combine_kernel(const int32_t* __restrict__ offs,
+                                                              const float* __restrict__ ws_o,
+                                                              const float* __restrict__ ws_ml, int hq,
+                                                              void* __restrict__ out, int out_bf16) {
   __shared__ float red[4];
-  __shared__ float part_o[HD], part_l;
+  __shared__ float4 po[8][HD / 4];
+  __shared__ float pl[8];
   const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int d = tid & (HD - 1), half = tid >> 7;
+  const int r = tid >> 5, c = tid & 31;
   const int w0 = offs[b], ns = offs[b + 1] - w0;
   // exact max of the split maxima (max is order-free)
   float M = -INFINITY;
-  for (int s = tid; s < ns; s += 2 * HD) M = fmaxf(M, ws_ml[((int64_t)(w0 + s) * hq + h) * 2]);
+  for (int s = tid; s < ns; s += 256) M = fmaxf(M, ws_ml[((int64_t)(w0 + s) * hq + h) * 2]);
   M = wave_max(M);
   if ((tid & 63) == 0) red[tid >> 6] = M;
   __syncthreads();
   M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float l = 0.0f, o = 0.0f;
-  int s = half;
-  for (; s + 6 < ns; s += 8) {
-    float mv[4], lv[4], ov[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t ph = (int64_t)(w0 + s + 2 * u) * hq + h;
-      mv[u] = ws_ml[ph * 2];
-      lv[u] = ws_ml[ph * 2 + 1];
-      ov[u] = ws_o[ph * HD + d];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float c = __builtin_amdgcn_exp2f(mv[u] - M);
-      l = l + c * lv[u];
-      o = o + c * ov[u];
-    }
-  }
-  for (; s < ns; s += 2) {
+
+  float l = 0.0f;
+  float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  auto fold = [&](const float2 ml, const float4 ov) {
+    const float w = __builtin_amdgcn_exp2f(ml.x - M);
+    l = l + w * ml.y;
+    o.x = o.x + w * ov.x;
+    o.y = o.y + w * ov.y;
+    o.z = o.z + w * ov.z;
+    o.w = o.w + w * ov.w;
+  };
+  auto part = [&](int s, float2& ml, float4& ov) {
     const int64_t ph = (int64_t)(w0 + s) * hq + h;
-    const float c = __builtin_amdgcn_exp2f(ws_ml[ph * 2] - M);
-    l = l + c * ws_ml[ph * 2 + 1];
-    o = o + c * ws_o[ph * HD + d];
+    ml = *reinterpret_cast<const float2*>(ws_ml + ph * 2);
+    ov = *reinterpret_cast<const float4*>(ws_o + ph * HD + 4 * c);
+  };
+  int s = r;
+  for (; s + 8 < ns; s += 16) {  // two splits of this group per trip, folded in order
+    float2 ml0, ml1;
+    float4 o0, o1;
+    part(s, ml0, o0);
+    part(s + 8, ml1, o1);
+    fold(ml0, o0);
+    fold(ml1, o1);
   }
-  if (half == 1) {
-    part_o[d] = o;
-    if (d == 0) part_l = l;
+  if (s < ns) {
+    float2 ml0;
+    float4 o0;
+    part(s, ml0, o0);
+    fold(ml0, o0);
   }
+  po[r][c] = o;
+  if (c == 0) pl[r] = l;
   __syncthreads();
-  if (half == 0) {
-    const float r = (o + part_o[d]) / (l + part_l);
-    const int64_t at = ((int64_t)b * hq + h) * HD + d;
-    if (out_bf16)
-      reinterpret_cast<uint16_t*>(out)[at] = (uint16_t)f32_to_bf16_rne(r);
-    else
-      reinterpret_cast<float*>(out)[at] = r;
+  if (tid < HD / 4) {
+    float4 t[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) t[q] = po[q][tid];
+    auto add = [](float4 x, float4 y) { return make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w); };
+    const float4 os = add(add(add(t[0], t[1]), add(t[2], t[3])), add(add(t[4], t[5]), add(t[6], t[7])));
+    const float ls = ((pl[0] + pl[1]) + (pl[2] + pl[3])) + ((pl[4] + pl[5]) + (pl[6] + pl[7]));
+    const float res[4] = {os.x / ls, os.y / ls, os.z / ls, os.w / ls};
+    const int64_t at = ((int64_t)b * hq + h) * HD + 4 * tid;
+    // element stores: out need only be aligned to its element size
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (out_bf16)
+        reinterpret_cast<uint16_t*>(out)[at + e] = (uint16_t)f32_to_bf16_rne(res[e]);
+      else
+        reinterpret_cast<float*>(out)[at + e] = res[e];
+    }
   }
 }
 
@@ -296,7 +315,7 @@ hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t s) {
   hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)(p.total_splits * p.num_kv_heads)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)p.batch, (unsigned)p.num_q_heads), dim3(2 * HD), 0, s,
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)p.batch, (unsigned)p.num_q_heads), dim3(256), 0, s,
                      p.split_offsets, p.ws_o, p.ws_ml, p.num_q_heads, p.out, p.out_bf16 ? 1 : 0);
   return hipGetLastError();
 }
