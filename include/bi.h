@@ -207,6 +207,72 @@ bi_status bi_decode_attention(const void* q, const void* k_pages, const void* v_
                               void* workspace, size_t workspace_bytes,
                               void* out, bi_dtype out_dtype, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Per-token steps of a decode step (Qwen3-style layer). They carry one
+ * sequence's greedy token stream from logits back to the next layer input.
+ * The pages trace non-reproducible completions to the batch a request lands
+ * in, with a long identical prefix and a fork at one token (readhandoff.com,
+ * agent-run reproducibility pinning, sections "What does temperature zero
+ * actually guarantee?" and "Where the divergence showed up"), and measure the
+ * cost on Qwen3-8B decoding (same page, "Key takeaways"). Each output element
+ * depends on its own token's inputs only, through a fixed sequence of fp32
+ * operations, so none of these can depend on the batch.
+ * ------------------------------------------------------------------------ */
+
+/* bi_add_rmsnorm: residual add fused with the RMSNorm that follows it.
+ *   x <- RNE_bf16(x + d)      (in place; fp32 add of the two bf16 values)
+ *   y  = bi_rmsnorm(x, w, eps) of the updated x, same rules as bi_rmsnorm.
+ *   x  bf16 [m, n], row stride ldx (read, then overwritten).
+ *   d  bf16 [m, n], row stride ldd.   w  bf16 [n].   y [m, n] y_dtype.
+ * x must not overlap d, w or y. */
+bi_status bi_add_rmsnorm(void* x, int64_t ldx, const void* d, int64_t ldd, const void* w, float eps,
+                         void* y, int64_t ldy, bi_dtype y_dtype,
+                         int64_t m, int64_t n, hipStream_t stream);
+
+/* bi_embed: out[i, :] = table[tokens[i], :] (token embedding lookup).
+ *   table  bf16 [vocab, n], row stride ld.   tokens int64 [m] (DEVICE).
+ *   out    bf16 [m, n], row stride ldo.
+ * n, ld, ldo multiples of 8. A token outside [0, vocab) yields a zero row
+ * (the kernel never reads outside the table; the host cannot check device
+ * contents). */
+bi_status bi_embed(const void* table, int64_t ld, int64_t vocab, const int64_t* tokens,
+                   void* out, int64_t ldo, int64_t m, int64_t n, hipStream_t stream);
+
+/* bi_silu_mul: out[i, j] = RNE_bf16(silu(g) * u), g = gu[i, j],
+ * u = gu[i, n + j], silu(g) = g / (1 + e^-g), all in fp32 (the gated MLP
+ * activation; gate and up come from one GEMM with N = 2n).
+ *   gu  bf16 [m, 2n], row stride ldg.   out  bf16 [m, n], row stride ldo.
+ * n, ldg, ldo multiples of 8; m <= 65535. */
+bi_status bi_silu_mul(const void* gu, int64_t ldg, void* out, int64_t ldo,
+                      int64_t m, int64_t n, hipStream_t stream);
+
+/* bi_qknorm_rope_append: the attention prologue of one decode token per
+ * sequence.
+ *   qkv  bf16 [batch, (num_q_heads + 2 num_kv_heads) * head_dim], row stride
+ *        ldqkv: the q heads, then the k heads, then the v heads.
+ *   For each q and k head: r = 1 / sqrt(mean(x^2) + eps) over the head,
+ *   t = (x * r) * w (w = q_norm_w or k_norm_w, bf16 [head_dim]), then the
+ *   rotary embedding at position p = positions[b] on the pairs (i, i + 64):
+ *     out[i]      = t[i] * cos[p][i] - t[i+64] * sin[p][i]
+ *     out[i + 64] = t[i+64] * cos[p][i] + t[i] * sin[p][i],
+ *   rounded once to bf16. q heads go to q_out [batch, num_q_heads, head_dim];
+ *   k heads, and v heads unchanged, go to slot p % page_size of page
+ *   block_table[b * max_pages + p / page_size] of k_pages / v_pages
+ *   ([num_pages, num_kv_heads, page_size, head_dim], the bi_decode_attention
+ *   layout). positions[b] is the new token's index, i.e. the sequence's
+ *   length before this token.
+ *   cos_tab, sin_tab  fp32 [max_pos, head_dim / 2]: the caller's table.
+ * Supported: head_dim == 128. A position outside [0, max_pos) or outside the
+ * block table, or a table entry outside [0, num_pages), writes no cache slot
+ * and zeros to that token's q_out rows. Pointers need only their element
+ * alignment. */
+bi_status bi_qknorm_rope_append(const void* qkv, int64_t ldqkv, const void* q_norm_w, const void* k_norm_w,
+                                float eps, const float* cos_tab, const float* sin_tab, int64_t max_pos,
+                                const int32_t* positions, const int32_t* block_table, int64_t max_pages,
+                                int64_t num_pages, void* k_pages, void* v_pages, void* q_out,
+                                int64_t batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                int page_size, hipStream_t stream);
+
 /* Static text for a status code (never NULL). */
 const char* bi_status_string(bi_status s);
 

@@ -22,6 +22,7 @@ __all__ = [
     "BiError", "LIB_PATH", "lib",
     "bi_mm", "bi_addmm", "bi_gemm_config", "bi_rmsnorm", "bi_mean", "bi_log_softmax",
     "bi_decode_plan", "bi_decode_workspace_bytes", "bi_decode_attention",
+    "bi_add_rmsnorm", "bi_embed", "bi_silu_mul", "bi_qknorm_rope_append",
     "bi_status_string", "bi_last_error_message",
     "BI_BF16", "BI_F32", "STATUS",
 ]
@@ -59,6 +60,15 @@ lib.bi_decode_workspace_bytes.restype = _sz
 lib.bi_decode_attention.argtypes = [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
                                     _f32, _vp, _sz, _vp, _i32, _vp]
 lib.bi_decode_attention.restype = _st
+lib.bi_add_rmsnorm.argtypes = [_vp, _i64, _vp, _i64, _vp, _f32, _vp, _i64, _i32, _i64, _i64, _vp]
+lib.bi_add_rmsnorm.restype = _st
+lib.bi_embed.argtypes = [_vp, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _vp]
+lib.bi_embed.restype = _st
+lib.bi_silu_mul.argtypes = [_vp, _i64, _vp, _i64, _i64, _i64, _vp]
+lib.bi_silu_mul.restype = _st
+lib.bi_qknorm_rope_append.argtypes = [_vp, _i64, _vp, _vp, _f32, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _vp,
+                                      _i64, _i32, _i32, _i32, _i32, _vp]
+lib.bi_qknorm_rope_append.restype = _st
 lib.bi_status_string.argtypes = [_st]
 lib.bi_status_string.restype = ctypes.c_char_p
 lib.bi_last_error_message.argtypes = []
@@ -259,3 +269,82 @@ def bi_decode_attention(q, k_pages, v_pages, block_table, context_lens, split_of
                                    page, int(split_tokens), float(scale), _ptr(workspace), workspace.numel(),
                                    _ptr(out), _dtype_code(out.dtype), _stream(stream)))
     return out
+
+
+def bi_add_rmsnorm(x: torch.Tensor, d: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, out: torch.Tensor | None = None,
+                   *, out_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
+    """x <- bf16(x + d) in place; returns rmsnorm(x) (x, d bf16 [M, N], w bf16 [N])."""
+    _need_bf16(x, "x")
+    _need_bf16(d, "d")
+    _need_bf16(w, "w")
+    m, n = x.shape
+    if d.shape != x.shape:
+        raise ValueError("d must have x's shape")
+    if w.dim() != 1 or w.shape[0] != n or not w.is_contiguous():
+        raise ValueError("w must be a contiguous [N] vector")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    x, ldx = _mat(x, "x")
+    d, ldd = _mat(d, "d")
+    out, ldy = _mat(out, "out")
+    _check(lib.bi_add_rmsnorm(_ptr(x), ldx, _ptr(d), ldd, _ptr(w), float(eps), _ptr(out), ldy,
+                              _dtype_code(out.dtype), m, n, _stream(stream)))
+    return out
+
+
+def bi_embed(table: torch.Tensor, tokens: torch.Tensor, out: torch.Tensor | None = None, *, stream=None):
+    """out[i] = table[tokens[i]] (bf16 [V, N] table, int64 [M] device tokens); bad tokens give zero rows."""
+    _need_bf16(table, "table")
+    if tokens.dtype != torch.int64 or tokens.dim() != 1 or not tokens.is_contiguous():
+        raise TypeError("tokens must be a contiguous int64 vector")
+    vocab, n = table.shape
+    m = tokens.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=table.device)
+    table, ld = _mat(table, "table")
+    out, ldo = _mat(out, "out")
+    _check(lib.bi_embed(_ptr(table), ld, vocab, _ptr(tokens), _ptr(out), ldo, m, n, _stream(stream)))
+    return out
+
+
+def bi_silu_mul(gu: torch.Tensor, out: torch.Tensor | None = None, *, stream=None) -> torch.Tensor:
+    """out = silu(gu[:, :n]) * gu[:, n:] (bf16 [M, 2n] -> bf16 [M, n])."""
+    _need_bf16(gu, "gu")
+    m, n2 = gu.shape
+    if n2 % 2:
+        raise ValueError("gu must have an even number of columns")
+    n = n2 // 2
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=gu.device)
+    gu, ldg = _mat(gu, "gu")
+    out, ldo = _mat(out, "out")
+    _check(lib.bi_silu_mul(_ptr(gu), ldg, _ptr(out), ldo, m, n, _stream(stream)))
+    return out
+
+
+def bi_qknorm_rope_append(qkv, q_norm_w, k_norm_w, cos_tab, sin_tab, positions, block_table, k_pages, v_pages, *,
+                          num_q_heads: int, num_kv_heads: int, eps: float = 1e-6, q_out=None, stream=None):
+    """Per-head q/k RMSNorm + rotary embedding; q to q_out [B, Hq, D], k and v into the paged cache at positions."""
+    for t, nm in ((qkv, "qkv"), (q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w"), (k_pages, "k_pages"),
+                  (v_pages, "v_pages")):
+        _need_bf16(t, nm)
+    if cos_tab.dtype != torch.float32 or sin_tab.dtype != torch.float32 or cos_tab.shape != sin_tab.shape:
+        raise TypeError("cos_tab and sin_tab must be fp32 tables of one shape")
+    if positions.dtype != torch.int32 or block_table.dtype != torch.int32:
+        raise TypeError("positions and block_table must be int32")
+    for t, nm in ((cos_tab, "cos_tab"), (sin_tab, "sin_tab"), (positions, "positions"), (block_table, "block_table"),
+                  (k_pages, "k_pages"), (v_pages, "v_pages"), (q_norm_w, "q_norm_w"), (k_norm_w, "k_norm_w")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    bsz = qkv.shape[0]
+    num_pages, hkv, page, d = k_pages.shape
+    if hkv != num_kv_heads or v_pages.shape != k_pages.shape:
+        raise ValueError("cache shape disagrees with num_kv_heads")
+    if q_out is None:
+        q_out = torch.empty((bsz, num_q_heads, d), dtype=torch.bfloat16, device=qkv.device)
+    qkv, ldq = _mat(qkv, "qkv")
+    _check(lib.bi_qknorm_rope_append(_ptr(qkv), ldq, _ptr(q_norm_w), _ptr(k_norm_w), float(eps), _ptr(cos_tab),
+                                     _ptr(sin_tab), cos_tab.shape[0], _ptr(positions), _ptr(block_table),
+                                     block_table.shape[1], num_pages, _ptr(k_pages), _ptr(v_pages), _ptr(q_out), bsz,
+                                     num_q_heads, num_kv_heads, d, page, _stream(stream)))
+    return q_out

@@ -252,6 +252,92 @@ bi_status bi_decode_attention(const void* q, const void* k_pages, const void* v_
   return hip_status(bi::launch_decode_attention(p, stream), "decode attention launch");
 }
 
+bi_status bi_add_rmsnorm(void* x, int64_t ldx, const void* d, int64_t ldd, const void* w, float eps, void* y,
+                         int64_t ldy, bi_dtype y_dtype, int64_t m, int64_t n, hipStream_t stream) {
+  if (m < 0 || n < 0) return fail(BI_ERR_SHAPE, "negative size");
+  if (!valid_dtype(y_dtype)) return fail(BI_ERR_DTYPE, "y_dtype %d is not BI_BF16 or BI_F32", (int)y_dtype);
+  if (m == 0) return ok();
+  if (n == 0) return fail(BI_ERR_SHAPE, "n == 0: RMSNorm of an empty row is undefined");
+  if (x == nullptr || d == nullptr || w == nullptr || y == nullptr) return fail(BI_ERR_NULL, "x, d, w or y is NULL");
+  if (m > INT_MAX || n > INT_MAX) return fail(BI_ERR_UNSUPPORTED, "a size exceeds 2^31-1");
+  if (ldx < n || ldd < n || ldy < n) return fail(BI_ERR_STRIDE, "ldx/ldd/ldy smaller than n");
+  const int64_t yq = y_dtype == BI_BF16 ? 8 : 4;
+  if (!aligned(x, 16) || !aligned(d, 16) || !aligned(w, 16) || !aligned(y, 16) || ldx % 8 != 0 || ldd % 8 != 0 ||
+      ldy % yq != 0)
+    return fail(BI_ERR_ALIGN, "x, d, w, y must be 16-byte aligned; ldx, ldd multiples of 8, ldy of %lld",
+                (long long)yq);
+  return hip_status(bi::launch_add_rmsnorm(x, ldx, d, ldd, w, eps, y, ldy, y_dtype == BI_BF16, m, n, stream),
+                    "add_rmsnorm launch");
+}
+
+bi_status bi_embed(const void* table, int64_t ld, int64_t vocab, const int64_t* tokens, void* out, int64_t ldo,
+                   int64_t m, int64_t n, hipStream_t stream) {
+  if (m < 0 || n < 0 || vocab < 0) return fail(BI_ERR_SHAPE, "negative size");
+  if (m == 0 || n == 0) return ok();
+  if (table == nullptr || tokens == nullptr || out == nullptr) return fail(BI_ERR_NULL, "table, tokens or out is NULL");
+  if (vocab == 0) return fail(BI_ERR_SHAPE, "empty table");
+  if (m > INT_MAX || n > INT_MAX) return fail(BI_ERR_UNSUPPORTED, "a size exceeds 2^31-1");
+  if (ld < n || ldo < n) return fail(BI_ERR_STRIDE, "ld/ldo smaller than n");
+  if (n % 8 != 0 || ld % 8 != 0 || ldo % 8 != 0 || !aligned(table, 16) || !aligned(out, 16) || !aligned(tokens, 8))
+    return fail(BI_ERR_ALIGN, "table, out 16-byte aligned with n, ld, ldo multiples of 8; tokens 8-byte aligned");
+  return hip_status(bi::launch_embed(table, ld, vocab, tokens, out, ldo, m, n, stream), "embed launch");
+}
+
+bi_status bi_silu_mul(const void* gu, int64_t ldg, void* out, int64_t ldo, int64_t m, int64_t n, hipStream_t stream) {
+  if (m < 0 || n < 0) return fail(BI_ERR_SHAPE, "negative size");
+  if (m == 0 || n == 0) return ok();
+  if (gu == nullptr || out == nullptr) return fail(BI_ERR_NULL, "gu or out is NULL");
+  if (m > 65535 || n > INT_MAX / 2) return fail(BI_ERR_UNSUPPORTED, "m > 65535 or n too large");
+  if (ldg < 2 * n || ldo < n) return fail(BI_ERR_STRIDE, "ldg < 2n or ldo < n");
+  if (n % 8 != 0 || ldg % 8 != 0 || ldo % 8 != 0 || !aligned(gu, 16) || !aligned(out, 16))
+    return fail(BI_ERR_ALIGN, "gu, out 16-byte aligned with n, ldg, ldo multiples of 8");
+  return hip_status(bi::launch_silu_mul(gu, ldg, out, ldo, m, n, stream), "silu_mul launch");
+}
+
+bi_status bi_qknorm_rope_append(const void* qkv, int64_t ldqkv, const void* q_norm_w, const void* k_norm_w, float eps,
+                                const float* cos_tab, const float* sin_tab, int64_t max_pos, const int32_t* positions,
+                                const int32_t* block_table, int64_t max_pages, int64_t num_pages, void* k_pages,
+                                void* v_pages, void* q_out, int64_t batch, int num_q_heads, int num_kv_heads,
+                                int head_dim, int page_size, hipStream_t stream) {
+  if (batch < 0 || max_pos < 0 || max_pages < 0 || num_pages < 0) return fail(BI_ERR_SHAPE, "negative size");
+  if (head_dim != 128 || page_size < 1 || num_q_heads < 1 || num_kv_heads < 1)
+    return fail(BI_ERR_UNSUPPORTED, "supported: head_dim 128, page_size >= 1, at least one q and kv head (got %d, %d, %d/%d)",
+                head_dim, page_size, num_q_heads, num_kv_heads);
+  if (batch == 0) return ok();
+  if (qkv == nullptr || q_norm_w == nullptr || k_norm_w == nullptr || cos_tab == nullptr || sin_tab == nullptr ||
+      positions == nullptr || block_table == nullptr || k_pages == nullptr || v_pages == nullptr || q_out == nullptr)
+    return fail(BI_ERR_NULL, "a required pointer is NULL");
+  if (max_pos < 1 || max_pages < 1 || num_pages < 1) return fail(BI_ERR_SHAPE, "max_pos, max_pages, num_pages must be >= 1");
+  const int64_t width = (int64_t)(num_q_heads + 2 * num_kv_heads) * head_dim;
+  if (ldqkv < width) return fail(BI_ERR_STRIDE, "ldqkv < (num_q_heads + 2 num_kv_heads) * head_dim");
+  if (batch > INT_MAX || num_q_heads + 2 * num_kv_heads > 65535) return fail(BI_ERR_UNSUPPORTED, "grid size out of range");
+  if (!aligned(qkv, 2) || !aligned(q_norm_w, 2) || !aligned(k_norm_w, 2) || !aligned(cos_tab, 4) ||
+      !aligned(sin_tab, 4) || !aligned(positions, 4) || !aligned(block_table, 4) || !aligned(k_pages, 2) ||
+      !aligned(v_pages, 2) || !aligned(q_out, 2))
+    return fail(BI_ERR_ALIGN, "a pointer is not aligned to its element size");
+  bi::RopeParams p;
+  p.qkv = qkv;
+  p.ldqkv = ldqkv;
+  p.q_norm_w = q_norm_w;
+  p.k_norm_w = k_norm_w;
+  p.eps = eps;
+  p.cos_tab = cos_tab;
+  p.sin_tab = sin_tab;
+  p.max_pos = max_pos;
+  p.positions = positions;
+  p.block_table = block_table;
+  p.max_pages = max_pages;
+  p.num_pages = num_pages;
+  p.k_pages = k_pages;
+  p.v_pages = v_pages;
+  p.q_out = q_out;
+  p.batch = batch;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.page_size = page_size;
+  return hip_status(bi::launch_qknorm_rope_append(p, stream), "qknorm_rope_append launch");
+}
+
 const char* bi_status_string(bi_status s) {
   switch (s) {
     case BI_OK: return "BI_OK";

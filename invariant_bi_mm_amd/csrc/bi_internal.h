@@ -32,6 +32,8 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t stream);
 
 hipError_t launch_rmsnorm(const void* x, int64_t ldx, const void* w, float eps, void* y,
                           int64_t ldy, bool y_bf16, int64_t m, int64_t n, hipStream_t stream);
+hipError_t launch_add_rmsnorm(void* x, int64_t ldx, const void* d, int64_t ldd, const void* w, float eps, void* y,
+                              int64_t ldy, bool y_bf16, int64_t m, int64_t n, hipStream_t stream);
 hipError_t launch_mean(const void* x, bool x_bf16, int64_t ldx, float* y, int64_t m, int64_t n,
                        hipStream_t stream);
 hipError_t launch_log_softmax(const float* x, int64_t ldx, float* y, int64_t ldy, int64_t* argmax,
@@ -55,5 +57,30 @@ struct DecodeParams {
   bool out_bf16;
 };
 hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t stream);
+
+hipError_t launch_embed(const void* table, int64_t ld, int64_t vocab, const int64_t* tokens, void* out, int64_t ldo,
+                        int64_t m, int64_t n, hipStream_t stream);
+hipError_t launch_silu_mul(const void* gu, int64_t ldg, void* out, int64_t ldo, int64_t m, int64_t n,
+                           hipStream_t stream);
+
+struct RopeParams {
+  const void* qkv;
+  int64_t ldqkv;
+  const void* q_norm_w;
+  const void* k_norm_w;
+  float eps;
+  const float* cos_tab;
+  const float* sin_tab;
+  int64_t max_pos;
+  const int32_t* positions;
+  const int32_t* block_table;
+  int64_t max_pages, num_pages;
+  void* k_pages;
+  void* v_pages;
+  void* q_out;
+  int64_t batch;
+  int num_q_heads, num_kv_heads, page_size;
+};
+hipError_t launch_qknorm_rope_append(const RopeParams& p, hipStream_t stream);
 
 }  // namespace bi

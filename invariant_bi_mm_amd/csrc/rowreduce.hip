@@ -29,17 +29,47 @@ namespace {
 // full chunk (n % 8) are folded last, by lanes 0..n%8-1.
 // CPT == 0 selects the streaming variant (no register cache; chunks are read
 // again for the output pass) used for rows longer than 64 * 16 chunks.
+//
+// ADD: residual form. The row first becomes x + d, rounded once to bf16
+// (fp32 add of the two bf16 values, then RNE), that sum is written back over
+// x and normalised. Every element of x is read before the lane that owns it
+// writes it, so the in-place update needs no barrier; the streaming variant
+// recomputes the sum in its second pass instead of reading its own writes.
 // ---------------------------------------------------------------------------
-template <int CPT>
-__global__ __launch_bounds__(64) void rmsnorm_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+__device__ __forceinline__ u32x4 add_bf16x8(const u32x4& a, const u32x4& b) {
+  float fa[8], fb[8];
+  unpack8(a, fa);
+  unpack8(b, fb);
+  return u32x4{pack_bf16x2(fa[0] + fb[0], fa[1] + fb[1]), pack_bf16x2(fa[2] + fb[2], fa[3] + fb[3]),
+               pack_bf16x2(fa[4] + fb[4], fa[5] + fb[5]), pack_bf16x2(fa[6] + fb[6], fa[7] + fb[7])};
+}
+
+template <int CPT, bool ADD>
+__global__ __launch_bounds__(64) void rmsnorm_kernel(uint16_t* __restrict__ x, int64_t ldx,
+                                                      const uint16_t* __restrict__ d, int64_t ldd,
                                                       const uint16_t* __restrict__ w, float eps,
                                                       void* __restrict__ y, int64_t ldy, int y_bf16,
                                                       int n) {
   const int row = blockIdx.x;
   const int lane = threadIdx.x;
-  const uint16_t* xr = x + (int64_t)row * ldx;
+  uint16_t* xr = x + (int64_t)row * ldx;
+  const uint16_t* dr = ADD ? d + (int64_t)row * ldd : nullptr;
   const int nch = n >> 3;
   const int tail = n & 7;
+  // chunk c of the (updated) row
+  auto chunk = [&](int c) {
+    const u32x4 v = reinterpret_cast<const u32x4*>(xr)[c];
+    if constexpr (ADD) return add_bf16x8(v, reinterpret_cast<const u32x4*>(dr)[c]);
+    else return v;
+  };
+  auto elem = [&](int j) {  // element j (tail) of the updated row, as bf16 bits
+    if constexpr (ADD) {
+      const float t = __uint_as_float(uint32_t(xr[j]) << 16) + __uint_as_float(uint32_t(dr[j]) << 16);
+      return (uint16_t)f32_to_bf16_rne(t);
+    } else {
+      return xr[j];
+    }
+  };
 
   u32x4 cache[CPT > 0 ? CPT : 1];
   u32x4 wcache[CPT > 0 ? CPT : 1];  // the weight chunks, fetched with x (no second round trip)
@@ -48,7 +78,7 @@ __global__ __launch_bounds__(64) void rmsnorm_kernel(const uint16_t* __restrict_
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = lane + 64 * i;
-      cache[i] = c < nch ? reinterpret_cast<const u32x4*>(xr)[c] : u32x4{0u, 0u, 0u, 0u};
+      cache[i] = c < nch ? chunk(c) : u32x4{0u, 0u, 0u, 0u};
       wcache[i] = c < nch ? reinterpret_cast<const u32x4*>(w)[c] : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
@@ -61,19 +91,22 @@ __global__ __launch_bounds__(64) void rmsnorm_kernel(const uint16_t* __restrict_
   } else {
     for (int c = lane; c < nch; c += 64) {
       float f[8];
-      unpack8(reinterpret_cast<const u32x4*>(xr)[c], f);
+      unpack8(chunk(c), f);
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(f[e], f[e], ss);
     }
   }
+  uint16_t tail_v = 0;
   if (lane < tail) {
-    const float t = __uint_as_float(uint32_t(xr[nch * 8 + lane]) << 16);
+    tail_v = elem(nch * 8 + lane);
+    const float t = __uint_as_float(uint32_t(tail_v) << 16);
     ss = __builtin_fmaf(t, t, ss);
   }
   ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / (float)n + eps);
 
   auto emit = [&](int c, const u32x4& xv, const u32x4& wv) {
+    if constexpr (ADD) reinterpret_cast<u32x4*>(xr)[c] = xv;
     float f[8], wf[8];
     unpack8(xv, f);
     unpack8(wv, wf);
@@ -97,12 +130,12 @@ __global__ __launch_bounds__(64) void rmsnorm_kernel(const uint16_t* __restrict_
       if (c < nch) emit(c, cache[i], wcache[i]);
     }
   } else {
-    for (int c = lane; c < nch; c += 64)
-      emit(c, reinterpret_cast<const u32x4*>(xr)[c], reinterpret_cast<const u32x4*>(w)[c]);
+    for (int c = lane; c < nch; c += 64) emit(c, chunk(c), reinterpret_cast<const u32x4*>(w)[c]);
   }
   if (lane < tail) {
     const int j = nch * 8 + lane;
-    const float t = __uint_as_float(uint32_t(xr[j]) << 16);
+    if constexpr (ADD) xr[j] = tail_v;
+    const float t = __uint_as_float(uint32_t(tail_v) << 16);
     const float wj = __uint_as_float(uint32_t(w[j]) << 16);
     const float o = (t * r) * wj;
     if (y_bf16)
@@ -321,23 +354,37 @@ int pick_cpt(int64_t nch) {
   return 0;
 }
 
+template <bool ADD>
+hipError_t launch_rmsnorm_impl(uint16_t* xp, int64_t ldx, const uint16_t* dp, int64_t ldd, const uint16_t* wp,
+                               float eps, void* y, int64_t ldy, bool y_bf16, int64_t m, int64_t n, hipStream_t s) {
+  const int yb = y_bf16 ? 1 : 0;
+  const dim3 grid((unsigned)m), block(64);
+#define BI_RMS(C) hipLaunchKernelGGL((rmsnorm_kernel<C, ADD>), grid, block, 0, s, xp, ldx, dp, ldd, wp, eps, y, ldy, yb, (int)n)
+  switch (pick_cpt(n / 8)) {
+    case 1: BI_RMS(1); break;
+    case 2: BI_RMS(2); break;
+    case 4: BI_RMS(4); break;
+    case 8: BI_RMS(8); break;
+    case 16: BI_RMS(16); break;
+    default: BI_RMS(0); break;
+  }
+#undef BI_RMS
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_rmsnorm(const void* x, int64_t ldx, const void* w, float eps, void* y, int64_t ldy,
                           bool y_bf16, int64_t m, int64_t n, hipStream_t s) {
-  const uint16_t* xp = static_cast<const uint16_t*>(x);
-  const uint16_t* wp = static_cast<const uint16_t*>(w);
-  const int yb = y_bf16 ? 1 : 0;
-  const dim3 grid((unsigned)m), block(64);
-  switch (pick_cpt(n / 8)) {
-    case 1: hipLaunchKernelGGL(rmsnorm_kernel<1>, grid, block, 0, s, xp, ldx, wp, eps, y, ldy, yb, (int)n); break;
-    case 2: hipLaunchKernelGGL(rmsnorm_kernel<2>, grid, block, 0, s, xp, ldx, wp, eps, y, ldy, yb, (int)n); break;
-    case 4: hipLaunchKernelGGL(rmsnorm_kernel<4>, grid, block, 0, s, xp, ldx, wp, eps, y, ldy, yb, (int)n); break;
-    case 8: hipLaunchKernelGGL(rmsnorm_kernel<8>, grid, block, 0, s, xp, ldx, wp, eps, y, ldy, yb, (int)n); break;
-    case 16: hipLaunchKernelGGL(rmsnorm_kernel<16>, grid, block, 0, s, xp, ldx, wp, eps, y, ldy, yb, (int)n); break;
-    default: hipLaunchKernelGGL(rmsnorm_kernel<0>, grid, block, 0, s, xp, ldx, wp, eps, y, ldy, yb, (int)n); break;
-  }
-  return hipGetLastError();
+  // the kernel's x is writable only in the residual form; here it is only read
+  return launch_rmsnorm_impl<false>(const_cast<uint16_t*>(static_cast<const uint16_t*>(x)), ldx, nullptr, 0,
+                                    static_cast<const uint16_t*>(w), eps, y, ldy, y_bf16, m, n, s);
+}
+
+hipError_t launch_add_rmsnorm(void* x, int64_t ldx, const void* d, int64_t ldd, const void* w, float eps, void* y,
+                              int64_t ldy, bool y_bf16, int64_t m, int64_t n, hipStream_t s) {
+  return launch_rmsnorm_impl<true>(static_cast<uint16_t*>(x), ldx, static_cast<const uint16_t*>(d), ldd,
+                                   static_cast<const uint16_t*>(w), eps, y, ldy, y_bf16, m, n, s);
 }
 
 hipError_t launch_mean(const void* x, bool x_bf16, int64_t ldx, float* y, int64_t m, int64_t n,

@@ -1,0 +1,115 @@
+"""One greedy decode step of a Qwen3-style model, end to end on the library.
+
+The pages judge batch invariance by a token stream: temperature-0
+completions of one prompt that agree for a long prefix and then fork,
+because the batch a request lands in changes the kernels' reduction order
+(readhandoff.com, agent-run reproducibility pinning, sections "What does
+temperature zero actually guarantee?" and "Where the divergence showed
+up"); the cost is measured on Qwen3-8B decoding ("Key takeaways"). This
+module chains the library's kernels into that per-token computation so a
+sequence's stream can be checked bit for bit across batch compositions.
+
+Per layer (activations bf16, weights [K, N] bf16, fp32 accumulation):
+
+    h = rmsnorm(x)                          bi_rmsnorm / bi_add_rmsnorm
+    qkv = h @ W_qkv                         bi_mm
+    q -> q_out; k, v -> paged cache         bi_qknorm_rope_append
+    a = attention(q, cache)                 bi_decode_attention (split 256)
+    x += a @ W_o ; h = rmsnorm(x)           bi_mm, bi_add_rmsnorm
+    x += silu(g) * u @ W_down               bi_mm, bi_silu_mul, bi_mm
+then logits = rmsnorm(x) @ W_lm + b_lm (bi_addmm, fp32), log-probabilities
+and the greedy token (bi_log_softmax). Every arithmetic step runs in the HIP
+kernels; torch only allocates and moves the few host-side plan integers
+(context lengths, split offsets) to the device.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import torch
+
+from . import (bi_add_rmsnorm, bi_addmm, bi_decode_attention, bi_decode_plan, bi_decode_workspace_bytes, bi_embed,
+               bi_log_softmax, bi_mm, bi_qknorm_rope_append, bi_rmsnorm, bi_silu_mul)
+
+__all__ = ["Qwen3Shape", "QWEN3_8B", "Batch", "Decoder"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Qwen3Shape:
+    hidden: int = 4096
+    num_q_heads: int = 32
+    num_kv_heads: int = 8
+    head_dim: int = 128
+    intermediate: int = 12288
+    vocab: int = 151936
+    layers: int = 36
+    eps: float = 1e-6
+    page_size: int = 16
+    split_tokens: int = 256
+
+
+QWEN3_8B = Qwen3Shape()
+
+
+@dataclasses.dataclass
+class Batch:
+    """The sequences of one step: their block tables (device int32
+    [B, max_pages], into the decoder's page pool) and how many tokens each
+    has cached before this step (host int32 [B])."""
+    block_table: torch.Tensor
+    lens: torch.Tensor
+
+
+class Decoder:
+    """Holds the weights and the paged KV cache (one page pool per layer).
+
+    weights: dict of device tensors, bf16 unless noted: embed [V, H];
+    lists over layers of w_in [H], w_qkv [H, (Hq + 2 Hkv) D], q_norm [D],
+    k_norm [D], w_o [Hq D, H], w_post [H], w_gu [H, 2 I], w_down [I, H];
+    w_final [H]; w_lm [H, V]; b_lm [V]; cos, sin fp32 [max_pos, D / 2].
+    """
+
+    def __init__(self, shape: Qwen3Shape, weights: dict, num_pages: int, device="cuda"):
+        s = shape
+        if s.num_q_heads * s.head_dim != s.hidden:
+            raise ValueError("hidden must equal num_q_heads * head_dim")
+        self.s, self.w = s, weights
+        self.k_pages = [torch.empty((num_pages, s.num_kv_heads, s.page_size, s.head_dim), dtype=torch.bfloat16,
+                                    device=device) for _ in range(s.layers)]
+        self.v_pages = [torch.empty_like(k) for k in self.k_pages]
+        self.device = device
+
+    def step(self, tokens: torch.Tensor, batch: Batch):
+        """Run one token per sequence. tokens: device int64 [B]. Appends the
+        tokens' k, v to the cache and advances batch.lens. Returns (fp32
+        logits [B, V], fp32 log-probabilities [B, V], greedy tokens int64 [B])."""
+        s, w = self.s, self.w
+        bsz = tokens.shape[0]
+        dev = self.device
+        lens_after = batch.lens + 1
+        if int(lens_after.max()) > batch.block_table.shape[1] * s.page_size:
+            raise ValueError("a sequence has no page left for the new token")
+        positions = batch.lens.to(dev, non_blocking=False)
+        offs, total = bi_decode_plan(lens_after, s.split_tokens)
+        lens_dev = lens_after.to(dev)
+        offs_dev = offs.to(dev)
+        ws = torch.empty(bi_decode_workspace_bytes(total, s.num_q_heads, s.head_dim), dtype=torch.uint8, device=dev)
+
+        x = bi_embed(w["embed"], tokens)
+        h = bi_rmsnorm(x, w["w_in"][0], s.eps)
+        for l in range(s.layers):
+            qkv = bi_mm(h, w["w_qkv"][l], out_dtype=torch.bfloat16)
+            q = bi_qknorm_rope_append(qkv, w["q_norm"][l], w["k_norm"][l], w["cos"], w["sin"], positions,
+                                      batch.block_table, self.k_pages[l], self.v_pages[l],
+                                      num_q_heads=s.num_q_heads, num_kv_heads=s.num_kv_heads, eps=s.eps)
+            a = bi_decode_attention(q, self.k_pages[l], self.v_pages[l], batch.block_table, lens_dev, offs_dev, total,
+                                    workspace=ws, out_dtype=torch.bfloat16, split_tokens=s.split_tokens)
+            o = bi_mm(a.view(bsz, s.hidden), w["w_o"][l], out_dtype=torch.bfloat16)
+            h = bi_add_rmsnorm(x, o, w["w_post"][l], s.eps)
+            gu = bi_mm(h, w["w_gu"][l], out_dtype=torch.bfloat16)
+            dn = bi_mm(bi_silu_mul(gu), w["w_down"][l], out_dtype=torch.bfloat16)
+            h = bi_add_rmsnorm(x, dn, w["w_in"][l + 1] if l + 1 < s.layers else w["w_final"], s.eps)
+        logits = bi_addmm(w["b_lm"], h, w["w_lm"])
+        logp, nxt = bi_log_softmax(logits)
+        batch.lens = lens_after
+        return logits, logp, nxt

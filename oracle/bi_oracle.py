@@ -57,6 +57,12 @@ __all__ = [
     "decode_split_counts",
     "relative_frobenius",
     "elementwise_ratio",
+    "round_bf16",
+    "bf16_bits_of",
+    "embed",
+    "add_rmsnorm",
+    "silu_mul",
+    "qknorm_rope",
 ]
 
 
@@ -268,3 +274,98 @@ def elementwise_ratio(got, ref) -> float:
     if got.size == 0:
         return 0.0
     return float(np.max(np.abs(got - ref) / (np.abs(ref) + 1.0)))
+
+
+# --------------------------------------------------------------------------
+# per-token steps of a decode step (the token path of the completions
+# experiment: readhandoff.com, agent-run reproducibility pinning, "Where the
+# divergence showed up"; Qwen3-8B decoding in its "Key takeaways")
+# --------------------------------------------------------------------------
+BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def round_bf16(v) -> np.ndarray:
+    """fp64 -> the nearest bfloat16 value (ties to even), returned as fp64.
+
+    bfloat16 keeps 8 significant bits: with v = m * 2^e, 0.5 <= |m| < 1,
+    the result is rint(m * 2^8) * 2^(e-8), where rint rounds half to even.
+    Magnitudes that round past the largest finite bfloat16 become inf.
+    (Below 2^-126, where bfloat16 loses precision gradually, this keeps 8
+    bits; no quantity here gets that small.)
+    """
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)
+    r = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+    return np.where(np.abs(r) > BF16_MAX, np.copysign(np.inf, v), r)
+
+
+def bf16_bits_of(v) -> np.ndarray:
+    """Bit patterns (uint16) of fp64 values that are already bfloat16 values
+    (as returned by round_bf16): the upper half of their exact fp32 form."""
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def embed(table_bits, tokens) -> np.ndarray:
+    """out[i] = table[tokens[i]] (a token outside the table gives a zero row)."""
+    tb = bf16_bits_to_f64(table_bits)
+    out = np.zeros((len(tokens), tb.shape[1]))
+    for i, t in enumerate(np.asarray(tokens)):
+        if 0 <= t < tb.shape[0]:
+            out[i] = tb[t]
+    return out
+
+
+def add_rmsnorm(x_bits, d_bits, w_bits, eps: float):
+    """Residual add then RMSNorm: x' = round_bf16(x + d) (the residual stream
+    is stored in bf16), y = rmsnorm(x'). Returns (x' as bf16 bits, y fp64)."""
+    xn = round_bf16(bf16_bits_to_f64(x_bits) + bf16_bits_to_f64(d_bits))
+    bits = bf16_bits_of(xn)
+    return bits, rmsnorm(bits, w_bits, eps)
+
+
+def silu_mul(gu_bits) -> np.ndarray:
+    """out_ij = silu(g_ij) * u_ij, g = gu[:, :n], u = gu[:, n:],
+    silu(g) = g / (1 + e^-g): the gated MLP activation of a Qwen3 layer."""
+    gu = bf16_bits_to_f64(gu_bits)
+    n = gu.shape[1] // 2
+    g, u = gu[:, :n], gu[:, n:]
+    return g / (1.0 + np.exp(-g)) * u
+
+
+def qknorm_rope(qkv_bits, q_norm_w_bits, k_norm_w_bits, eps: float, cos_tab, sin_tab, positions,
+                num_q_heads: int, num_kv_heads: int):
+    """Qwen3 attention prologue for one new token per sequence.
+
+    Each q and k head x (length D) is RMS-normalised with its weight,
+    t = w * x / sqrt(mean(x^2) + eps), then rotated at position p on the
+    pairs (i, i + D/2): (t_i, t_{i+D/2}) -> (t_i c - t_{i+D/2} s,
+    t_{i+D/2} c + t_i s) with c = cos_tab[p, i], s = sin_tab[p, i]. v heads
+    pass unchanged. Returns (q [B, Hq, D], k [B, Hkv, D], v [B, Hkv, D]) in
+    fp64.
+    """
+    qkv = bf16_bits_to_f64(qkv_bits)
+    bsz = qkv.shape[0]
+    d = 128
+    heads = qkv[:, :(num_q_heads + 2 * num_kv_heads) * d].reshape(bsz, num_q_heads + 2 * num_kv_heads, d)
+    qw = bf16_bits_to_f64(q_norm_w_bits)
+    kw = bf16_bits_to_f64(k_norm_w_bits)
+    cos = np.asarray(cos_tab, dtype=np.float64)
+    sin = np.asarray(sin_tab, dtype=np.float64)
+
+    def norm_rot(x, w, p):
+        t = w * x / np.sqrt(np.mean(x * x) + eps)
+        c, s = cos[p], sin[p]
+        a, b = t[:d // 2], t[d // 2:]
+        return np.concatenate([a * c - b * s, b * c + a * s])
+
+    q = np.empty((bsz, num_q_heads, d))
+    k = np.empty((bsz, num_kv_heads, d))
+    for i in range(bsz):
+        p = int(positions[i])
+        for h in range(num_q_heads):
+            q[i, h] = norm_rot(heads[i, h], qw, p)
+        for g in range(num_kv_heads):
+            k[i, g] = norm_rot(heads[i, num_q_heads + g], kw, p)
+    v = heads[:, num_q_heads + num_kv_heads:].copy()
+    return q, k, v

@@ -31,6 +31,7 @@ __all__ = [
     "paged_kv_layout",
     "bf16_bits_numpy",
     "f32_numpy",
+    "rope_tables",
 ]
 
 
@@ -108,3 +109,15 @@ def bf16_bits_numpy(t: torch.Tensor):
 
 def f32_numpy(t: torch.Tensor):
     return t.detach().cpu().contiguous().to(torch.float32).numpy()
+
+
+def rope_tables(max_pos: int, head_dim: int = 128, theta: float = 1.0e6):
+    """The rotary-embedding angle table both sides take as an input:
+    angle[p, i] = p * theta^(-2i / head_dim) for i < head_dim / 2, evaluated
+    in float64 and stored as fp32 (cos, sin) [max_pos, head_dim / 2].
+    theta = 1e6 is the Qwen3 base. It is the input of the rotation, not the
+    rotation itself, which each side applies on its own."""
+    i = torch.arange(head_dim // 2, dtype=torch.float64)
+    inv = theta ** (-2.0 * i / head_dim)
+    ang = torch.arange(max_pos, dtype=torch.float64)[:, None] * inv[None, :]
+    return torch.cos(ang).to(torch.float32), torch.sin(ang).to(torch.float32)

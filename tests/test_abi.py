@@ -33,7 +33,8 @@ def test_header_symbols_exported(bi):
     names = declared_functions()
     assert {"bi_mm", "bi_addmm", "bi_rmsnorm", "bi_mean", "bi_log_softmax", "bi_decode_plan",
             "bi_decode_workspace_bytes", "bi_decode_attention", "bi_status_string",
-            "bi_last_error_message", "bi_gemm_config"} <= set(names)
+            "bi_last_error_message", "bi_gemm_config", "bi_add_rmsnorm", "bi_embed", "bi_silu_mul",
+            "bi_qknorm_rope_append"} <= set(names)
     raw = ctypes.CDLL(bi.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), f"{n} declared in bi.h but not exported"
@@ -138,6 +139,36 @@ def test_decode_validation(bi):
     assert attn(bi, ws=None) == WORKSPACE
     assert attn(bi, q=A2) == ALIGN
     assert attn(bi, batch=0, q=None, k=None) == OK
+
+
+def test_decode_step_kernels_validation(bi):
+    L = bi.lib
+    # bi_add_rmsnorm(x, ldx, d, ldd, w, eps, y, ldy, y_dtype, m, n, stream)
+    ar = lambda **k: L.bi_add_rmsnorm(k.get("x", A16), k.get("ldx", 64), k.get("d", A16), k.get("ldd", 64),  # noqa
+                                      k.get("w", A16), 1e-6, k.get("y", A16), k.get("ldy", 64), k.get("dt", 0),
+                                      k.get("m", 2), k.get("n", 64), None)
+    assert ar(m=-1) == SHAPE and ar(dt=5) == DTYPE and ar(n=0) == SHAPE and ar(d=None) == NULL
+    assert ar(ldd=32) == STRIDE and ar(ldd=68) == ALIGN and ar(d=A2) == ALIGN and ar(m=0, x=None) == OK
+    # bi_embed(table, ld, vocab, tokens, out, ldo, m, n, stream)
+    em = lambda **k: L.bi_embed(k.get("t", A16), k.get("ld", 64), k.get("v", 100), k.get("tok", A16),  # noqa
+                                k.get("o", A16), k.get("ldo", 64), k.get("m", 3), k.get("n", 64), None)
+    assert em(v=-1) == SHAPE and em(v=0) == SHAPE and em(tok=None) == NULL and em(ld=32) == STRIDE
+    assert em(n=60, ld=64, ldo=64) == ALIGN and em(tok=A2 + 4 - 2) == ALIGN and em(m=0, t=None) == OK
+    # bi_silu_mul(gu, ldg, out, ldo, m, n, stream)
+    sm = lambda **k: L.bi_silu_mul(k.get("gu", A16), k.get("ldg", 128), k.get("o", A16), k.get("ldo", 64),  # noqa
+                                   k.get("m", 2), k.get("n", 64), None)
+    assert sm(m=-2) == SHAPE and sm(o=None) == NULL and sm(ldg=64) == STRIDE and sm(n=60, ldg=120, ldo=64) == ALIGN
+    assert sm(m=70000) == UNSUPPORTED and sm(m=0, gu=None) == OK
+    # bi_qknorm_rope_append(qkv, ldqkv, qw, kw, eps, cos, sin, max_pos, pos, bt, max_pages, num_pages,
+    #                       kp, vp, q_out, batch, hq, hkv, head_dim, page_size, stream)
+    def qr(**k):
+        return L.bi_qknorm_rope_append(k.get("qkv", A16), k.get("ld", 6144), A16, A16, 1e-6, A16, A16,
+                                       k.get("max_pos", 4096), A16, A16, k.get("max_pages", 8), k.get("pages", 64),
+                                       A16, A16, k.get("q_out", A16), k.get("b", 2), k.get("hq", 32),
+                                       k.get("hkv", 8), k.get("d", 128), k.get("page", 16), None)
+    assert qr(b=-1) == SHAPE and qr(d=64) == UNSUPPORTED and qr(page=0) == UNSUPPORTED
+    assert qr(q_out=None) == NULL and qr(ld=6000) == STRIDE and qr(pages=0) == SHAPE
+    assert qr(qkv=A2 + 1) == ALIGN and qr(b=0, qkv=None) == OK
 
 
 def test_decode_plan_and_workspace(bi):
