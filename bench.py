@@ -17,6 +17,11 @@ Each kernel has a roofline time t_min = max(flops / 2.5 PFLOP/s, bytes /
 8 TB/s) from its algorithmic flops and bytes. ``value`` is the whole step's
 roofline fraction: sum of t_min over the step / measured step time, in %.
 
+Reported beside it (not part of ``value``): ``e2e_decode_step``, greedy
+decode steps of a Qwen3-8B-shaped model (36 layers, random weights, 64
+sequences with lengths log-uniform in [1, 32768]) chained through the
+library, with its own HBM bound.
+
 Prints ONE JSON line on stdout; a human-readable table goes to stderr.
 """
 from __future__ import annotations
@@ -330,6 +335,62 @@ def sweep(torch, S, bi):
     print("\n".join(rows))
 
 
+E2E_BATCH = 64
+E2E_STEPS = 3
+
+
+def e2e_decode(torch, S, bi, dev, steps=E2E_STEPS, warmup=1, batch_size=E2E_BATCH):
+    """Greedy decode steps of a Qwen3-8B-shaped model (all 36 layers, random
+    weights) for batch_size sequences whose cached lengths are log-uniform
+    in [1, 32768], every step through the library's kernels. Reported next
+    to the per-kernel metric, not folded into it. Its roofline: the bytes a
+    step must move at least (every weight once, the whole KV cache once,
+    activations and logits) over 8 TB/s."""
+    from invariant_bi_mm_amd.decode import QWEN3_8B, Batch, Decoder
+    s = QWEN3_8B
+    t0 = time.time()
+    w = S.qwen3_weights(s.hidden, s.num_q_heads, s.num_kv_heads, s.head_dim, s.intermediate, s.vocab, s.layers,
+                        seed=20000, device=dev)
+    lens = S.context_lens(batch_size, seed=21000)
+    room = steps + warmup
+    table, num_pages = S.paged_kv_layout(lens + room, s.page_size, seed=21001)
+    dec = Decoder(s, w, num_pages=num_pages, device=dev)
+    for l in range(s.layers):  # the cached context: random keys and values
+        dec.k_pages[l].normal_()
+        dec.v_pages[l].normal_()
+    batch = Batch(block_table=table.to(dev), lens=lens.clone())
+    tok = torch.randint(0, s.vocab, (batch_size,), generator=S.generator(21002)).to(dev)
+    torch.cuda.synchronize()
+    log(f"e2e decode: weights + {num_pages} cache pages x {s.layers} layers ready in {time.time() - t0:.1f}s")
+    for _ in range(warmup):
+        _, _, tok = dec.step(tok, batch)
+    torch.cuda.synchronize()
+    ctx0 = int(batch.lens.sum())
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        _, _, tok = dec.step(tok, batch)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    h, i_, v = s.hidden, s.intermediate, s.vocab
+    qkv_n = (s.num_q_heads + 2 * s.num_kv_heads) * s.head_dim
+    w_bytes = 2 * s.layers * (h * qkv_n + h * h + h * 2 * i_ + i_ * h) + 2 * h * v + 2 * v
+    ctx_mid = ctx0 + batch_size * (steps + 1) / 2  # cached tokens read, averaged over the timed steps
+    kv_bytes = 2 * 2 * s.num_kv_heads * s.head_dim * s.layers * ctx_mid
+    act_bytes = batch_size * (2 * h + 4 * v * 3 + 8)  # embed row, logits + log-probs written, logits read, token
+    t_min_ms = (w_bytes + kv_bytes + act_bytes) / PEAK_HBM * 1e3
+    res = {"model": "Qwen3-8B-shaped (36 layers, hidden 4096, 32/8 heads, intermediate 12288, vocab 151936), "
+                    "random weights", "batch": batch_size, "context_tokens_at_start": ctx0,
+           "steps": steps, "ms_per_step": round(ms, 3), "tokens_per_s": round(batch_size / (ms / 1e3), 1),
+           "hbm_bytes_min_per_step": w_bytes + kv_bytes + act_bytes, "roofline_frac": round(t_min_ms / ms, 4)}
+    log(f"e2e decode: {ms:.2f} ms/step at batch {batch_size} ({res['tokens_per_s']:.0f} tokens/s), "
+        f"{100 * t_min_ms / ms:.1f}% of the HBM bound ({t_min_ms:.2f} ms)")
+    del dec, w
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -337,6 +398,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--no-torch", action="store_true", help="skip the non-invariant torch baseline")
+    ap.add_argument("--no-e2e", action="store_true", help="skip the end-to-end decode-step measurement")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
                     help="measured HBM traffic per kernel (written from rocprofv3 FETCH_SIZE/WRITE_SIZE runs)")
     ap.add_argument("--sweep", action="store_true",
@@ -417,6 +479,8 @@ def main():
     roof["algorithmic_per_launch"] = {"flops": f, "bytes": b}
     roof["avg_launch_ms"] = per[dom]
 
+    e2e = None if args.no_e2e else e2e_decode(torch, S, bi, dev)
+
     torch_base = None
     if not args.no_torch:
         tops = [(n, fn, *work[n]) for n, fn in wl.torch_ops()]
@@ -459,6 +523,7 @@ def main():
         },
         "per_kernel_ms": {k: round(v, 4) for k, v in per.items()},
         "roofline": roof,
+        "e2e_decode_step": e2e,
         "torch_baseline": torch_base,
         "cpu_baseline": cpu,
     }

@@ -133,25 +133,8 @@ def test_qknorm_rope_append_rejects_bad_positions_without_writing(lib):
 
 # ---------------------------------------------------------------- end to end
 def make_weights(shape, layers, seed, device=DEV, max_pos=40000, qk_norm=(0.5, 1.5)):
-    """Random Qwen3-style weights (variance 0.02 for the projections, as for
-    the projection GEMM workloads; norm weights U(0.5, 1.5), the q/k ones
-    U(qk_norm); bias N(0, 0.1))."""
-    h, d = shape.hidden, shape.head_dim
-    qkv_n = (shape.num_q_heads + 2 * shape.num_kv_heads) * d
-    r = lambda s, var, k: S.normal_bf16(s, var, seed=seed + k, device=device)  # noqa: E731
-    u = lambda n, k, lo=0.5, hi=1.5: S.uniform_bf16((n,), lo, hi, seed=seed + k, device=device)  # noqa: E731
-    w = {"embed": r((shape.vocab, h), 1.0, 1),
-         "w_in": [u(h, 100 + l) for l in range(layers)], "w_post": [u(h, 200 + l) for l in range(layers)],
-         "q_norm": [u(d, 300 + l, *qk_norm) for l in range(layers)],
-         "k_norm": [u(d, 400 + l, *qk_norm) for l in range(layers)],
-         "w_qkv": [r((h, qkv_n), 0.02, 500 + l) for l in range(layers)],
-         "w_o": [r((h, h), 0.02, 600 + l) for l in range(layers)],
-         "w_gu": [r((h, 2 * shape.intermediate), 0.02, 700 + l) for l in range(layers)],
-         "w_down": [r((shape.intermediate, h), 0.02, 800 + l) for l in range(layers)],
-         "w_final": u(h, 2), "w_lm": r((h, shape.vocab), 0.02, 3), "b_lm": r((shape.vocab,), 0.1, 4)}
-    cos, sin = S.rope_tables(max_pos, d)
-    w["cos"], w["sin"] = cos.to(device), sin.to(device)
-    return w
+    return S.qwen3_weights(shape.hidden, shape.num_q_heads, shape.num_kv_heads, shape.head_dim, shape.intermediate,
+                           shape.vocab, layers, seed, device=device, max_pos=max_pos, qk_norm=qk_norm)
 
 
 def prompt_cache(shape, layers, length, seed):
