@@ -145,15 +145,22 @@ class Workload:
         return out
 
 
-def source_digest():
-    """sha256 over the HIP sources; measured traffic is tied to it."""
+# The HIP source that defines each step's kernel (with the shared headers,
+# the input of a per-kernel digest: measured traffic stays valid until that
+# kernel's own source changes).
+KERNEL_SOURCE = {"gemm_qkv": "gemm.hip", "gemm_o": "gemm.hip", "gemm_gateup": "gemm.hip", "gemm_down": "gemm.hip",
+                 "lm_head": "gemm.hip", "lm_logsm": "rowreduce.hip", "rmsnorm": "rowreduce.hip",
+                 "mean": "rowreduce.hip", "logsm": "rowreduce.hip", "decode_attn": "decode_attention.hip"}
+
+
+def source_digest(kernel: str) -> str:
+    """sha256 over the HIP source defining `kernel` and the shared headers."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "invariant_bi_mm_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as fh:
-                h.update(name.encode() + b"\0" + fh.read())
+    for name in (KERNEL_SOURCE[kernel], "bi_internal.h", "device_common.h"):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(name.encode() + b"\0" + fh.read())
     return h.hexdigest()
 
 
@@ -465,9 +472,10 @@ def main():
     if args.traffic and os.path.exists(args.traffic):
         with open(args.traffic) as fh:
             rec = json.load(fh)
-        # counters are only valid for the kernel sources they were taken on
-        if rec.get("source_sha256") == source_digest():
-            traffic = rec.get("kernels", {}).get(dom, {}).get("hbm_bytes_per_launch")
+        # counters are only valid for the kernel source they were taken on
+        kr = rec.get("kernels", {}).get(dom, {})
+        if kr.get("source_sha256") == source_digest(dom):
+            traffic = kr.get("hbm_bytes_per_launch")
     if is_mfma:
         roof = {"bound": "mfma", "achieved": f / (per[dom] / 1e3) / 1e12, "peak": PEAK_BF16 / 1e12,
                 "unit": "TFLOP/s"}
