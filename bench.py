@@ -20,7 +20,9 @@ roofline fraction: sum of t_min over the step / measured step time, in %.
 Reported beside it (not part of ``value``): ``e2e_decode_step``, greedy
 decode steps of a Qwen3-8B-shaped model (36 layers, random weights, 64
 sequences with lengths log-uniform in [1, 32768]) chained through the
-library, with its own HBM bound.
+library, with its own HBM bound; and ``prefill_attention``, causal prefill of
+4 prompts of 2048 tokens with the decode split structure, against the fp32
+vector-ALU peak.
 
 Prints ONE JSON line on stdout; a human-readable table goes to stderr.
 """
@@ -398,6 +400,46 @@ def e2e_decode(torch, S, bi, dev, steps=E2E_STEPS, warmup=1, batch_size=E2E_BATC
     return res
 
 
+PEAK_F32_VALU = 157.3e12  # MI355X fp32 vector FLOP/s (published)
+PREFILL_SEQS, PREFILL_TOKENS = 4, 2048
+
+
+def prefill_measure(torch, S, bi, dev, reps=5):
+    """Causal prefill attention of PREFILL_SEQS prompts of PREFILL_TOKENS
+    tokens (Qwen3-8B heads: 32 q / 8 kv, head_dim 128, one layer), with the
+    decode split structure so every token's output equals its decode-step
+    bits. Its arithmetic is fp32 vector FMA (the decode arithmetic), so the
+    roofline is the fp32 vector peak; algorithmic flops = 4 * D * Hq *
+    sum over tokens of (position + 1) (QK and PV, 2 flops per multiply-add)."""
+    n, T = PREFILL_SEQS, PREFILL_TOKENS
+    lens = torch.full((n,), T, dtype=torch.int32)
+    table, npages = S.paged_kv_layout(lens, 16, seed=22000)
+    kp = S.normal_bf16((npages, 8, 16, 128), 1.0, seed=22001, device=dev)
+    vp = S.normal_bf16((npages, 8, 16, 128), 1.0, seed=22002, device=dev)
+    q = S.normal_bf16((n * T, 32, 128), 1.0, seed=22003, device=dev)
+    q_pos, q_offs, work, sizes = bi.bi_prefill_plan(lens, torch.zeros(n, dtype=torch.int32))
+    qp, qo, wk, tb = q_pos.to(dev), q_offs.to(dev), work.to(dev), table.to(dev)
+    ws = torch.empty(bi.bi_decode_workspace_bytes(sizes[1], 32, 128), dtype=torch.uint8, device=dev)
+    out = torch.empty((n * T, 32, 128), dtype=torch.float32, device=dev)
+    f = lambda: bi.bi_prefill_attention(q, kp, vp, tb, qp, qo, wk, sizes, workspace=ws, out=out)  # noqa: E731
+    f()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        f()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 4.0 * 128 * 32 * n * (T * (T + 1) / 2)
+    res = {"sequences": n, "tokens_per_sequence": T, "ms": round(ms, 3), "TFLOP/s": round(flops / ms / 1e9, 1),
+           "bound": "alu (fp32 vector FMA)", "peak_TFLOP/s": PEAK_F32_VALU / 1e12,
+           "frac": round(flops / (ms / 1e3) / PEAK_F32_VALU, 4), "tokens_per_s": round(n * T / (ms / 1e3))}
+    log(f"prefill attention: {n} x {T} tokens in {ms:.3f} ms, {res['TFLOP/s']} TFLOP/s "
+        f"({100 * res['frac']:.1f}% of the fp32 vector peak)")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -405,7 +447,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--no-torch", action="store_true", help="skip the non-invariant torch baseline")
-    ap.add_argument("--no-e2e", action="store_true", help="skip the end-to-end decode-step measurement")
+    ap.add_argument("--no-e2e", action="store_true",
+                    help="skip the end-to-end decode-step and prefill measurements")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
                     help="measured HBM traffic per kernel (written from rocprofv3 FETCH_SIZE/WRITE_SIZE runs)")
     ap.add_argument("--sweep", action="store_true",
@@ -488,6 +531,7 @@ def main():
     roof["avg_launch_ms"] = per[dom]
 
     e2e = None if args.no_e2e else e2e_decode(torch, S, bi, dev)
+    pre = None if args.no_e2e else prefill_measure(torch, S, bi, dev)
 
     torch_base = None
     if not args.no_torch:
@@ -532,6 +576,7 @@ def main():
         "per_kernel_ms": {k: round(v, 4) for k, v in per.items()},
         "roofline": roof,
         "e2e_decode_step": e2e,
+        "prefill_attention": pre,
         "torch_baseline": torch_base,
         "cpu_baseline": cpu,
     }

@@ -208,6 +208,58 @@ bi_status bi_decode_attention(const void* q, const void* k_pages, const void* v_
                               void* out, bi_dtype out_dtype, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Prefill / extend attention with the decode split structure.
+ *
+ * A chunk of new tokens per sequence (already appended to the cache)
+ * attends causally: the token at position p sees tokens 0..p of its
+ * sequence. Its reduction is cut at the same multiples of split_tokens as a
+ * decode step with p + 1 cached tokens, each split is reduced with the very
+ * arithmetic of bi_decode_attention's split kernel, and the partials are
+ * merged by its combine. So a token's output has the same bits whether it is
+ * prefilled in any chunking, in any batch, or decoded -- the chunked-prefill
+ * side of the batch dependence the pages trace to attention (readhandoff.com,
+ * agent-run reproducibility pinning, "What does temperature zero actually
+ * guarantee?"; "Batch-invariant inference kernels (Thinking Machines) --
+ * Evidence & limits", "Evidence" and "Limitations").
+ * ------------------------------------------------------------------------ */
+
+/* Host-side plan. Query rows are the chunk tokens of sequence 0, then of
+ * sequence 1, ...: sequence b contributes host_chunk_lens[b] rows at
+ * positions host_ctx_before[b], host_ctx_before[b] + 1, ... (HOST arrays
+ * [batch]). Call once with host_q_pos, host_q_offsets and host_work all NULL
+ * to get out_sizes[3] = {rows, total_splits, n_work}; then again with
+ *   host_q_pos      int32 [rows]       each row's position,
+ *   host_q_offsets  int32 [rows + 1]   split offsets: sum over earlier rows
+ *                                      of ceil((pos + 1) / split_tokens),
+ *   host_work       int32 [4 n_work]   work items (first row, row count <= 8,
+ *                                      sequence, split), split-major per
+ *                                      sequence.
+ * Returns BI_OK or an error status (the message in bi_last_error_message). */
+bi_status bi_prefill_plan(const int32_t* host_chunk_lens, const int32_t* host_ctx_before, int64_t batch,
+                          int split_tokens, int32_t* host_q_pos, int32_t* host_q_offsets, int32_t* host_work,
+                          int64_t* out_sizes);
+
+/* bi_prefill_attention
+ *   q            bf16 [rows, num_q_heads, head_dim], contiguous (row order as
+ *                in the plan).
+ *   k_pages, v_pages, block_table [batch, max_pages]: as bi_decode_attention;
+ *                the cache must already hold every chunk token.
+ *   q_pos, q_offsets, work: the plan's arrays, on the DEVICE.
+ *   n_work, n_rows, total_splits: the plan's sizes.
+ *   workspace    >= bi_decode_workspace_bytes(total_splits, num_q_heads,
+ *                head_dim) bytes.
+ *   out          [rows, num_q_heads, head_dim], out_dtype.
+ * Supported set as bi_decode_attention (BI_ERR_UNSUPPORTED otherwise). The
+ * cache must hold finite values in the slots the chunk sees. */
+bi_status bi_prefill_attention(const void* q, const void* k_pages, const void* v_pages,
+                               const int32_t* block_table, int64_t max_pages, const int32_t* q_pos,
+                               const int32_t* q_offsets, const int32_t* work, int64_t n_work, int64_t n_rows,
+                               int64_t total_splits, int64_t batch, int num_q_heads, int num_kv_heads,
+                               int head_dim, int page_size, int split_tokens, float scale,
+                               void* workspace, size_t workspace_bytes, void* out, bi_dtype out_dtype,
+                               hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Per-token steps of a decode step (Qwen3-style layer). They carry one
  * sequence's greedy token stream from logits back to the next layer input.
  * The pages trace non-reproducible completions to the batch a request lands

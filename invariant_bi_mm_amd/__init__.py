@@ -23,6 +23,7 @@ __all__ = [
     "bi_mm", "bi_addmm", "bi_gemm_config", "bi_rmsnorm", "bi_mean", "bi_log_softmax",
     "bi_decode_plan", "bi_decode_workspace_bytes", "bi_decode_attention",
     "bi_add_rmsnorm", "bi_embed", "bi_silu_mul", "bi_qknorm_rope_append",
+    "bi_prefill_plan", "bi_prefill_attention",
     "bi_status_string", "bi_last_error_message",
     "BI_BF16", "BI_F32", "STATUS",
 ]
@@ -69,6 +70,11 @@ lib.bi_silu_mul.restype = _st
 lib.bi_qknorm_rope_append.argtypes = [_vp, _i64, _vp, _vp, _f32, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _vp,
                                       _i64, _i32, _i32, _i32, _i32, _vp]
 lib.bi_qknorm_rope_append.restype = _st
+lib.bi_prefill_plan.argtypes = [_vp, _vp, _i64, _i32, _vp, _vp, _vp, _vp]
+lib.bi_prefill_plan.restype = _st
+lib.bi_prefill_attention.argtypes = [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _i32,
+                                     _i32, _i32, _i32, _f32, _vp, _sz, _vp, _i32, _vp]
+lib.bi_prefill_attention.restype = _st
 lib.bi_status_string.argtypes = [_st]
 lib.bi_status_string.restype = ctypes.c_char_p
 lib.bi_last_error_message.argtypes = []
@@ -348,3 +354,53 @@ def bi_qknorm_rope_append(qkv, q_norm_w, k_norm_w, cos_tab, sin_tab, positions, 
                                      block_table.shape[1], num_pages, _ptr(k_pages), _ptr(v_pages), _ptr(q_out), bsz,
                                      num_q_heads, num_kv_heads, d, page, _stream(stream)))
     return q_out
+
+
+def bi_prefill_plan(chunk_lens_host: torch.Tensor, ctx_before_host: torch.Tensor, split_tokens: int = 256):
+    """Host plan for bi_prefill_attention: (q_pos [rows], q_offsets [rows+1], work [n_work, 4]) int32 CPU
+    tensors and (rows, total_splits, n_work)."""
+    cl = chunk_lens_host.to(torch.int32).contiguous()
+    cb = ctx_before_host.to(torch.int32).contiguous()
+    if cl.device.type != "cpu" or cb.device.type != "cpu" or cl.shape != cb.shape or cl.dim() != 1:
+        raise ValueError("chunk_lens and ctx_before must be 1-D host tensors of one length")
+    sizes = (ctypes.c_int64 * 3)()
+    _check(lib.bi_prefill_plan(_ptr(cl), _ptr(cb), cl.shape[0], int(split_tokens), None, None, None, sizes))
+    rows, total, n_work = (int(x) for x in sizes)
+    q_pos = torch.empty(max(rows, 1), dtype=torch.int32)
+    q_offs = torch.empty(rows + 1, dtype=torch.int32)
+    work = torch.empty((max(n_work, 1), 4), dtype=torch.int32)
+    _check(lib.bi_prefill_plan(_ptr(cl), _ptr(cb), cl.shape[0], int(split_tokens), _ptr(q_pos), _ptr(q_offs),
+                               _ptr(work), sizes))
+    return q_pos[:rows], q_offs, work[:n_work], (rows, total, n_work)
+
+
+def bi_prefill_attention(q, k_pages, v_pages, block_table, q_pos, q_offsets, work, sizes, *, scale=None,
+                         split_tokens: int = 256, workspace=None, out=None, out_dtype: torch.dtype = torch.float32,
+                         stream=None):
+    """Causal attention of chunk tokens over their sequences' paged cache, with the decode split structure.
+    q [rows, Hq, D] bf16; q_pos, q_offsets, work: the plan's arrays on the device; sizes: the plan's tuple."""
+    _need_bf16(q, "q")
+    _need_bf16(k_pages, "k_pages")
+    _need_bf16(v_pages, "v_pages")
+    rows, total, n_work = sizes
+    nr, hq, d = q.shape
+    if nr != rows:
+        raise ValueError("q has a different number of rows than the plan")
+    _, hkv, page, d2 = k_pages.shape
+    for t, nm in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (block_table, "block_table"),
+                  (q_pos, "q_pos"), (q_offsets, "q_offsets"), (work, "work")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if scale is None:
+        scale = d ** -0.5
+    need = bi_decode_workspace_bytes(total, hq, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((rows, hq, d), dtype=out_dtype, device=q.device)
+    _check(lib.bi_prefill_attention(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), block_table.shape[1],
+                                    _ptr(q_pos), _ptr(q_offsets), _ptr(work), n_work, rows, total,
+                                    block_table.shape[0], hq, hkv, d, page, int(split_tokens), float(scale),
+                                    _ptr(workspace), workspace.numel(), _ptr(out), _dtype_code(out.dtype),
+                                    _stream(stream)))
+    return out

@@ -8,6 +8,8 @@
 #include <cstdio>
 #include <string>
 
+#include <algorithm>
+
 #include "bi_internal.h"
 
 namespace {
@@ -250,6 +252,110 @@ bi_status bi_decode_attention(const void* q, const void* k_pages, const void* v_
   p.out = out;
   p.out_bf16 = out_dtype == BI_BF16;
   return hip_status(bi::launch_decode_attention(p, stream), "decode attention launch");
+}
+
+bi_status bi_prefill_plan(const int32_t* host_chunk_lens, const int32_t* host_ctx_before, int64_t batch,
+                          int split_tokens, int32_t* host_q_pos, int32_t* host_q_offsets, int32_t* host_work,
+                          int64_t* out_sizes) {
+  if (batch < 0 || split_tokens <= 0) return fail(BI_ERR_SHAPE, "batch < 0 or split_tokens <= 0");
+  if (out_sizes == nullptr) return fail(BI_ERR_NULL, "out_sizes is NULL");
+  if (batch > 0 && (host_chunk_lens == nullptr || host_ctx_before == nullptr))
+    return fail(BI_ERR_NULL, "chunk_lens or ctx_before is NULL");
+  const bool fill = host_q_pos != nullptr || host_q_offsets != nullptr || host_work != nullptr;
+  if (fill && (host_q_pos == nullptr || host_q_offsets == nullptr || host_work == nullptr))
+    return fail(BI_ERR_NULL, "q_pos, q_offsets and work must all be given (or all NULL for the sizes)");
+  const int64_t qb = bi::prefill_rows_per_item();
+  int64_t rows = 0, splits = 0, items = 0;
+  for (int64_t b = 0; b < batch; ++b) {
+    const int64_t n = host_chunk_lens[b], c0 = host_ctx_before[b];
+    if (n < 0 || c0 < 0) return fail(BI_ERR_SHAPE, "chunk_lens[%lld] or ctx_before[%lld] < 0", (long long)b, (long long)b);
+    if (c0 + n > INT_MAX) return fail(BI_ERR_UNSUPPORTED, "a position exceeds 2^31-1");
+    if (n == 0) continue;
+    // rows of this sequence, their positions and split offsets
+    for (int64_t i = 0; i < n; ++i) {
+      if (fill) {
+        host_q_pos[rows + i] = (int32_t)(c0 + i);
+        host_q_offsets[rows + i] = (int32_t)splits;
+      }
+      splits += (c0 + i + split_tokens) / split_tokens;  // ceil((pos + 1) / split_tokens)
+      if (splits > INT_MAX) return fail(BI_ERR_UNSUPPORTED, "total split count exceeds 2^31-1");
+    }
+    // work items: split-major, so the blocks sharing a split's K/V run together
+    const int64_t blocks = (n + qb - 1) / qb;
+    const int64_t max_split = (c0 + n - 1) / split_tokens;
+    for (int64_t sp = 0; sp <= max_split; ++sp) {
+      for (int64_t k = 0; k < blocks; ++k) {
+        const int64_t r0 = k * qb, nr = std::min(qb, n - r0);
+        const int64_t last = c0 + r0 + nr - 1;  // position of the block's last row
+        if (last < sp * split_tokens) continue;   // no row of the block sees this split
+        if (fill) {
+          host_work[4 * items + 0] = (int32_t)(rows + r0);
+          host_work[4 * items + 1] = (int32_t)nr;
+          host_work[4 * items + 2] = (int32_t)b;
+          host_work[4 * items + 3] = (int32_t)sp;
+        }
+        ++items;
+      }
+    }
+    rows += n;
+    if (rows > INT_MAX || items > INT_MAX) return fail(BI_ERR_UNSUPPORTED, "too many rows or work items");
+  }
+  if (fill) host_q_offsets[rows] = (int32_t)splits;
+  out_sizes[0] = rows;
+  out_sizes[1] = splits;
+  out_sizes[2] = items;
+  return ok();
+}
+
+bi_status bi_prefill_attention(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                               int64_t max_pages, const int32_t* q_pos, const int32_t* q_offsets, const int32_t* work,
+                               int64_t n_work, int64_t n_rows, int64_t total_splits, int64_t batch, int num_q_heads,
+                               int num_kv_heads, int head_dim, int page_size, int split_tokens, float scale,
+                               void* workspace, size_t workspace_bytes, void* out, bi_dtype out_dtype,
+                               hipStream_t stream) {
+  if (n_rows < 0 || n_work < 0 || total_splits < 0 || batch < 0 || max_pages < 0)
+    return fail(BI_ERR_SHAPE, "negative size");
+  if (!valid_dtype(out_dtype)) return fail(BI_ERR_DTYPE, "out_dtype %d is not BI_BF16 or BI_F32", (int)out_dtype);
+  if (head_dim != 128 || page_size != 16 || split_tokens != 256 || num_kv_heads < 1 ||
+      num_q_heads != 4 * num_kv_heads)
+    return fail(BI_ERR_UNSUPPORTED,
+                "supported: head_dim 128, page_size 16, split_tokens 256, num_q_heads = 4 * num_kv_heads "
+                "(got %d, %d, %d, %d/%d)",
+                head_dim, page_size, split_tokens, num_q_heads, num_kv_heads);
+  if (n_rows == 0) return ok();
+  if (q == nullptr || k_pages == nullptr || v_pages == nullptr || block_table == nullptr || q_pos == nullptr ||
+      q_offsets == nullptr || work == nullptr || out == nullptr)
+    return fail(BI_ERR_NULL, "a required pointer is NULL");
+  if (max_pages < 1 || batch < 1 || n_work < 1) return fail(BI_ERR_SHAPE, "max_pages, batch and n_work must be >= 1");
+  if (total_splits < n_rows) return fail(BI_ERR_SHAPE, "total_splits < n_rows (every row has at least one split)");
+  if (n_work * num_kv_heads > INT_MAX || n_rows > INT_MAX || num_q_heads > 65535)
+    return fail(BI_ERR_UNSUPPORTED, "grid size out of range");
+  const size_t need = bi_decode_workspace_bytes(total_splits, num_q_heads, head_dim);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(BI_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(workspace, 16) ||
+      !aligned(out, dsize(out_dtype)) || !aligned(block_table, 4) || !aligned(q_pos, 4) || !aligned(q_offsets, 4) ||
+      !aligned(work, 4))
+    return fail(BI_ERR_ALIGN, "q, k_pages, v_pages, workspace must be 16-byte aligned");
+  bi::PrefillParams p;
+  p.q = q;
+  p.k_pages = k_pages;
+  p.v_pages = v_pages;
+  p.block_table = block_table;
+  p.q_pos = q_pos;
+  p.q_offsets = q_offsets;
+  p.work = work;
+  p.max_pages = max_pages;
+  p.n_work = n_work;
+  p.n_rows = n_rows;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.scale = scale;
+  p.ws_o = static_cast<float*>(workspace);
+  p.ws_ml = p.ws_o + total_splits * num_q_heads * head_dim;
+  p.out = out;
+  p.out_bf16 = out_dtype == BI_BF16;
+  return hip_status(bi::launch_prefill_attention(p, stream), "prefill attention launch");
 }
 
 bi_status bi_add_rmsnorm(void* x, int64_t ldx, const void* d, int64_t ldd, const void* w, float eps, void* y,

@@ -58,6 +58,27 @@ struct DecodeParams {
 };
 hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t stream);
 
+struct PrefillParams {
+  const void* q;
+  const void* k_pages;
+  const void* v_pages;
+  const int32_t* block_table;
+  const int32_t* q_pos;
+  const int32_t* q_offsets;
+  const int32_t* work;
+  int64_t max_pages;
+  int64_t n_work, n_rows;
+  int num_q_heads, num_kv_heads;
+  float scale;
+  float* ws_o;
+  float* ws_ml;
+  void* out;
+  bool out_bf16;
+};
+hipError_t launch_prefill_attention(const PrefillParams& p, hipStream_t stream);
+// Query rows per prefill work item (the kernel's block of rows sharing one split's K/V).
+int prefill_rows_per_item();
+
 hipError_t launch_embed(const void* table, int64_t ld, int64_t vocab, const int64_t* tokens, void* out, int64_t ldo,
                         int64_t m, int64_t n, hipStream_t stream);
 hipError_t launch_silu_mul(const void* gu, int64_t ldg, void* out, int64_t ldo, int64_t m, int64_t n,

@@ -60,6 +60,122 @@ struct SplitArgs {
   float* ws_ml;
 };
 
+// ---------------------------------------------------------------------------
+// The per-(query, split) arithmetic, shared by the decode and the prefill
+// kernels so that a token's partials have the same bits whichever computes
+// them. Thread layout: 256 threads = 16 groups of 16 lanes; lane dl of group
+// grp owns head-dim slice [8 dl, 8 dl + 8) of slot grp of each of the split's
+// pages, i.e. of tokens j * PAGE + grp, j = 0..PPS-1.
+// ---------------------------------------------------------------------------
+
+// q of the GQA heads h = 0..3 of one query, scaled by scale * log2(e).
+__device__ __forceinline__ void load_q(const uint16_t* q_row, int dl, float qscale, float (&qf)[GQA][8]) {
+#pragma unroll
+  for (int h = 0; h < GQA; ++h) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(q_row + h * HD + dl * 8);
+    unpack8(v, qf[h]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[h][e] = qf[h][e] * qscale;
+  }
+}
+
+// Phase 1: S[h][i] = log2-domain score of token i of the split for head h,
+// -inf for i >= nt: an 8-term fma chain per lane, then the 16-lane butterfly.
+__device__ __forceinline__ void split_scores(const float (&qf)[GQA][8], const u32x4 (&kv)[PPS], int grp, int dl, int nt,
+                                             float (*S)[SPLIT]) {
+#pragma unroll
+  for (int j = 0; j < PPS; ++j) {
+    const int i = j * PAGE + grp;
+    float kf[8];
+    unpack8(kv[j], kf);
+    float dot[GQA];
+#pragma unroll
+    for (int h = 0; h < GQA; ++h) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(qf[h][e], kf[e], acc);
+      dot[h] = group16_sum(acc);
+    }
+    if (dl < GQA) S[dl][i] = (i < nt) ? dot[dl] : -INFINITY;
+  }
+}
+
+// Phase 2, one row (query, head) by one wave: exact max, p = 2^(s - max)
+// written back, l = sum p (per-lane order, then the wave butterfly).
+__device__ __forceinline__ void split_softmax_row(float* row, int lane, float& mx_out, float& l_out) {
+  float v[SPLIT / 64];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < SPLIT / 64; ++r) {
+    v[r] = row[lane + 64 * r];
+    mx = fmaxf(mx, v[r]);
+  }
+  mx = wave_max(mx);
+  float l = 0.0f;
+#pragma unroll
+  for (int r = 0; r < SPLIT / 64; ++r) {
+    const float pr = __builtin_amdgcn_exp2f(v[r] - mx);  // 2^-inf = 0 for masked slots
+    row[lane + 64 * r] = pr;
+    l = l + pr;
+  }
+  mx_out = mx;
+  l_out = wave_sum(l);
+}
+
+// Phase 3 for one query: o[h][e] = sum_j p(token j * PAGE + grp) v[e] (fma
+// chain in j), then the 4 groups of a wave merged (xor 16, then xor 32).
+__device__ __forceinline__ void split_pv(const u32x4 (&kv)[PPS], const float (*S)[SPLIT], int grp, float (&o)[GQA][8]) {
+#pragma unroll
+  for (int h = 0; h < GQA; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < PPS; ++j) {
+    const int i = j * PAGE + grp;
+    float vf[8];
+    unpack8(kv[j], vf);
+#pragma unroll
+    for (int h = 0; h < GQA; ++h) {
+      const float pr = S[h][i];  // 0 for masked slots
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] = __builtin_fmaf(pr, vf[e], o[h][e]);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < GQA; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float t = o[h][e];
+      t = t + xor_shfl(t, 16);
+      t = t + xor_shfl(t, 32);
+      o[h][e] = t;
+    }
+}
+
+// The 4 waves' o merged in wave order, written as the split's partial:
+// thread handles (h, d) pairs tid and tid + 256.
+__device__ __forceinline__ void write_partial(const float (*O)[GQA][HD], int tid, float* ws_o_base) {
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int idx = tid + 256 * r;
+    const int h = idx >> 7, d = idx & (HD - 1);
+    ws_o_base[h * HD + d] = ((O[0][h][d] + O[1][h][d]) + O[2][h][d]) + O[3][h][d];
+  }
+}
+
+// K (or V) of the split's tokens this thread owns; slots at or past nt read 0.
+__device__ __forceinline__ void load_kv(const uint16_t* pages, const int32_t* bt, int64_t page_stride, int64_t slot_off,
+                                        int grp, int nt, u32x4 (&kv)[PPS]) {
+#pragma unroll
+  for (int j = 0; j < PPS; ++j) {
+    kv[j] = u32x4{0u, 0u, 0u, 0u};
+    if (j * PAGE + grp < nt) {
+      const int64_t page = bt[j];
+      kv[j] = *reinterpret_cast<const u32x4*>(pages + page * page_stride + slot_off);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
   __shared__ float S[GQA][SPLIT];
   __shared__ float O[4][GQA][HD];
@@ -94,107 +210,28 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
   const int32_t* bt = a.bt + (int64_t)b * a.max_pages + t0 / PAGE;
 
   float qf[GQA][8];
-#pragma unroll
-  for (int h = 0; h < GQA; ++h) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * a.hq + g * GQA + h) * HD + dl * 8);
-    unpack8(v, qf[h]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qf[h][e] = qf[h][e] * a.qscale;
-  }
+  load_q(a.q + ((int64_t)b * a.hq + g * GQA) * HD, dl, a.qscale, qf);
 
   const int64_t head_stride = (int64_t)PAGE * HD;           // one head-page
   const int64_t page_stride = (int64_t)a.hkv * head_stride;  // one physical page
   const int64_t slot_off = (int64_t)g * head_stride + (int64_t)grp * HD + dl * 8;
 
-  // ---- phase 1: scores
   u32x4 kv[PPS];
-#pragma unroll
-  for (int j = 0; j < PPS; ++j) {
-    kv[j] = u32x4{0u, 0u, 0u, 0u};
-    if (j * PAGE + grp < nt) {
-      const int64_t page = bt[j];
-      kv[j] = *reinterpret_cast<const u32x4*>(a.kp + page * page_stride + slot_off);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < PPS; ++j) {
-    const int i = j * PAGE + grp;
-    float kf[8];
-    unpack8(kv[j], kf);
-    float dot[GQA];
-#pragma unroll
-    for (int h = 0; h < GQA; ++h) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(qf[h][e], kf[e], acc);
-      dot[h] = group16_sum(acc);
-    }
-    if (dl < GQA) S[dl][i] = (i < nt) ? dot[dl] : -INFINITY;
-  }
+  load_kv(a.kp, bt, page_stride, slot_off, grp, nt, kv);
+  split_scores(qf, kv, grp, dl, nt, S);
   __syncthreads();
-
-  // ---- phase 2: per query head (wave h) max, p, sum p
   {
-    const int h = wave;
-    float v[SPLIT / 64];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < SPLIT / 64; ++r) {
-      v[r] = S[h][lane + 64 * r];
-      mx = fmaxf(mx, v[r]);
-    }
-    mx = wave_max(mx);
-    float l = 0.0f;
-#pragma unroll
-    for (int r = 0; r < SPLIT / 64; ++r) {
-      const float p = __builtin_amdgcn_exp2f(v[r] - mx);  // 2^-inf = 0 for padded slots
-      S[h][lane + 64 * r] = p;
-      l = l + p;
-    }
-    l = wave_sum(l);
+    float mx, l;
+    split_softmax_row(S[wave], lane, mx, l);  // wave h: query head h
     if (lane == 0) {
-      ML[h][0] = mx;
-      ML[h][1] = l;
+      ML[wave][0] = mx;
+      ML[wave][1] = l;
     }
   }
   __syncthreads();
-
-  // ---- phase 3: o = sum p v
-#pragma unroll
-  for (int j = 0; j < PPS; ++j) {
-    kv[j] = u32x4{0u, 0u, 0u, 0u};
-    if (j * PAGE + grp < nt) {
-      const int64_t page = bt[j];
-      kv[j] = *reinterpret_cast<const u32x4*>(a.vp + page * page_stride + slot_off);
-    }
-  }
+  load_kv(a.vp, bt, page_stride, slot_off, grp, nt, kv);
   float o[GQA][8];
-#pragma unroll
-  for (int h = 0; h < GQA; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[h][e] = 0.0f;
-#pragma unroll
-  for (int j = 0; j < PPS; ++j) {
-    const int i = j * PAGE + grp;
-    float vf[8];
-    unpack8(kv[j], vf);
-#pragma unroll
-    for (int h = 0; h < GQA; ++h) {
-      const float p = S[h][i];  // 0 for padded slots, whose v is 0 too
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] = __builtin_fmaf(p, vf[e], o[h][e]);
-    }
-  }
-  // merge the 4 groups of this wave (xor 16, then xor 32)
-#pragma unroll
-  for (int h = 0; h < GQA; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float t = o[h][e];
-      t = t + xor_shfl(t, 16);
-      t = t + xor_shfl(t, 32);
-      o[h][e] = t;
-    }
+  split_pv(kv, S, grp, o);
   if (lane < 16) {
 #pragma unroll
     for (int h = 0; h < GQA; ++h)
@@ -202,18 +239,103 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
       for (int e = 0; e < 8; ++e) O[wave][h][dl * 8 + e] = o[h][e];
   }
   __syncthreads();
-  // merge the 4 waves in wave order; thread handles (h, d) pairs tid, tid+256
   const int64_t base = (int64_t)w * a.hq + g * GQA;
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int idx = tid + 256 * r;
-    const int h = idx >> 7, d = idx & (HD - 1);
-    const float t = ((O[0][h][d] + O[1][h][d]) + O[2][h][d]) + O[3][h][d];
-    a.ws_o[(base + h) * HD + d] = t;
-  }
+  write_partial(O, tid, a.ws_o + base * HD);
   if (tid < GQA) {
     a.ws_ml[(base + tid) * 2 + 0] = ML[tid][0];
     a.ws_ml[(base + tid) * 2 + 1] = ML[tid][1];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill / extend: the tokens of a chunk attend causally to their sequence's
+// cache (which already holds them). Query row r at position p uses exactly
+// the split structure of a decode step with p + 1 cached tokens: splits
+// s = 0 .. ceil((p + 1) / SPLIT) - 1, each reduced by the functions above
+// with nt = min(SPLIT, p + 1 - s * SPLIT), merged by the decode combine
+// kernel. So a prefilled token's output has the bits a decode step would
+// give it, whatever the chunking and the batch.
+//
+// One workgroup per (work item, kv head); a work item is up to QB
+// consecutive query rows of one sequence and one split they see. The split's
+// K and V are loaded once for all of them (slots past the last row's nt read
+// 0); for an earlier row, the slots it must not see carry p = 0, and
+// fma(0, v, o) = o for finite v, so they add nothing.
+// ---------------------------------------------------------------------------
+constexpr int QB = 8;
+
+struct PrefillArgs {
+  const uint16_t* q;  // [rows, hq, HD]
+  const uint16_t* kp;
+  const uint16_t* vp;
+  const int32_t* bt;    // [batch, max_pages]
+  const int32_t* pos;   // [rows]
+  const int32_t* qoffs; // [rows + 1]
+  const int32_t* work;  // [n_work, 4]: row0, n_rows, sequence, split
+  int64_t max_pages;
+  int hq, hkv;
+  float qscale;
+  float* ws_o;
+  float* ws_ml;
+};
+
+__global__ __launch_bounds__(256) void prefill_split_kernel(PrefillArgs a) {
+  __shared__ float S[QB][GQA][SPLIT];
+  __shared__ float O[4][GQA][HD];
+  __shared__ float ML[QB][GQA][2];
+
+  const int wi = blockIdx.x / a.hkv, g = blockIdx.x % a.hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int grp = tid >> 4, dl = tid & 15;
+  const int row0 = a.work[4 * wi], nq = a.work[4 * wi + 1], b = a.work[4 * wi + 2], s = a.work[4 * wi + 3];
+  const int t0 = s * SPLIT;
+  const int nt_max = min(SPLIT, a.pos[row0 + nq - 1] + 1 - t0);
+  const int32_t* bt = a.bt + (int64_t)b * a.max_pages + t0 / PAGE;
+  const int64_t head_stride = (int64_t)PAGE * HD;
+  const int64_t page_stride = (int64_t)a.hkv * head_stride;
+  const int64_t slot_off = (int64_t)g * head_stride + (int64_t)grp * HD + dl * 8;
+
+  u32x4 kv[PPS];
+  load_kv(a.kp, bt, page_stride, slot_off, grp, nt_max, kv);
+  for (int t = 0; t < nq; ++t) {
+    const int nt = min(SPLIT, a.pos[row0 + t] + 1 - t0);  // <= 0: this row does not see the split
+    float qf[GQA][8];
+    load_q(a.q + ((int64_t)(row0 + t) * a.hq + g * GQA) * HD, dl, a.qscale, qf);
+    split_scores(qf, kv, grp, dl, nt, S[t]);
+  }
+  __syncthreads();
+  for (int r = wave; r < nq * GQA; r += 4) {
+    float mx, l;
+    split_softmax_row(S[r / GQA][r % GQA], lane, mx, l);
+    if (lane == 0) {
+      ML[r / GQA][r % GQA][0] = mx;
+      ML[r / GQA][r % GQA][1] = l;
+    }
+  }
+  __syncthreads();
+  load_kv(a.vp, bt, page_stride, slot_off, grp, nt_max, kv);
+  for (int t = 0; t < nq; ++t) {
+    const int row = row0 + t;
+    const bool sees = a.pos[row] + 1 - t0 > 0;
+    float o[GQA][8];
+    split_pv(kv, S[t], grp, o);
+    if (lane < 16) {
+#pragma unroll
+      for (int h = 0; h < GQA; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) O[wave][h][dl * 8 + e] = o[h][e];
+    }
+    __syncthreads();
+    if (sees) {
+      const int64_t base = (int64_t)(a.qoffs[row] + s) * a.hq + g * GQA;
+      write_partial(O, tid, a.ws_o + base * HD);
+      if (tid < GQA) {
+        a.ws_ml[(base + tid) * 2 + 0] = ML[t][tid][0];
+        a.ws_ml[(base + tid) * 2 + 1] = ML[t][tid][1];
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -319,5 +441,30 @@ hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t s) {
                      p.split_offsets, p.ws_o, p.ws_ml, p.num_q_heads, p.out, p.out_bf16 ? 1 : 0);
   return hipGetLastError();
 }
+
+hipError_t launch_prefill_attention(const PrefillParams& p, hipStream_t s) {
+  PrefillArgs a;
+  a.q = static_cast<const uint16_t*>(p.q);
+  a.kp = static_cast<const uint16_t*>(p.k_pages);
+  a.vp = static_cast<const uint16_t*>(p.v_pages);
+  a.bt = p.block_table;
+  a.pos = p.q_pos;
+  a.qoffs = p.q_offsets;
+  a.work = p.work;
+  a.max_pages = p.max_pages;
+  a.hq = p.num_q_heads;
+  a.hkv = p.num_kv_heads;
+  a.qscale = p.scale * LOG2E;
+  a.ws_o = p.ws_o;
+  a.ws_ml = p.ws_ml;
+  hipLaunchKernelGGL(prefill_split_kernel, dim3((unsigned)(p.n_work * p.num_kv_heads)), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)p.n_rows, (unsigned)p.num_q_heads), dim3(256), 0, s,
+                     p.q_offsets, p.ws_o, p.ws_ml, p.num_q_heads, p.out, p.out_bf16 ? 1 : 0);
+  return hipGetLastError();
+}
+
+int prefill_rows_per_item() { return QB; }
 
 }  // namespace bi

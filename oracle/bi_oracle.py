@@ -55,6 +55,7 @@ __all__ = [
     "decode_attention",
     "decode_attention_split",
     "decode_split_counts",
+    "prefill_attention",
     "relative_frobenius",
     "elementwise_ratio",
     "round_bf16",
@@ -203,6 +204,28 @@ def decode_attention(q_bits, k_pages_bits, v_pages_bits, block_table, context_le
                 s = scale * (k @ q[b, h])
                 p = np.exp(s - s.max())
                 out[b, h] = (p / p.sum()) @ v
+    return out
+
+
+def prefill_attention(q_bits, k_pages_bits, v_pages_bits, block_table, q_seq, q_pos, scale: float) -> np.ndarray:
+    """Causal attention of chunk tokens: row r (sequence q_seq[r], position
+    p = q_pos[r]) attends tokens 0..p of its sequence, out[r, h] =
+    softmax_t(scale * q[r, h] . K_t) V over those p + 1 tokens, kv head
+    h // (Hq / Hkv). The cache already holds the chunk's tokens."""
+    q = bf16_bits_to_f64(q_bits)
+    rows, hq, d = q.shape
+    hkv = k_pages_bits.shape[1]
+    group = hq // hkv
+    out = np.empty((rows, hq, d))
+    for r in range(rows):
+        b, L = int(q_seq[r]), int(q_pos[r]) + 1
+        for g in range(hkv):
+            k = gather_kv(k_pages_bits, block_table, L, g, b)
+            v = gather_kv(v_pages_bits, block_table, L, g, b)
+            for h in range(g * group, (g + 1) * group):
+                sc = scale * (k @ q[r, h])
+                p = np.exp(sc - sc.max())
+                out[r, h] = (p / p.sum()) @ v
     return out
 
 

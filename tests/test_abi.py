@@ -34,7 +34,7 @@ def test_header_symbols_exported(bi):
     assert {"bi_mm", "bi_addmm", "bi_rmsnorm", "bi_mean", "bi_log_softmax", "bi_decode_plan",
             "bi_decode_workspace_bytes", "bi_decode_attention", "bi_status_string",
             "bi_last_error_message", "bi_gemm_config", "bi_add_rmsnorm", "bi_embed", "bi_silu_mul",
-            "bi_qknorm_rope_append"} <= set(names)
+            "bi_qknorm_rope_append", "bi_prefill_plan", "bi_prefill_attention"} <= set(names)
     raw = ctypes.CDLL(bi.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), f"{n} declared in bi.h but not exported"
@@ -169,6 +169,52 @@ def test_decode_step_kernels_validation(bi):
     assert qr(b=-1) == SHAPE and qr(d=64) == UNSUPPORTED and qr(page=0) == UNSUPPORTED
     assert qr(q_out=None) == NULL and qr(ld=6000) == STRIDE and qr(pages=0) == SHAPE
     assert qr(qkv=A2 + 1) == ALIGN and qr(b=0, qkv=None) == OK
+
+
+def test_prefill_plan_rows_offsets_and_work_cover_every_visible_split(bi):
+    import numpy as np
+    chunk = torch.tensor([3, 20, 0, 5, 17, 1], dtype=torch.int32)
+    ctx = torch.tensor([0, 250, 7, 510, 0, 1000], dtype=torch.int32)
+    q_pos, q_offs, work, (rows, total, n_work) = bi.bi_prefill_plan(chunk, ctx)
+    assert rows == int(chunk.sum()) and q_offs.shape[0] == rows + 1 and int(q_offs[-1]) == total
+    seq = np.repeat(np.arange(len(chunk)), chunk.numpy())
+    want_pos = np.concatenate([np.arange(c, c + n) for c, n in zip(ctx.tolist(), chunk.tolist())])
+    assert np.array_equal(q_pos.numpy(), want_pos)
+    nsplit = (want_pos + 256) // 256
+    assert np.array_equal(np.diff(q_offs.numpy()), nsplit)
+    seen = {}
+    for r0, nr, b, sp in work.tolist():
+        assert 1 <= nr <= 8 and np.all(seq[r0:r0 + nr] == b)                       # one sequence per item
+        assert np.array_equal(want_pos[r0:r0 + nr], np.arange(want_pos[r0], want_pos[r0] + nr))
+        assert want_pos[r0 + nr - 1] >= 256 * sp                                   # its last row sees the split
+        for r in range(r0, r0 + nr):
+            if want_pos[r] >= 256 * sp:
+                assert (r, sp) not in seen
+                seen[(r, sp)] = True
+    assert len(seen) == total  # every (row, visible split) exactly once
+    # sizes-only call, and errors
+    sizes = (ctypes.c_int64 * 3)()
+    L = bi.lib
+    cl, cb = chunk.contiguous(), ctx.contiguous()
+    assert L.bi_prefill_plan(cl.data_ptr(), cb.data_ptr(), 6, 256, None, None, None, sizes) == OK
+    assert tuple(sizes) == (rows, total, n_work)
+    assert L.bi_prefill_plan(cl.data_ptr(), cb.data_ptr(), 6, 0, None, None, None, sizes) == SHAPE
+    assert L.bi_prefill_plan(cl.data_ptr(), cb.data_ptr(), 6, 256, None, None, None, None) == NULL
+    assert L.bi_prefill_plan(cl.data_ptr(), cb.data_ptr(), 6, 256, A16, None, None, sizes) == NULL
+    bad = torch.tensor([-1], dtype=torch.int32)
+    assert L.bi_prefill_plan(bad.data_ptr(), cb.data_ptr(), 1, 256, None, None, None, sizes) == SHAPE
+
+
+def test_prefill_attention_validation(bi):
+    def pa(**k):
+        return bi.lib.bi_prefill_attention(A16, A16, A16, A16, k.get("max_pages", 4), A16, A16, A16,
+                                           k.get("n_work", 3), k.get("rows", 10), k.get("total", 12), k.get("b", 2),
+                                           k.get("hq", 32), k.get("hkv", 8), k.get("d", 128), 16, k.get("split", 256),
+                                           0.088, k.get("ws", A16), k.get("wsb", 1 << 30), k.get("out", A16),
+                                           k.get("dt", 1), None)
+    assert pa(rows=-1) == SHAPE and pa(dt=3) == DTYPE and pa(d=64) == UNSUPPORTED and pa(split=128) == UNSUPPORTED
+    assert pa(hq=16) == UNSUPPORTED and pa(out=None) == NULL and pa(n_work=0) == SHAPE
+    assert pa(total=5) == SHAPE and pa(wsb=100) == WORKSPACE and pa(ws=A2) == ALIGN and pa(rows=0, out=None) == OK
 
 
 def test_decode_plan_and_workspace(bi):

@@ -191,3 +191,48 @@ def test_decoder_rows_are_independent_and_one_token_cache_attends_to_itself():
     qkv = O.bf16_bits_of(O.round_bf16(O.mm(h, w["w_qkv"][0])))
     d1.step(np.array([1]))
     assert np.array_equal(d1.kv[0][0][1][0, 0], O.bf16_bits_to_f64(qkv)[0, 5 * 128:6 * 128])
+
+
+# ------------------------------------------------------------------ prefill attention
+def _paged(rng, lens, hkv=1, page=16):
+    pages = sum((L + page - 1) // page for L in lens)
+    perm = rng.permutation(pages)
+    table = np.zeros((len(lens), max((L + page - 1) // page for L in lens)), dtype=np.int32)
+    off = 0
+    for b, L in enumerate(lens):
+        n = (L + page - 1) // page
+        table[b, :n] = perm[off:off + n]
+        off += n
+    return rand_bf16(rng, (pages, hkv, page, 128)), rand_bf16(rng, (pages, hkv, page, 128)), table
+
+
+def test_prefill_first_token_sees_only_itself_and_rows_equal_decode():
+    rng = np.random.default_rng(6)
+    kp, vp, table = _paged(rng, [40, 300])
+    q_seq, q_pos = [0, 0, 0, 1, 1], [0, 17, 39, 255, 299]
+    q = rand_bf16(rng, (5, 4, 128))
+    out = O.prefill_attention(q, kp, vp, table, q_seq, q_pos, 128 ** -0.5)
+    v0 = O.bf16_bits_to_f64(vp[table[0, 0], 0, 0])
+    for h in range(4):
+        assert np.array_equal(out[0, h], v0)  # softmax over one token is exactly 1
+    # each row is the decode attention of its sequence truncated to p + 1 tokens
+    for r in range(5):
+        one = O.decode_attention(q[r:r + 1], kp, vp, table[q_seq[r]:q_seq[r] + 1], [q_pos[r] + 1], 128 ** -0.5)
+        assert np.allclose(out[r], one[0], rtol=1e-13, atol=1e-13)
+
+
+def test_prefill_brute_force_causal_mask():
+    # two tokens, scores a and b: row 1 = (e^a v0 + e^b v1) / (e^a + e^b), computed with fsum
+    rng = np.random.default_rng(7)
+    kp, vp, table = _paged(rng, [2])
+    q = rand_bf16(rng, (2, 4, 128))
+    out = O.prefill_attention(q, kp, vp, table, [0, 0], [0, 1], 0.125)
+    K = O.bf16_bits_to_f64(kp[table[0, 0], 0, :2])
+    V = O.bf16_bits_to_f64(vp[table[0, 0], 0, :2])
+    qq = O.bf16_bits_to_f64(q)
+    for h in range(4):
+        s = [0.125 * math.fsum(qq[1, h] * K[t]) for t in range(2)]
+        w = [math.exp(x - max(s)) for x in s]
+        want = [math.fsum([w[0] * V[0, d], w[1] * V[1, d]]) / math.fsum(w) for d in range(128)]
+        assert np.allclose(out[1, h], want, rtol=1e-13, atol=1e-14)
+        assert np.array_equal(out[0, h], V[0])
