@@ -69,6 +69,14 @@ __device__ __forceinline__ int swz(int row, int ch) {
   return row * 8 + (ch ^ ((row ^ (row >> 3)) & 7));
 }
 
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 // Workgroup id -> (tile_m, tile_n). Bijective on [0, tiles).
 __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int tiles = tiles_m * tiles_n;
@@ -217,12 +225,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
   const int tr_lo = 2 * (tr_g & 1) + ((tr_l & 3) >> 1);  // chunk within the 4-chunk group
   const int tr_in = 4 * (tr_l & 1);                      // element within the chunk
 
-  // Fragments of one 16-wide k step from LDS stage d, and the FM x FN MFMAs
-  // that consume them. The k loop below keeps two fragment sets so the LDS
-  // reads of step kk+1 are in flight while the MFMAs of step kk run.
-  auto frags = [&](int kk, const u32x4* as, const u32x4* bs, bf16x8* af, bf16x8* bfr) {
+  // Fragments of one 16-wide k step from LDS stage d, and the MFMAs that
+  // consume them, for the first FMV of the wave's FM 32-row blocks (FMV is a
+  // compile-time count, see below). The k loop keeps two fragment sets so the
+  // LDS reads of step kk+1 are in flight while the MFMAs of step kk run.
+  auto frags = [&](auto FMV, int kk, const u32x4* as, const u32x4* bs, bf16x8* af, bf16x8* bfr) {
+    constexpr int fmv = decltype(FMV)::value;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) af[i] = __builtin_bit_cast(bf16x8, as[swz(arow0 + i * 32, kk * 2 + khalf)]);
+    for (int i = 0; i < fmv; ++i) af[i] = __builtin_bit_cast(bf16x8, as[swz(arow0 + i * 32, kk * 2 + khalf)]);
     if constexpr (B_NK) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) bfr[j] = __builtin_bit_cast(bf16x8, bs[swz(brow0 + j * 32, kk * 2 + khalf)]);
@@ -240,9 +250,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
       }
     }
   };
-  auto mma = [&](const bf16x8* af, const bf16x8* bfr) {
+  auto mma = [&](auto FMV, const bf16x8* af, const bf16x8* bfr) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < decltype(FMV)::value; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
@@ -255,32 +265,52 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
   // disjoint alias scopes, so the compiler does not make the reads of one
   // stage wait for the loads still landing in the other. A load past the
   // last tile reads zeros into the unused stage.
+  //
+  // FMV: how many of the wave's FM 32-row blocks hold rows below M. A block
+  // wholly past M is neither read from LDS nor multiplied -- its outputs are
+  // never stored, and every stored element still gets the same MFMA chain.
+  // Each wave runs the loop copy for its own count (one branch before the
+  // loop); all copies load and meet at the barriers alike. Full tiles take
+  // the FMV = FM copy, which is the plain loop.
   static_assert(TK / 16 == 4, "the k step pipeline below assumes four 16-wide steps per tile");
   bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-  auto step = [&](int kt, const u32x4* __restrict__ as, const u32x4* __restrict__ bs, u32x4* __restrict__ as_w,
-                  u32x4* __restrict__ bs_w) {
-    load(kt + 1, as_w, bs_w);
-    // keep the loads at the head of the tile: nothing in this block consumes
-    // them, and the scheduler would otherwise sink them to the barrier
-    __builtin_amdgcn_sched_barrier(0);
-    frags(0, as, bs, fa0, fb0);
-    frags(1, as, bs, fa1, fb1);
-    mma(fa0, fb0);
-    frags(2, as, bs, fa0, fb0);
-    mma(fa1, fb1);
-    frags(3, as, bs, fa1, fb1);
-    mma(fa0, fb0);
-    mma(fa1, fb1);
+  auto kloop = [&](auto FMV) {
+    auto step = [&](int kt, const u32x4* __restrict__ as, const u32x4* __restrict__ bs, u32x4* __restrict__ as_w,
+                    u32x4* __restrict__ bs_w) {
+      load(kt + 1, as_w, bs_w);
+      // keep the loads at the head of the tile: nothing in this block consumes
+      // them, and the scheduler would otherwise sink them to the barrier
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (decltype(FMV)::value > 0) {
+        frags(FMV, 0, as, bs, fa0, fb0);
+        frags(FMV, 1, as, bs, fa1, fb1);
+        mma(FMV, fa0, fb0);
+        frags(FMV, 2, as, bs, fa0, fb0);
+        mma(FMV, fa1, fb1);
+        frags(FMV, 3, as, bs, fa1, fb1);
+        mma(FMV, fa0, fb0);
+        mma(FMV, fa1, fb1);
+      }
+      __syncthreads();
+    };
+    load(0, As0, Bs0);
     __syncthreads();
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, As0, Bs0, As1, Bs1);
+      step(kt + 1, As1, Bs1, As0, Bs0);
+    }
+    if (kt < nk) step(kt, As0, Bs0, As1, Bs1);
   };
-  load(0, As0, Bs0);
-  __syncthreads();
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    step(kt, As0, Bs0, As1, Bs1);
-    step(kt + 1, As1, Bs1, As0, Bs0);
+  const int wave_rows = M - m0 - wm * WTM;  // wave-uniform
+  const int fmv = wave_rows <= 0 ? 0 : min(FM, (wave_rows + 31) / 32);
+  if (fmv == FM) {
+    kloop(std::integral_constant<int, FM>{});
+  } else {
+    static_for<0, FM>([&](auto I) {
+      if (fmv == decltype(I)::value) kloop(I);
+    });
   }
-  if (kt < nk) step(kt, As0, Bs0, As1, Bs1);
 
   // Epilogue: lane holds C[8*(r/4) + 4*(lane/32) + r%4][lane%32] of each
   // 32x32 tile, r = 0..15.
@@ -366,11 +396,7 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   if (cfg.tile_m == TM_ && cfg.tile_n == TN_ && cfg.waves == WM_ * WN_)                            \
     return p.b_is_nk ? launch_cfg<TM_, TN_, WM_, WN_, true>(a, s) : launch_cfg<TM_, TN_, WM_, WN_, false>(a, s);
   BI_GEMM_CASE(128, 128, 2, 2)
-  BI_GEMM_CASE(256, 128, 2, 2)
-  BI_GEMM_CASE(128, 256, 2, 2)
-  BI_GEMM_CASE(256, 256, 2, 2)
   BI_GEMM_CASE(256, 256, 2, 4)
-  BI_GEMM_CASE(256, 128, 4, 2)
 #undef BI_GEMM_CASE
   return hipErrorInvalidConfiguration;
 }
