@@ -240,3 +240,30 @@ def test_decode_token_stream_is_batch_invariant_qwen3_8b_shape(lib):
         assert stream == runs[0][0]
         for (l0, p0), (l1, p1) in zip(runs[0][1], rows):
             assert same_bits(l0, l1) and same_bits(p0, p1)
+
+
+def test_per_token_kernels_are_batch_invariant(lib):
+    """A fixed row through add_rmsnorm, silu_mul, embed and the q/k prologue alone and inside
+    batches of other random rows, at several positions: identical bytes."""
+    n = 4096
+    row_x = S.normal_bf16((1, n), 1.0, seed=800, device=DEV)
+    row_d = S.normal_bf16((1, n), 1.0, seed=801, device=DEV)
+    row_gu = S.normal_bf16((1, 2 * 12288), 4.0, seed=802, device=DEV)
+    w = S.uniform_bf16((n,), 0.5, 1.5, seed=803, device=DEV)
+    x1 = row_x.clone()
+    y1 = lib.bi_add_rmsnorm(x1, row_d, w)
+    s1 = lib.bi_silu_mul(row_gu)
+    table = S.normal_bf16((5000, n), 1.0, seed=804, device=DEV)
+    e1 = lib.bi_embed(table, torch.tensor([4321], dtype=torch.int64, device=DEV))
+    for m in (2, 7, 64, 300):
+        for pos in (0, m // 2, m - 1):
+            x = S.normal_bf16((m, n), 1.0, seed=810 + m, device=DEV)
+            d = S.normal_bf16((m, n), 1.0, seed=820 + m, device=DEV)
+            gu = S.normal_bf16((m, 2 * 12288), 4.0, seed=830 + m, device=DEV)
+            x[pos], d[pos], gu[pos] = row_x[0], row_d[0], row_gu[0]
+            y = lib.bi_add_rmsnorm(x, d, w)
+            assert same_bits(y[pos], y1[0]) and same_bits(x[pos], x1[0])
+            assert same_bits(lib.bi_silu_mul(gu)[pos], s1[0])
+            tok = torch.randint(0, 5000, (m,), generator=torch.Generator().manual_seed(m)).to(DEV)
+            tok[pos] = 4321
+            assert same_bits(lib.bi_embed(table, tok)[pos], e1[0])
