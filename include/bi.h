@@ -188,7 +188,11 @@ size_t bi_decode_workspace_bytes(int64_t total_splits, int num_q_heads, int head
  *   context_lens  int32 [batch], each >= 1 and <= max_pages * page_size.
  *   split_offsets int32 [batch + 1] on the DEVICE, as written by
  *                 bi_decode_plan for the same lengths and split_tokens.
- *   total_splits  split_offsets[batch].
+ *   total_splits  split_offsets[batch], or any upper bound of it: the
+ *                 kernels read the exact count from split_offsets[batch] on
+ *                 the device, and workgroups past it exit at once. One
+ *                 captured launch can so serve steps whose lengths grow.
+ *                 The workspace must hold total_splits splits.
  *   scale         multiplier of q . k (normally 1 / sqrt(head_dim)).
  *   workspace     device buffer of at least bi_decode_workspace_bytes().
  *   out           [batch, num_q_heads, head_dim], contiguous, out_dtype.

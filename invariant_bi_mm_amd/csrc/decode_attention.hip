@@ -190,6 +190,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int grp = tid >> 4;  // 0..15
   const int dl = tid & 15;   // head-dim slice
+  // The grid may cover more splits than exist (the host passes an upper
+  // bound so one captured launch serves growing lengths): the exact count is
+  // split_offsets[batch], and workgroups past it have nothing to do.
+  if (w >= a.offs[a.batch]) return;
 
   // sequence owning split w: the b with offs[b] <= w < offs[b+1]. The
   // offsets are read with coalesced loads and compared in parallel (one

@@ -31,7 +31,7 @@ import torch
 from . import (bi_add_rmsnorm, bi_addmm, bi_decode_attention, bi_decode_plan, bi_decode_workspace_bytes, bi_embed,
                bi_log_softmax, bi_mm, bi_qknorm_rope_append, bi_rmsnorm, bi_silu_mul)
 
-__all__ = ["Qwen3Shape", "QWEN3_8B", "Batch", "Decoder"]
+__all__ = ["Qwen3Shape", "QWEN3_8B", "Batch", "Decoder", "GraphStep"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -79,6 +79,32 @@ class Decoder:
         self.v_pages = [torch.empty_like(k) for k in self.k_pages]
         self.device = device
 
+    def _layers(self, x, positions, lens_dev, offs_dev, total, ws, block_table):
+        """The kernels of one step after the embedding; returns (logits, log-probs, greedy tokens)."""
+        s, w = self.s, self.w
+        bsz = x.shape[0]
+        h = bi_rmsnorm(x, w["w_in"][0], s.eps)
+        for l in range(s.layers):
+            qkv = bi_mm(h, w["w_qkv"][l], out_dtype=torch.bfloat16)
+            q = bi_qknorm_rope_append(qkv, w["q_norm"][l], w["k_norm"][l], w["cos"], w["sin"], positions,
+                                      block_table, self.k_pages[l], self.v_pages[l],
+                                      num_q_heads=s.num_q_heads, num_kv_heads=s.num_kv_heads, eps=s.eps)
+            a = bi_decode_attention(q, self.k_pages[l], self.v_pages[l], block_table, lens_dev, offs_dev, total,
+                                    workspace=ws, out_dtype=torch.bfloat16, split_tokens=s.split_tokens)
+            o = bi_mm(a.view(bsz, s.hidden), w["w_o"][l], out_dtype=torch.bfloat16)
+            h = bi_add_rmsnorm(x, o, w["w_post"][l], s.eps)
+            gu = bi_mm(h, w["w_gu"][l], out_dtype=torch.bfloat16)
+            dn = bi_mm(bi_silu_mul(gu), w["w_down"][l], out_dtype=torch.bfloat16)
+            h = bi_add_rmsnorm(x, dn, w["w_in"][l + 1] if l + 1 < s.layers else w["w_final"], s.eps)
+        logits = bi_addmm(w["b_lm"], h, w["w_lm"])
+        logp, nxt = bi_log_softmax(logits)
+        return logits, logp, nxt
+
+    def graph(self, batch: Batch, max_steps: int) -> "GraphStep":
+        """Capture one step of this batch as a HIP graph that can be replayed
+        for up to max_steps successive steps (see GraphStep)."""
+        return GraphStep(self, batch, max_steps)
+
     def step(self, tokens: torch.Tensor, batch: Batch):
         """Run one token per sequence. tokens: device int64 [B]. Appends the
         tokens' k, v to the cache and advances batch.lens. Returns (fp32
@@ -96,20 +122,72 @@ class Decoder:
         ws = torch.empty(bi_decode_workspace_bytes(total, s.num_q_heads, s.head_dim), dtype=torch.uint8, device=dev)
 
         x = bi_embed(w["embed"], tokens)
-        h = bi_rmsnorm(x, w["w_in"][0], s.eps)
-        for l in range(s.layers):
-            qkv = bi_mm(h, w["w_qkv"][l], out_dtype=torch.bfloat16)
-            q = bi_qknorm_rope_append(qkv, w["q_norm"][l], w["k_norm"][l], w["cos"], w["sin"], positions,
-                                      batch.block_table, self.k_pages[l], self.v_pages[l],
-                                      num_q_heads=s.num_q_heads, num_kv_heads=s.num_kv_heads, eps=s.eps)
-            a = bi_decode_attention(q, self.k_pages[l], self.v_pages[l], batch.block_table, lens_dev, offs_dev, total,
-                                    workspace=ws, out_dtype=torch.bfloat16, split_tokens=s.split_tokens)
-            o = bi_mm(a.view(bsz, s.hidden), w["w_o"][l], out_dtype=torch.bfloat16)
-            h = bi_add_rmsnorm(x, o, w["w_post"][l], s.eps)
-            gu = bi_mm(h, w["w_gu"][l], out_dtype=torch.bfloat16)
-            dn = bi_mm(bi_silu_mul(gu), w["w_down"][l], out_dtype=torch.bfloat16)
-            h = bi_add_rmsnorm(x, dn, w["w_in"][l + 1] if l + 1 < s.layers else w["w_final"], s.eps)
-        logits = bi_addmm(w["b_lm"], h, w["w_lm"])
-        logp, nxt = bi_log_softmax(logits)
+        logits, logp, nxt = self._layers(x, positions, lens_dev, offs_dev, total, ws, batch.block_table)
         batch.lens = lens_after
         return logits, logp, nxt
+
+
+class GraphStep:
+    """A decode step of one batch captured once and replayed step after step.
+
+    A step launches ~10 kernels per layer; replaying them as one HIP graph
+    removes the host launch cost between them. What changes from step to
+    step lives in fixed device buffers that the host refreshes before each
+    replay: the tokens (the previous replay writes its greedy tokens there),
+    the positions, the context lengths and the split offsets. The attention
+    launches cover an upper bound of the split count over max_steps steps;
+    workgroups past the current count exit at once, so every replay does the
+    same work as an eager step and gives the same bits.
+    """
+
+    def __init__(self, decoder: Decoder, batch: Batch, max_steps: int):
+        s = decoder.s
+        dev = decoder.device
+        self.dec, self.batch, self.left = decoder, batch, max_steps
+        bsz = batch.block_table.shape[0]
+        if int((batch.lens + max_steps).max()) > batch.block_table.shape[1] * s.page_size:
+            raise ValueError("the block table has no room for max_steps more tokens")
+        lens_max = (batch.lens.to(torch.int64) + max_steps)
+        self.bound = int(((lens_max + s.split_tokens - 1) // s.split_tokens).sum())
+        self.tokens = torch.zeros(bsz, dtype=torch.int64, device=dev)
+        self.positions = torch.zeros(bsz, dtype=torch.int32, device=dev)
+        self.lens_dev = torch.ones(bsz, dtype=torch.int32, device=dev)
+        self.offs_dev = torch.zeros(bsz + 1, dtype=torch.int32, device=dev)
+        self._host = torch.empty(3 * bsz + 1, dtype=torch.int32, pin_memory=True)
+        self.ws = torch.empty(bi_decode_workspace_bytes(self.bound, s.num_q_heads, s.head_dim), dtype=torch.uint8,
+                              device=dev)
+        self._set(batch.lens)  # valid contents for the capture's argument checks
+        torch.cuda.synchronize()
+        self.g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g):
+            x = bi_embed(decoder.w["embed"], self.tokens)
+            self.logits, self.logp, nxt = decoder._layers(x, self.positions, self.lens_dev, self.offs_dev,
+                                                          self.bound, self.ws, batch.block_table)
+            self.tokens.copy_(nxt)
+
+    def _set(self, lens: torch.Tensor):
+        bsz = lens.shape[0]
+        lens_after = lens + 1
+        offs, _ = bi_decode_plan(lens_after, self.dec.s.split_tokens)
+        h = self._host
+        h[:bsz] = lens
+        h[bsz:2 * bsz] = lens_after
+        h[2 * bsz:] = offs
+        self.positions.copy_(h[:bsz], non_blocking=True)
+        self.lens_dev.copy_(h[bsz:2 * bsz], non_blocking=True)
+        self.offs_dev.copy_(h[2 * bsz:], non_blocking=True)
+
+    def run(self, tokens: torch.Tensor | None = None):
+        """One step. tokens (device int64 [B]) for the first step; later steps
+        take the previous step's greedy tokens. Returns the graph's (logits,
+        log-probabilities, tokens) buffers, overwritten by the next replay."""
+        if self.left <= 0:
+            raise RuntimeError("captured for fewer steps: capture again")
+        torch.cuda.current_stream().synchronize()  # the pinned staging buffer is reused
+        if tokens is not None:
+            self.tokens.copy_(tokens)
+        self._set(self.batch.lens)
+        self.g.replay()
+        self.batch.lens = self.batch.lens + 1
+        self.left -= 1
+        return self.logits, self.logp, self.tokens

@@ -267,3 +267,31 @@ def test_per_token_kernels_are_batch_invariant(lib):
             tok = torch.randint(0, 5000, (m,), generator=torch.Generator().manual_seed(m)).to(DEV)
             tok[pos] = 4321
             assert same_bits(lib.bi_embed(table, tok)[pos], e1[0])
+
+
+def test_graph_replay_equals_eager_steps(lib):
+    """The decode step captured once as a HIP graph and replayed step after step (eager host work and
+    a synchronisation between replays) gives every step's logits and tokens the eager step's bits,
+    also across a step where a sequence's split count grows under the same capture."""
+    from invariant_bi_mm_amd.decode import Decoder, Qwen3Shape
+    shape = Qwen3Shape(hidden=1024, num_q_heads=8, num_kv_heads=2, intermediate=3072, vocab=8192, layers=2)
+    w = make_weights(shape, 2, seed=9400, max_pos=1024)
+    lens = [254, 17, 300]  # sequence 0 reaches a second split at its third new token
+    caches = [prompt_cache(shape, 2, L, seed=9410 + 10 * i) for i, L in enumerate(lens)]
+    runs = []
+    for mode in ("eager", "graph"):
+        dec = Decoder(shape, w, num_pages=64)
+        batch = place(dec, caches, lens, room=6, seed=9420)
+        tok = torch.tensor([5, 77, 8000], dtype=torch.int64, device=DEV)
+        outs = []
+        gs = dec.graph(batch, 5) if mode == "graph" else None
+        for i in range(5):
+            if gs is None:
+                logits, _, nxt = dec.step(tok, batch)
+                tok = nxt
+            else:
+                logits, _, nxt = gs.run(tok if i == 0 else None)
+            outs.append((logits.clone(), nxt.clone()))
+        runs.append(outs)
+    for i, ((l0, n0), (l1, n1)) in enumerate(zip(*runs)):
+        assert same_bits(l0, l1) and same_bits(n0, n1), f"step {i}"
