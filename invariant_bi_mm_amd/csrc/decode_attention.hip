@@ -68,35 +68,64 @@ struct SplitArgs {
 // pages, i.e. of tokens j * PAGE + grp, j = 0..PPS-1.
 // ---------------------------------------------------------------------------
 
-// q of the GQA heads h = 0..3 of one query, scaled by scale * log2(e).
-__device__ __forceinline__ void load_q(const uint16_t* q_row, int dl, float qscale, float (&qf)[GQA][8]) {
+// Phase 1: scores S[t][h][key] of the split's SPLIT keys for query rows
+// r = GQA t + h, t < ntok tokens, on the matrix cores:
+//   S = (sum_d q[r][d] k[key][d]) * qscale   (qscale = scale * log2(e)),
+// the sum taken by v_mfma_f32_16x16x32_bf16 over d in four steps of 32
+// (exact bf16 products, fp32 accumulation, increasing d), then one fp32
+// multiply; keys at or past nt_of(t) get -inf. Wave w covers keys
+// [64 w, 64 w + 64) as four 16-key tiles, tile kt being slots 0..15 of page
+// 4 w + kt; its MFMA B operand (lane l: key l % 16, d 8 (l / 16) .. +7 of a
+// 32-wide step) is read straight from the page with 16-byte loads. Query
+// rows go 16 to an MFMA; rows past GQA ntok read zeros and are not stored.
+// The element (r, key) gets the same chain whichever row of the MFMA holds
+// r, so a token's scores do not depend on the other tokens of the block.
+template <int NTOK, typename NtOf>
+__device__ __forceinline__ void split_scores(const uint16_t* q0, int64_t q_tok_stride, int ntok, NtOf nt_of,
+                                             const uint16_t* kp, const int32_t* bt, int64_t page_stride,
+                                             int64_t head_off, int wave, int lane, float qscale,
+                                             float (*S)[GQA][SPLIT]) {
+  constexpr int RB = (NTOK * GQA + 15) / 16;
+  const int nt_max = nt_of(ntok - 1);  // the block's last token sees the most keys
+  const int sl = lane & 15, dq = 8 * (lane >> 4);
+  u32x4 kf[4][4];
 #pragma unroll
-  for (int h = 0; h < GQA; ++h) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(q_row + h * HD + dl * 8);
-    unpack8(v, qf[h]);
+  for (int kt = 0; kt < 4; ++kt) {
+    const int pg = 4 * wave + kt;
+    if (16 * pg < nt_max) {
+      const uint16_t* base = kp + (int64_t)bt[pg] * page_stride + head_off + sl * HD + dq;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qf[h][e] = qf[h][e] * qscale;
-  }
-}
-
-// Phase 1: S[h][i] = log2-domain score of token i of the split for head h,
-// -inf for i >= nt: an 8-term fma chain per lane, then the 16-lane butterfly.
-__device__ __forceinline__ void split_scores(const float (&qf)[GQA][8], const u32x4 (&kv)[PPS], int grp, int dl, int nt,
-                                             float (*S)[SPLIT]) {
+      for (int ds = 0; ds < 4; ++ds) kf[kt][ds] = *reinterpret_cast<const u32x4*>(base + 32 * ds);
+    } else {
 #pragma unroll
-  for (int j = 0; j < PPS; ++j) {
-    const int i = j * PAGE + grp;
-    float kf[8];
-    unpack8(kv[j], kf);
-    float dot[GQA];
-#pragma unroll
-    for (int h = 0; h < GQA; ++h) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(qf[h][e], kf[e], acc);
-      dot[h] = group16_sum(acc);
+      for (int ds = 0; ds < 4; ++ds) kf[kt][ds] = u32x4{0u, 0u, 0u, 0u};
     }
-    if (dl < GQA) S[dl][i] = (i < nt) ? dot[dl] : -INFINITY;
+  }
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = 16 * rb + sl;  // the query row this lane feeds to the MFMA
+    bf16x8 qa[4];
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (r / GQA < ntok)
+        v = *reinterpret_cast<const u32x4*>(q0 + (r / GQA) * q_tok_stride + (r % GQA) * HD + 32 * ds + dq);
+      qa[ds] = __builtin_bit_cast(bf16x8, v);
+    }
+    const int t_out = 4 * rb + (lane >> 4);  // token of the 4 rows this lane receives (GQA == 4)
+    const int nt_t = t_out < ntok ? nt_of(t_out) : 0;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ds], __builtin_bit_cast(bf16x8, kf[kt][ds]), acc, 0, 0, 0);
+      const int key = 64 * wave + 16 * kt + sl;
+      if (t_out < ntok) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[t_out][i][key] = key < nt_t ? acc[i] * qscale : -INFINITY;
+      }
+    }
   }
 }
 
@@ -177,7 +206,7 @@ __device__ __forceinline__ void load_kv(const uint16_t* pages, const int32_t* bt
 }
 
 __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
-  __shared__ float S[GQA][SPLIT];
+  __shared__ float S[1][GQA][SPLIT];
   __shared__ float O[4][GQA][HD];
   __shared__ float ML[GQA][2];
 
@@ -213,29 +242,26 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
   const int nt = min(SPLIT, L - t0);
   const int32_t* bt = a.bt + (int64_t)b * a.max_pages + t0 / PAGE;
 
-  float qf[GQA][8];
-  load_q(a.q + ((int64_t)b * a.hq + g * GQA) * HD, dl, a.qscale, qf);
-
   const int64_t head_stride = (int64_t)PAGE * HD;           // one head-page
   const int64_t page_stride = (int64_t)a.hkv * head_stride;  // one physical page
   const int64_t slot_off = (int64_t)g * head_stride + (int64_t)grp * HD + dl * 8;
 
-  u32x4 kv[PPS];
-  load_kv(a.kp, bt, page_stride, slot_off, grp, nt, kv);
-  split_scores(qf, kv, grp, dl, nt, S);
+  split_scores<1>(a.q + ((int64_t)b * a.hq + g * GQA) * HD, 0, 1, [&](int) { return nt; }, a.kp, bt, page_stride,
+                  (int64_t)g * head_stride, wave, lane, a.qscale, S);
   __syncthreads();
   {
     float mx, l;
-    split_softmax_row(S[wave], lane, mx, l);  // wave h: query head h
+    split_softmax_row(S[0][wave], lane, mx, l);  // wave h: query head h
     if (lane == 0) {
       ML[wave][0] = mx;
       ML[wave][1] = l;
     }
   }
   __syncthreads();
+  u32x4 kv[PPS];
   load_kv(a.vp, bt, page_stride, slot_off, grp, nt, kv);
   float o[GQA][8];
-  split_pv(kv, S, grp, o);
+  split_pv(kv, S[0], grp, o);
   if (lane < 16) {
 #pragma unroll
     for (int h = 0; h < GQA; ++h)
@@ -300,14 +326,9 @@ __global__ __launch_bounds__(256) void prefill_split_kernel(PrefillArgs a) {
   const int64_t page_stride = (int64_t)a.hkv * head_stride;
   const int64_t slot_off = (int64_t)g * head_stride + (int64_t)grp * HD + dl * 8;
 
-  u32x4 kv[PPS];
-  load_kv(a.kp, bt, page_stride, slot_off, grp, nt_max, kv);
-  for (int t = 0; t < nq; ++t) {
-    const int nt = min(SPLIT, a.pos[row0 + t] + 1 - t0);  // <= 0: this row does not see the split
-    float qf[GQA][8];
-    load_q(a.q + ((int64_t)(row0 + t) * a.hq + g * GQA) * HD, dl, a.qscale, qf);
-    split_scores(qf, kv, grp, dl, nt, S[t]);
-  }
+  split_scores<QB>(a.q + ((int64_t)row0 * a.hq + g * GQA) * HD, (int64_t)a.hq * HD, nq,
+                   [&](int t) { return min(SPLIT, a.pos[row0 + t] + 1 - t0); }, a.kp, bt, page_stride,
+                   (int64_t)g * head_stride, wave, lane, a.qscale, S);
   __syncthreads();
   for (int r = wave; r < nq * GQA; r += 4) {
     float mx, l;
@@ -318,6 +339,7 @@ __global__ __launch_bounds__(256) void prefill_split_kernel(PrefillArgs a) {
     }
   }
   __syncthreads();
+  u32x4 kv[PPS];
   load_kv(a.vp, bt, page_stride, slot_off, grp, nt_max, kv);
   for (int t = 0; t < nq; ++t) {
     const int row = row0 + t;
