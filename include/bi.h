@@ -179,11 +179,15 @@ size_t bi_decode_workspace_bytes(int64_t total_splits, int num_q_heads, int head
 
 /* bi_decode_attention
  *   q             bf16 [batch, num_q_heads, head_dim], contiguous.
- *   k_pages,
- *   v_pages       bf16 [num_pages, num_kv_heads, page_size, head_dim],
- *                 contiguous; token t of sequence b is in physical page
- *                 block_table[b * max_pages + t / page_size], slot
- *                 t % page_size.
+ *   k_pages       bf16 [num_pages, num_kv_heads, page_size, head_dim],
+ *                 contiguous (a key is a contiguous row).
+ *   v_pages       bf16 [num_pages, num_kv_heads, head_dim, page_size],
+ *                 contiguous (d-major: one head-dim element of a page's
+ *                 tokens is a contiguous row, so a value tile of 8 tokens
+ *                 is one 16-byte load). Token t of sequence b is in
+ *                 physical page block_table[b * max_pages + t / page_size],
+ *                 slot t % page_size, of both. Slots past a sequence's
+ *                 length may hold any bits (never used).
  *   block_table   int32 [batch, max_pages], contiguous.
  *   context_lens  int32 [batch], each >= 1 and <= max_pages * page_size.
  *   split_offsets int32 [batch + 1] on the DEVICE, as written by
@@ -313,9 +317,10 @@ bi_status bi_silu_mul(const void* gu, int64_t ldg, void* out, int64_t ldo,
  *     out[i + 64] = t[i+64] * cos[p][i] + t[i] * sin[p][i],
  *   rounded once to bf16. q heads go to q_out [batch, num_q_heads, head_dim];
  *   k heads, and v heads unchanged, go to slot p % page_size of page
- *   block_table[b * max_pages + p / page_size] of k_pages / v_pages
- *   ([num_pages, num_kv_heads, page_size, head_dim], the bi_decode_attention
- *   layout). positions[b] is the new token's index, i.e. the sequence's
+ *   block_table[b * max_pages + p / page_size] of k_pages
+ *   ([num_pages, num_kv_heads, page_size, head_dim]) / v_pages
+ *   ([num_pages, num_kv_heads, head_dim, page_size]), the bi_decode_attention
+ *   layouts. positions[b] is the new token's index, i.e. the sequence's
  *   length before this token.
  *   cos_tab, sin_tab  fp32 [max_pos, head_dim / 2]: the caller's table.
  * Supported: head_dim == 128. A position outside [0, max_pos) or outside the

@@ -23,7 +23,7 @@ __all__ = [
     "bi_mm", "bi_addmm", "bi_gemm_config", "bi_rmsnorm", "bi_mean", "bi_log_softmax",
     "bi_decode_plan", "bi_decode_workspace_bytes", "bi_decode_attention",
     "bi_add_rmsnorm", "bi_embed", "bi_silu_mul", "bi_qknorm_rope_append",
-    "bi_prefill_plan", "bi_prefill_attention",
+    "bi_prefill_plan", "bi_prefill_attention", "v_pages_shape",
     "bi_status_string", "bi_last_error_message",
     "BI_BF16", "BI_F32", "STATUS",
 ]
@@ -242,12 +242,21 @@ def bi_decode_workspace_bytes(total_splits: int, num_q_heads: int, head_dim: int
     return int(lib.bi_decode_workspace_bytes(total_splits, num_q_heads, head_dim))
 
 
+def v_pages_shape(k_pages) -> tuple:
+    """Shape of the V page pool that goes with k_pages [P, Hkv, page, D]:
+    [P, Hkv, D, page] (d-major, so a value tile of 8 tokens of one head-dim
+    element is one 16-byte load)."""
+    p, hkv, page, d = k_pages.shape
+    return (p, hkv, d, page)
+
+
 def bi_decode_attention(q, k_pages, v_pages, block_table, context_lens, split_offsets, total_splits: int, *,
                         scale: float | None = None, split_tokens: int = 256, workspace=None, out=None,
                         out_dtype: torch.dtype = torch.float32, stream=None):
     """Split-KV decode attention over a paged cache.
 
-    q [B, Hq, D] bf16; k_pages/v_pages [P, Hkv, page, D] bf16; block_table
+    q [B, Hq, D] bf16; k_pages [P, Hkv, page, D] and v_pages [P, Hkv, D, page]
+    (d-major) bf16; block_table
     [B, max_pages] int32; context_lens [B] int32 and split_offsets [B+1]
     int32 on the device (split_offsets from bi_decode_plan)."""
     _need_bf16(q, "q")
@@ -255,8 +264,8 @@ def bi_decode_attention(q, k_pages, v_pages, block_table, context_lens, split_of
     _need_bf16(v_pages, "v_pages")
     bsz, hq, d = q.shape
     _, hkv, page, d2 = k_pages.shape
-    if d2 != d or v_pages.shape != k_pages.shape:
-        raise ValueError("q/k/v shapes disagree")
+    if d2 != d or v_pages.shape != v_pages_shape(k_pages):
+        raise ValueError("q/k/v shapes disagree (v_pages is [P, Hkv, D, page])")
     for t, nm in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (block_table, "block_table"),
                   (context_lens, "context_lens"), (split_offsets, "split_offsets")):
         if not t.is_contiguous():
@@ -344,8 +353,8 @@ def bi_qknorm_rope_append(qkv, q_norm_w, k_norm_w, cos_tab, sin_tab, positions, 
             raise ValueError(f"{nm} must be contiguous")
     bsz = qkv.shape[0]
     num_pages, hkv, page, d = k_pages.shape
-    if hkv != num_kv_heads or v_pages.shape != k_pages.shape:
-        raise ValueError("cache shape disagrees with num_kv_heads")
+    if hkv != num_kv_heads or v_pages.shape != v_pages_shape(k_pages):
+        raise ValueError("cache shape disagrees with num_kv_heads (k [P, Hkv, page, D], v [P, Hkv, D, page])")
     if q_out is None:
         q_out = torch.empty((bsz, num_q_heads, d), dtype=torch.bfloat16, device=qkv.device)
     qkv, ldq = _mat(qkv, "qkv")
@@ -387,6 +396,8 @@ def bi_prefill_attention(q, k_pages, v_pages, block_table, q_pos, q_offsets, wor
     if nr != rows:
         raise ValueError("q has a different number of rows than the plan")
     _, hkv, page, d2 = k_pages.shape
+    if d2 != d or v_pages.shape != v_pages_shape(k_pages):
+        raise ValueError("q/k/v shapes disagree (v_pages is [P, Hkv, D, page])")
     for t, nm in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (block_table, "block_table"),
                   (q_pos, "q_pos"), (q_offsets, "q_offsets"), (work, "work")):
         if not t.is_contiguous():

@@ -15,18 +15,17 @@
 // (sequence, head) in increasing split order. The position of the sequence in
 // the batch only changes WHICH workgroup does the work.
 //
-// Kernel 1, one workgroup per (split, kv head), 256 threads = 16 groups of 16
-// lanes; lane dl of a group owns head-dim slice [8*dl, 8*dl + 8).
-//   phase 1: group i handles slot i of each of the split's (<= 16) pages: the
-//            16 groups read one 4 KB head-page together. Scores for the GQA
-//            query heads sharing this kv head are 8-term fixed-order dots
-//            plus a 16-lane butterfly, kept in LDS (log2 domain: q is
-//            pre-multiplied by scale * log2(e)).
+// Kernel 1, one workgroup per (split, kv head), 4 waves of 64 lanes; both
+// matrix phases use v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
+//   phase 1: scores of the GQA query heads sharing this kv head against the
+//            split's keys (wave w: keys [64 w, 64 w + 64)), K fragments read
+//            straight from the page; kept in LDS in the log2 domain (raw dot
+//            times scale * log2(e)).
 //   phase 2: wave h (one per query head) takes the exact max over the split,
-//            writes p = 2^(s - max) back and sums it (per-lane fixed order,
-//            then butterfly).
-//   phase 3: o = sum_t p_t v_t with the same token->group assignment, groups
-//            merged by butterfly inside a wave, waves merged in wave order.
+//            forms p = 2^(s - max), sums it, and writes p back as bf16 hi + lo.
+//   phase 3: o = sum_t p_t v_t (wave w: head-dim columns [32 w, 32 w + 32)
+//            over all the split's keys), V fragments read straight from the
+//            d-major page.
 //   output : (max, sum p, o[128]) per (split, query head), fp32.
 // Kernel 2, one workgroup per (sequence, query head):
 //   M = max_s m_s; l = sum_s 2^(m_s - M) l_s; o = sum_s 2^(m_s - M) o_s[d],
@@ -42,7 +41,10 @@ constexpr int HD = 128;     // head dim
 constexpr int PAGE = 16;    // tokens per page
 constexpr int SPLIT = 256;  // tokens per split
 constexpr int GQA = 4;      // query heads per kv head
-constexpr int PPS = SPLIT / PAGE;
+constexpr int SROW = SPLIT + 4;  // LDS row stride (floats) of a score row, padded against bank conflicts
+// Phase 2 rewrites a row of SROW floats as bf16 parts of p: hi at u16
+// [0, SPLIT), lo at u16 [PLO, PLO + SPLIT) (16-byte aligned, inside the row).
+constexpr int PLO = SPLIT;
 constexpr float LOG2E = 1.4426950408889634f;
 
 struct SplitArgs {
@@ -63,55 +65,82 @@ struct SplitArgs {
 // ---------------------------------------------------------------------------
 // The per-(query, split) arithmetic, shared by the decode and the prefill
 // kernels so that a token's partials have the same bits whichever computes
-// them. Thread layout: 256 threads = 16 groups of 16 lanes; lane dl of group
-// grp owns head-dim slice [8 dl, 8 dl + 8) of slot grp of each of the split's
-// pages, i.e. of tokens j * PAGE + grp, j = 0..PPS-1.
+// them. Cache layout per physical page: K [kv head][slot][d] (a key is a
+// contiguous row), V [kv head][d][slot] (a head-dim row of the page's tokens
+// is contiguous), both bf16; PAGE slots per page.
 // ---------------------------------------------------------------------------
+
+// Loads. A split's page numbers are read as wave-uniform (scalar) values;
+// every fragment is loaded, unconditionally, before the first is used, in
+// the order q, K, V, so that the wait for q and K leaves V in flight through
+// phases 1 and 2 (a load under a branch would make the compiler wait for it
+// at the join). npg >= 1 is the number of pages holding the keys the block
+// can see; a tile past it reads the last of them instead (in bounds; its keys
+// are masked where they are used).
+
+// K fragments: wave w covers keys [64 w, 64 w + 64) as four 16-key tiles,
+// tile kt being slots 0..15 of page 4 w + kt. The MFMA B operand of a 32-wide
+// d step (lane l: key l % 16, d 8 (l / 16) .. +7) is one 16-byte load of the
+// key row.
+__device__ __forceinline__ void load_k_frags(const uint16_t* kp, const int32_t* bt, int npg, int64_t page_stride,
+                                             int64_t head_off, int wave, int lane, u32x4 (&kf)[4][4]) {
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    const uint16_t* base = kp + (int64_t)bt[min(4 * wave + kt, npg - 1)] * page_stride + head_off +
+                           (lane & 15) * HD + 8 * (lane >> 4);
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) kf[kt][ds] = *reinterpret_cast<const u32x4*>(base + 32 * ds);
+  }
+}
+
+// q fragments (the MFMA A operand): row block rb holds query rows
+// r = 16 rb + l % 16 (token r / GQA, head r % GQA), d 8 (l / 16) .. +7 of each
+// 32-wide step. Rows of tokens >= ntok repeat token 0 (in bounds; those rows
+// of the products are never stored).
+template <int RB>
+__device__ __forceinline__ void load_q_frags(const uint16_t* q0, int64_t q_tok_stride, int ntok, int lane,
+                                             u32x4 (&qa)[RB][4]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int r = 16 * rb + (lane & 15);
+    const int t = r / GQA < ntok ? r / GQA : 0;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds)
+      qa[rb][ds] = *reinterpret_cast<const u32x4*>(q0 + t * q_tok_stride + (r % GQA) * HD + 32 * ds + 8 * (lane >> 4));
+  }
+}
+
+// V fragments, the B operand of phase 3: V pages are stored d-major
+// ([page][kv head][d][slot]), so for key step ks (keys [32 ks, 32 ks + 32),
+// pages 2 ks and 2 ks + 1) lane l's operand -- column d, keys 8 (l / 16) .. +7
+// -- is one 16-byte load of a d-row of one page. Wave w owns the columns
+// d in [32 w, 32 w + 32), two 16-wide tiles, over all the split's keys.
+__device__ __forceinline__ void load_v_frags(const uint16_t* vp, const int32_t* bt, int npg, int64_t page_stride,
+                                             int64_t head_off, int wave, int lane, u32x4 (&vf)[8][2]) {
+  const int q4 = lane >> 4;
+  const int d = 32 * wave + (lane & 15);
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const int32_t p0 = bt[min(2 * ks, npg - 1)], p1 = bt[min(2 * ks + 1, npg - 1)];
+    const uint16_t* base = vp + (int64_t)((q4 >> 1) ? p1 : p0) * page_stride + head_off + d * PAGE + 8 * (q4 & 1);
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) vf[ks][dt] = *reinterpret_cast<const u32x4*>(base + 16 * dt * PAGE);
+  }
+}
 
 // Phase 1: scores S[t][h][key] of the split's SPLIT keys for query rows
 // r = GQA t + h, t < ntok tokens, on the matrix cores:
 //   S = (sum_d q[r][d] k[key][d]) * qscale   (qscale = scale * log2(e)),
 // the sum taken by v_mfma_f32_16x16x32_bf16 over d in four steps of 32
 // (exact bf16 products, fp32 accumulation, increasing d), then one fp32
-// multiply; keys at or past nt_of(t) get -inf. Wave w covers keys
-// [64 w, 64 w + 64) as four 16-key tiles, tile kt being slots 0..15 of page
-// 4 w + kt; its MFMA B operand (lane l: key l % 16, d 8 (l / 16) .. +7 of a
-// 32-wide step) is read straight from the page with 16-byte loads. Query
-// rows go 16 to an MFMA; rows past GQA ntok read zeros and are not stored.
-// The element (r, key) gets the same chain whichever row of the MFMA holds
-// r, so a token's scores do not depend on the other tokens of the block.
-template <int NTOK, typename NtOf>
-__device__ __forceinline__ void split_scores(const uint16_t* q0, int64_t q_tok_stride, int ntok, NtOf nt_of,
-                                             const uint16_t* kp, const int32_t* bt, int64_t page_stride,
-                                             int64_t head_off, int wave, int lane, float qscale,
-                                             float (*S)[GQA][SPLIT]) {
-  constexpr int RB = (NTOK * GQA + 15) / 16;
-  const int nt_max = nt_of(ntok - 1);  // the block's last token sees the most keys
-  const int sl = lane & 15, dq = 8 * (lane >> 4);
-  u32x4 kf[4][4];
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    const int pg = 4 * wave + kt;
-    if (16 * pg < nt_max) {
-      const uint16_t* base = kp + (int64_t)bt[pg] * page_stride + head_off + sl * HD + dq;
-#pragma unroll
-      for (int ds = 0; ds < 4; ++ds) kf[kt][ds] = *reinterpret_cast<const u32x4*>(base + 32 * ds);
-    } else {
-#pragma unroll
-      for (int ds = 0; ds < 4; ++ds) kf[kt][ds] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
+// multiply; keys at or past nt_of(t) get -inf. Rows past GQA ntok are not
+// stored. The element (r, key) gets the same chain whichever row of the MFMA
+// holds r, so a token's scores do not depend on the other tokens of the block.
+template <int RB, typename NtOf>
+__device__ __forceinline__ void split_scores(const u32x4 (&qa)[RB][4], const u32x4 (&kf)[4][4], int ntok, NtOf nt_of,
+                                             int wave, int lane, float qscale, float (*S)[GQA][SROW]) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const int r = 16 * rb + sl;  // the query row this lane feeds to the MFMA
-    bf16x8 qa[4];
-#pragma unroll
-    for (int ds = 0; ds < 4; ++ds) {
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (r / GQA < ntok)
-        v = *reinterpret_cast<const u32x4*>(q0 + (r / GQA) * q_tok_stride + (r % GQA) * HD + 32 * ds + dq);
-      qa[ds] = __builtin_bit_cast(bf16x8, v);
-    }
     const int t_out = 4 * rb + (lane >> 4);  // token of the 4 rows this lane receives (GQA == 4)
     const int nt_t = t_out < ntok ? nt_of(t_out) : 0;
 #pragma unroll
@@ -119,8 +148,9 @@ __device__ __forceinline__ void split_scores(const uint16_t* q0, int64_t q_tok_s
       f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ds = 0; ds < 4; ++ds)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ds], __builtin_bit_cast(bf16x8, kf[kt][ds]), acc, 0, 0, 0);
-      const int key = 64 * wave + 16 * kt + sl;
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[rb][ds]),
+                                                      __builtin_bit_cast(bf16x8, kf[kt][ds]), acc, 0, 0, 0);
+      const int key = 64 * wave + 16 * kt + (lane & 15);
       if (t_out < ntok) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[t_out][i][key] = key < nt_t ? acc[i] * qscale : -INFINITY;
@@ -129,8 +159,11 @@ __device__ __forceinline__ void split_scores(const uint16_t* q0, int64_t q_tok_s
   }
 }
 
-// Phase 2, one row (query, head) by one wave: exact max, p = 2^(s - max)
-// written back, l = sum p (per-lane order, then the wave butterfly).
+// Phase 2, one row (query, head) by one wave: exact max, p = 2^(s - max),
+// l = sum p in fp32 (per-lane order, then the wave butterfly). p is written
+// back over the row as two bf16 parts, hi = RNE(p) and lo = RNE(p - hi) (the
+// difference is exact in fp32), the A operand of phase 3. The whole row is in
+// registers (mx depends on every element) before the first write.
 __device__ __forceinline__ void split_softmax_row(float* row, int lane, float& mx_out, float& l_out) {
   float v[SPLIT / 64];
   float mx = -INFINITY;
@@ -141,74 +174,67 @@ __device__ __forceinline__ void split_softmax_row(float* row, int lane, float& m
   }
   mx = wave_max(mx);
   float l = 0.0f;
+  uint16_t* pb = reinterpret_cast<uint16_t*>(row);
 #pragma unroll
   for (int r = 0; r < SPLIT / 64; ++r) {
     const float pr = __builtin_amdgcn_exp2f(v[r] - mx);  // 2^-inf = 0 for masked slots
-    row[lane + 64 * r] = pr;
+    const uint32_t hb = f32_to_bf16_rne(pr);
+    pb[lane + 64 * r] = (uint16_t)hb;
+    pb[PLO + lane + 64 * r] = (uint16_t)f32_to_bf16_rne(pr - __uint_as_float(hb << 16));
     l = l + pr;
   }
   mx_out = mx;
   l_out = wave_sum(l);
 }
 
-// Phase 3 for one query: o[h][e] = sum_j p(token j * PAGE + grp) v[e] (fma
-// chain in j), then the 4 groups of a wave merged (xor 16, then xor 32).
-__device__ __forceinline__ void split_pv(const u32x4 (&kv)[PPS], const float (*S)[SPLIT], int grp, float (&o)[GQA][8]) {
+// Phase 3 on the matrix cores: the split's partial output
+//   O[r][d] = sum over its SPLIT keys of p[r][key] v[key][d]
+// for one block of 16 query rows (4 tokens x the GQA heads), by
+// v_mfma_f32_16x16x32_bf16 with A = p and B = v (fragments from
+// load_v_frags). No partial crosses waves: wave w owns columns [32 w, 32 w + 32).
+// p enters as its two bf16 parts hi + lo (written by phase 2), so the
+// products carry ~16 bits of p; the chain per element is: key steps of 32 in
+// increasing order, hi then lo in each, fp32 accumulation. V of keys at or
+// past nt is zeroed here (the cache past a sequence's last token may hold
+// any bits, and 0 * NaN would poison the sum). acc[dt] = the wave's tile dt:
+// lane l holds rows 16 rb + 4 (l / 16) + i (i = 0..3), i.e. token
+// 4 rb + l / 16 and GQA head i, column d = 32 w + 16 dt + l % 16. Rows of
+// tokens >= ntok repeat token 0's p (never stored).
+__device__ __forceinline__ void split_pv(const u32x4 (&vf)[8][2], const float (*S)[GQA][SROW], int rb, int ntok,
+                                         int nt, int lane, f32x4 (&acc)[2]) {
+  const int r = 16 * rb + (lane & 15);  // the query row this lane feeds
+  const int t = r / GQA;
+  const int q4 = lane >> 4;
+  const uint16_t* prow = reinterpret_cast<const uint16_t*>(S[t < ntok ? t : 0][r % GQA]) + 8 * q4;
+  acc[0] = acc[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int h = 0; h < GQA; ++h)
+  for (int ks = 0; ks < 8; ++ks) {
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(prow + 32 * ks);
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(prow + PLO + 32 * ks);
+    const int valid = nt - (32 * ks + 8 * q4);  // keys of this lane's 8 that exist
+    u32x4 keep;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[h][e] = 0.0f;
+    for (int e = 0; e < 4; ++e) keep[e] = (2 * e < valid ? 0xFFFFu : 0u) | (2 * e + 1 < valid ? 0xFFFF0000u : 0u);
 #pragma unroll
-  for (int j = 0; j < PPS; ++j) {
-    const int i = j * PAGE + grp;
-    float vf[8];
-    unpack8(kv[j], vf);
-#pragma unroll
-    for (int h = 0; h < GQA; ++h) {
-      const float pr = S[h][i];  // 0 for masked slots
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] = __builtin_fmaf(pr, vf[e], o[h][e]);
+    for (int dt = 0; dt < 2; ++dt) {
+      const bf16x8 v = __builtin_bit_cast(bf16x8, vf[ks][dt] & keep);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi), v, acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, lo), v, acc[dt], 0, 0, 0);
     }
-  }
-#pragma unroll
-  for (int h = 0; h < GQA; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float t = o[h][e];
-      t = t + xor_shfl(t, 16);
-      t = t + xor_shfl(t, 32);
-      o[h][e] = t;
-    }
-}
-
-// The 4 waves' o merged in wave order, written as the split's partial:
-// thread handles (h, d) pairs tid and tid + 256.
-__device__ __forceinline__ void write_partial(const float (*O)[GQA][HD], int tid, float* ws_o_base) {
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int idx = tid + 256 * r;
-    const int h = idx >> 7, d = idx & (HD - 1);
-    ws_o_base[h * HD + d] = ((O[0][h][d] + O[1][h][d]) + O[2][h][d]) + O[3][h][d];
   }
 }
 
-// K (or V) of the split's tokens this thread owns; slots at or past nt read 0.
-__device__ __forceinline__ void load_kv(const uint16_t* pages, const int32_t* bt, int64_t page_stride, int64_t slot_off,
-                                        int grp, int nt, u32x4 (&kv)[PPS]) {
+// The wave's share of a row block's partials, for the token of this lane's
+// rows: out points at that token's [GQA][HD] fp32 partial (or is null).
+__device__ __forceinline__ void store_pv(const f32x4 (&acc)[2], int wave, int lane, float* out) {
 #pragma unroll
-  for (int j = 0; j < PPS; ++j) {
-    kv[j] = u32x4{0u, 0u, 0u, 0u};
-    if (j * PAGE + grp < nt) {
-      const int64_t page = bt[j];
-      kv[j] = *reinterpret_cast<const u32x4*>(pages + page * page_stride + slot_off);
-    }
-  }
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i * HD + 32 * wave + 16 * dt + (lane & 15)] = acc[dt][i];
 }
 
 __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
-  __shared__ float S[1][GQA][SPLIT];
-  __shared__ float O[4][GQA][HD];
-  __shared__ float ML[GQA][2];
+  __shared__ float S[1][GQA][SROW];
 
   // The kv heads of one split are adjacent in dispatch order, so the 4 KB
   // head slices of a physical page (all heads, 32 KB at 8 heads) are read at
@@ -216,65 +242,65 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
   const int w = blockIdx.x / a.hkv;  // global split index
   const int g = blockIdx.x % a.hkv;  // kv head
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int grp = tid >> 4;  // 0..15
-  const int dl = tid & 15;   // head-dim slice
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // The grid may cover more splits than exist (the host passes an upper
   // bound so one captured launch serves growing lengths): the exact count is
   // split_offsets[batch], and workgroups past it have nothing to do.
-  if (w >= a.offs[a.batch]) return;
+  const int total = a.offs[a.batch];
 
-  // sequence owning split w: the b with offs[b] <= w < offs[b+1]. The
-  // offsets are read with coalesced loads and compared in parallel (one
-  // memory round trip per 256 sequences instead of a dependent binary search).
-  __shared__ int sb;
-  if (tid == 0) sb = 0;
-  __syncthreads();
+  // The sequence owning split w: the one b with offs[b] <= w < offs[b+1]
+  // (lengths are >= 1, so the offsets increase strictly). Every thread reads
+  // its sequences' offsets and length with coalesced loads issued together
+  // with the count above (one memory round trip per 256 sequences), and the
+  // owner passes (b, s, L) through LDS.
+  __shared__ int sinfo[3];
   for (int base = 0; base < a.batch; base += 256) {
     const int t = base + tid;
-    if (t < a.batch && a.offs[t] <= w && w < a.offs[t + 1]) sb = t;
+    if (t < a.batch) {
+      const int o0 = a.offs[t], o1 = a.offs[t + 1], len = a.lens[t];
+      // all three loads in flight together (not sunk into the branches below)
+      asm volatile("" ::"v"(o0), "v"(o1), "v"(len));
+      if (o0 <= w && w < o1) {
+        sinfo[0] = t;
+        sinfo[1] = w - o0;
+        sinfo[2] = len;
+      }
+    }
   }
+  if (w >= total) return;  // uniform over the workgroup
   __syncthreads();
-  const int b = sb;
-  const int s = w - a.offs[b];
-  const int L = a.lens[b];
+  const int b = __builtin_amdgcn_readfirstlane(sinfo[0]);
+  const int s = __builtin_amdgcn_readfirstlane(sinfo[1]);
+  const int L = __builtin_amdgcn_readfirstlane(sinfo[2]);
   const int t0 = s * SPLIT;
   const int nt = min(SPLIT, L - t0);
+  const int npg = (nt + PAGE - 1) / PAGE;
   const int32_t* bt = a.bt + (int64_t)b * a.max_pages + t0 / PAGE;
 
   const int64_t head_stride = (int64_t)PAGE * HD;           // one head-page
   const int64_t page_stride = (int64_t)a.hkv * head_stride;  // one physical page
-  const int64_t slot_off = (int64_t)g * head_stride + (int64_t)grp * HD + dl * 8;
+  const int64_t head_off = (int64_t)g * head_stride;
 
-  split_scores<1>(a.q + ((int64_t)b * a.hq + g * GQA) * HD, 0, 1, [&](int) { return nt; }, a.kp, bt, page_stride,
-                  (int64_t)g * head_stride, wave, lane, a.qscale, S);
+  u32x4 qa[1][4], kf[4][4], vf[8][2];
+  load_q_frags<1>(a.q + ((int64_t)b * a.hq + g * GQA) * HD, 0, 1, lane, qa);
+  load_k_frags(a.kp, bt, npg, page_stride, head_off, wave, lane, kf);
+  load_v_frags(a.vp, bt, npg, page_stride, head_off, wave, lane, vf);
+  __builtin_amdgcn_sched_barrier(0);  // every load issued before the first MFMA waits
+  split_scores<1>(qa, kf, 1, [&](int) { return nt; }, wave, lane, a.qscale, S);
   __syncthreads();
+  const int64_t base = (int64_t)w * a.hq + g * GQA;  // partial row of (split w, query head g GQA)
   {
     float mx, l;
     split_softmax_row(S[0][wave], lane, mx, l);  // wave h: query head h
     if (lane == 0) {
-      ML[wave][0] = mx;
-      ML[wave][1] = l;
+      a.ws_ml[(base + wave) * 2 + 0] = mx;
+      a.ws_ml[(base + wave) * 2 + 1] = l;
     }
   }
   __syncthreads();
-  u32x4 kv[PPS];
-  load_kv(a.vp, bt, page_stride, slot_off, grp, nt, kv);
-  float o[GQA][8];
-  split_pv(kv, S[0], grp, o);
-  if (lane < 16) {
-#pragma unroll
-    for (int h = 0; h < GQA; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) O[wave][h][dl * 8 + e] = o[h][e];
-  }
-  __syncthreads();
-  const int64_t base = (int64_t)w * a.hq + g * GQA;
-  write_partial(O, tid, a.ws_o + base * HD);
-  if (tid < GQA) {
-    a.ws_ml[(base + tid) * 2 + 0] = ML[tid][0];
-    a.ws_ml[(base + tid) * 2 + 1] = ML[tid][1];
-  }
+  f32x4 acc[2];
+  split_pv(vf, S, 0, 1, nt, lane, acc);
+  if (lane < 16) store_pv(acc, wave, lane, a.ws_o + base * HD);  // rows 0..3: the one token
 }
 
 // ---------------------------------------------------------------------------
@@ -288,9 +314,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
 //
 // One workgroup per (work item, kv head); a work item is up to QB
 // consecutive query rows of one sequence and one split they see. The split's
-// K and V are loaded once for all of them (slots past the last row's nt read
-// 0); for an earlier row, the slots it must not see carry p = 0, and
-// fma(0, v, o) = o for finite v, so they add nothing.
+// K and V are loaded once for all of them (keys past the last row's nt read
+// 0); for an earlier row, the keys it must not see carry p = 0, and their
+// products (0 times a finite cached value) add exact zeros.
 // ---------------------------------------------------------------------------
 constexpr int QB = 8;
 
@@ -310,58 +336,52 @@ struct PrefillArgs {
 };
 
 __global__ __launch_bounds__(256) void prefill_split_kernel(PrefillArgs a) {
-  __shared__ float S[QB][GQA][SPLIT];
-  __shared__ float O[4][GQA][HD];
-  __shared__ float ML[QB][GQA][2];
+  __shared__ float S[QB][GQA][SROW];
 
   const int wi = blockIdx.x / a.hkv, g = blockIdx.x % a.hkv;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int grp = tid >> 4, dl = tid & 15;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row0 = a.work[4 * wi], nq = a.work[4 * wi + 1], b = a.work[4 * wi + 2], s = a.work[4 * wi + 3];
   const int t0 = s * SPLIT;
   const int nt_max = min(SPLIT, a.pos[row0 + nq - 1] + 1 - t0);
+  const int npg = (nt_max + PAGE - 1) / PAGE;
   const int32_t* bt = a.bt + (int64_t)b * a.max_pages + t0 / PAGE;
   const int64_t head_stride = (int64_t)PAGE * HD;
   const int64_t page_stride = (int64_t)a.hkv * head_stride;
-  const int64_t slot_off = (int64_t)g * head_stride + (int64_t)grp * HD + dl * 8;
+  const int64_t head_off = (int64_t)g * head_stride;
+  // partial row of (chunk row row0 + t, split s, query head g GQA), or -1
+  // when that row's position is before the split (it does not see it)
+  auto part_row = [&](int t) -> int64_t {
+    const int row = row0 + t;
+    return a.pos[row] + 1 - t0 > 0 ? (int64_t)(a.qoffs[row] + s) * a.hq + g * GQA : -1;
+  };
 
-  split_scores<QB>(a.q + ((int64_t)row0 * a.hq + g * GQA) * HD, (int64_t)a.hq * HD, nq,
-                   [&](int t) { return min(SPLIT, a.pos[row0 + t] + 1 - t0); }, a.kp, bt, page_stride,
-                   (int64_t)g * head_stride, wave, lane, a.qscale, S);
+  constexpr int RB = QB * GQA / 16;
+  u32x4 qa[RB][4], kf[4][4], vf[8][2];
+  load_q_frags<RB>(a.q + ((int64_t)row0 * a.hq + g * GQA) * HD, (int64_t)a.hq * HD, nq, lane, qa);
+  load_k_frags(a.kp, bt, npg, page_stride, head_off, wave, lane, kf);
+  load_v_frags(a.vp, bt, npg, page_stride, head_off, wave, lane, vf);
+  __builtin_amdgcn_sched_barrier(0);  // every load issued before the first MFMA waits
+  split_scores<RB>(qa, kf, nq, [&](int t) { return min(SPLIT, a.pos[row0 + t] + 1 - t0); }, wave, lane, a.qscale, S);
   __syncthreads();
   for (int r = wave; r < nq * GQA; r += 4) {
     float mx, l;
     split_softmax_row(S[r / GQA][r % GQA], lane, mx, l);
-    if (lane == 0) {
-      ML[r / GQA][r % GQA][0] = mx;
-      ML[r / GQA][r % GQA][1] = l;
+    const int64_t base = part_row(r / GQA);
+    if (lane == 0 && base >= 0) {
+      a.ws_ml[(base + r % GQA) * 2 + 0] = mx;
+      a.ws_ml[(base + r % GQA) * 2 + 1] = l;
     }
   }
   __syncthreads();
-  u32x4 kv[PPS];
-  load_kv(a.vp, bt, page_stride, slot_off, grp, nt_max, kv);
-  for (int t = 0; t < nq; ++t) {
-    const int row = row0 + t;
-    const bool sees = a.pos[row] + 1 - t0 > 0;
-    float o[GQA][8];
-    split_pv(kv, S[t], grp, o);
-    if (lane < 16) {
-#pragma unroll
-      for (int h = 0; h < GQA; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) O[wave][h][dl * 8 + e] = o[h][e];
+  for (int rb = 0; rb < (nq * GQA + 15) / 16; ++rb) {
+    f32x4 acc[2];
+    split_pv(vf, S, rb, nq, nt_max, lane, acc);
+    const int t = 4 * rb + (lane >> 4);
+    if (t < nq) {
+      const int64_t base = part_row(t);
+      if (base >= 0) store_pv(acc, wave, lane, a.ws_o + base * HD);
     }
-    __syncthreads();
-    if (sees) {
-      const int64_t base = (int64_t)(a.qoffs[row] + s) * a.hq + g * GQA;
-      write_partial(O, tid, a.ws_o + base * HD);
-      if (tid < GQA) {
-        a.ws_ml[(base + tid) * 2 + 0] = ML[t][tid][0];
-        a.ws_ml[(base + tid) * 2 + 1] = ML[t][tid][1];
-      }
-    }
-    __syncthreads();
   }
 }
 

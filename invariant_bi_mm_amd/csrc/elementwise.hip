@@ -75,7 +75,8 @@ struct RopeArgs {
 //     out[l]      = t[l] cos - t[l+64] sin
 //     out[l + 64] = t[l+64] cos + t[l] sin,   cos/sin = table[pos][l];
 //   q goes to q_out[b, h, :], k to the cache slot of token pos;
-//   v heads are copied to their cache slot unchanged.
+//   v heads are copied unchanged to their slot of the d-major V page
+//   ([page][kv head][d][slot]).
 // A position outside the table or the block table, or a page outside the
 // pool, writes nothing to the cache and zeros to q_out.
 __global__ __launch_bounds__(64) void qknorm_rope_append_kernel(RopeArgs a) {
@@ -92,9 +93,10 @@ __global__ __launch_bounds__(64) void qknorm_rope_append_kernel(RopeArgs a) {
   if (h >= nq + nk) {  // v head: copy
     if (ok) {
       const int g = h - nq - nk;
-      uint16_t* dst = a.vp + ((page * nk + g) * a.page + pos % a.page) * HD;
-      dst[l] = src[l];
-      dst[l + HALF] = src[l + HALF];
+      // V pages are d-major: [page][kv head][d][slot]
+      uint16_t* dst = a.vp + (page * nk + g) * HD * a.page + pos % a.page;
+      dst[(int64_t)l * a.page] = src[l];
+      dst[(int64_t)(l + HALF) * a.page] = src[l + HALF];
     }
     return;
   }

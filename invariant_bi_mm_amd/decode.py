@@ -76,7 +76,9 @@ class Decoder:
         self.s, self.w = s, weights
         self.k_pages = [torch.empty((num_pages, s.num_kv_heads, s.page_size, s.head_dim), dtype=torch.bfloat16,
                                     device=device) for _ in range(s.layers)]
-        self.v_pages = [torch.empty_like(k) for k in self.k_pages]
+        # V pages d-major [P, Hkv, D, page], the layout bi_decode_attention reads
+        self.v_pages = [torch.empty((num_pages, s.num_kv_heads, s.head_dim, s.page_size), dtype=torch.bfloat16,
+                                    device=device) for _ in range(s.layers)]
         self.device = device
 
     def _layers(self, x, positions, lens_dev, offs_dev, total, ws, block_table):

@@ -166,18 +166,20 @@ def argmax(x_f32) -> np.ndarray:
 # --------------------------------------------------------------------------
 # decode attention over a paged KV cache
 # --------------------------------------------------------------------------
-def gather_kv(pages_bits, block_table, seq_len: int, kv_head: int, b: int) -> np.ndarray:
+def gather_kv(pages_bits, block_table, seq_len: int, kv_head: int, b: int, d_major: bool = False) -> np.ndarray:
     """Logical tokens 0..seq_len-1 of sequence ``b``, head ``kv_head``, as a
     [seq_len, D] fp64 array. ``pages_bits`` is [P, Hkv, page_size, D] bf16
-    bits; token t lives in physical page block_table[b, t // page_size] at
-    slot t % page_size."""
-    page_size = pages_bits.shape[2]
-    d = pages_bits.shape[3]
+    bits (the key pages), or [P, Hkv, D, page_size] when ``d_major`` (the
+    value pages); token t lives in physical page block_table[b, t // page_size]
+    at slot t % page_size."""
+    page_size = pages_bits.shape[3 if d_major else 2]
+    d = pages_bits.shape[2 if d_major else 3]
     out = np.empty((seq_len, d), dtype=np.float64)
     for t0 in range(0, seq_len, page_size):
         p = int(block_table[b, t0 // page_size])
         n = min(page_size, seq_len - t0)
-        out[t0:t0 + n] = bf16_bits_to_f64(pages_bits[p, kv_head, :n, :])
+        blk = pages_bits[p, kv_head, :, :n].T if d_major else pages_bits[p, kv_head, :n, :]
+        out[t0:t0 + n] = bf16_bits_to_f64(blk)
     return out
 
 
@@ -199,7 +201,7 @@ def decode_attention(q_bits, k_pages_bits, v_pages_bits, block_table, context_le
         L = int(context_lens[b])
         for g in range(hkv):
             k = gather_kv(k_pages_bits, block_table, L, g, b)
-            v = gather_kv(v_pages_bits, block_table, L, g, b)
+            v = gather_kv(v_pages_bits, block_table, L, g, b, d_major=True)
             for h in range(g * group, (g + 1) * group):
                 s = scale * (k @ q[b, h])
                 p = np.exp(s - s.max())
@@ -221,7 +223,7 @@ def prefill_attention(q_bits, k_pages_bits, v_pages_bits, block_table, q_seq, q_
         b, L = int(q_seq[r]), int(q_pos[r]) + 1
         for g in range(hkv):
             k = gather_kv(k_pages_bits, block_table, L, g, b)
-            v = gather_kv(v_pages_bits, block_table, L, g, b)
+            v = gather_kv(v_pages_bits, block_table, L, g, b, d_major=True)
             for h in range(g * group, (g + 1) * group):
                 sc = scale * (k @ q[r, h])
                 p = np.exp(sc - sc.max())
@@ -258,7 +260,7 @@ def decode_attention_split(q_bits, k_pages_bits, v_pages_bits, block_table, cont
         L = int(context_lens[b])
         for g in range(hkv):
             k = gather_kv(k_pages_bits, block_table, L, g, b)
-            v = gather_kv(v_pages_bits, block_table, L, g, b)
+            v = gather_kv(v_pages_bits, block_table, L, g, b, d_major=True)
             for h in range(g * group, (g + 1) * group):
                 parts = []
                 for t0 in range(0, L, split_tokens):

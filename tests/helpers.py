@@ -49,3 +49,11 @@ def rne_bf16(t: torch.Tensor) -> torch.Tensor:
 
 def count_rows_differing(ref_row: torch.Tensor, rows: list) -> int:
     return sum(0 if same_bits(ref_row, r) else 1 for r in rows)
+
+
+def d_major(v):
+    """Value pages [P, Hkv, page, D] (token-major, as tests write them) in the
+    d-major layout the library and the oracle take: [P, Hkv, D, page]."""
+    if isinstance(v, torch.Tensor):
+        return v.transpose(2, 3).contiguous()
+    return np.ascontiguousarray(np.swapaxes(v, 2, 3))

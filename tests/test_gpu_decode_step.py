@@ -16,7 +16,7 @@ import torch
 
 import oracle as O
 import synthetic as S
-from helpers import ELEM_TOL, assert_close, bits, f32, same_bits
+from helpers import ELEM_TOL, assert_close, bits, d_major, f32, same_bits
 from oracle.decode_step import OracleDecoder
 
 pytestmark = pytest.mark.gpu
@@ -99,7 +99,7 @@ def test_qknorm_rope_append_parity_and_cache_slots(lib):
     qkv, qw, kw, cos, sin, pos, table = _rope_case(b, hq, hkv, 750)
     pos = torch.tensor([0, 17, 63, 40, 5], dtype=torch.int32)  # within 4 pages of 16
     kp = torch.full((64, hkv, page, 128), 7.0, dtype=torch.bfloat16, device=DEV)  # sentinel
-    vp = kp.clone()
+    vp = torch.full((64, hkv, 128, page), 7.0, dtype=torch.bfloat16, device=DEV)  # d-major
     q = lib.bi_qknorm_rope_append(qkv, qw, kw, cos.to(DEV), sin.to(DEV), pos.to(DEV), table.to(DEV), kp, vp,
                                   num_q_heads=hq, num_kv_heads=hkv, eps=1e-6)
     rq, rk, rv = O.qknorm_rope(bits(qkv), bits(qw), bits(kw), 1e-6, cos.numpy(), sin.numpy(), pos.numpy(), hq, hkv)
@@ -109,13 +109,13 @@ def test_qknorm_rope_append_parity_and_cache_slots(lib):
         p, s = int(table[i, pos[i] // page]), int(pos[i] % page)
         touched[p, s] = True
         close_bf16(kp[p, :, s], rk[i], f"k of token {i}")
-        assert same_bits(vp[p, :, s], qkv[i, (hq + hkv) * 128:].view(hkv, 128))
+        assert same_bits(vp[p, :, :, s], qkv[i, (hq + hkv) * 128:].view(hkv, 128))
     sentinel = torch.full((hkv, 128), 7.0, dtype=torch.bfloat16)
     kc, vc = kp.cpu(), vp.cpu()
     for p in range(64):
         for s in range(page):
             if not touched[p, s]:
-                assert same_bits(kc[p, :, s], sentinel) and same_bits(vc[p, :, s], sentinel)
+                assert same_bits(kc[p, :, s], sentinel) and same_bits(vc[p, :, :, s], sentinel)
 
 
 def test_qknorm_rope_append_rejects_bad_positions_without_writing(lib):
@@ -124,7 +124,7 @@ def test_qknorm_rope_append_rejects_bad_positions_without_writing(lib):
     table = torch.tensor([[0, 1], [2, 3], [4, 99]], dtype=torch.int32)  # page 99 is outside the pool of 8
     pos = torch.tensor([100, -1, 20], dtype=torch.int32)  # past the table; negative; page 99
     kp = torch.full((8, hkv, page, 128), 3.0, dtype=torch.bfloat16, device=DEV)
-    vp = kp.clone()
+    vp = torch.full((8, hkv, 128, page), 3.0, dtype=torch.bfloat16, device=DEV)
     q = lib.bi_qknorm_rope_append(qkv, qw, kw, cos.to(DEV), sin.to(DEV), pos.to(DEV), table.to(DEV), kp, vp,
                                   num_q_heads=hq, num_kv_heads=hkv)
     assert not q.any()
@@ -165,7 +165,7 @@ def place(decoder, caches, lens, room, seed):
         pg, sl = table[b, t // ps].long().to(DEV), (t % ps).to(DEV)
         for l, (k, v) in enumerate(cache):
             decoder.k_pages[l][pg, :, sl] = k
-            decoder.v_pages[l][pg, :, sl] = v
+            decoder.v_pages[l][pg, :, :, sl] = v  # d-major pages
     return Batch(block_table=table.to(DEV), lens=torch.tensor(lens, dtype=torch.int32))
 
 

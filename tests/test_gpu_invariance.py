@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import synthetic as S
-from helpers import digest, same_bits
+from helpers import d_major, digest, same_bits
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -223,7 +223,7 @@ def test_decode_batch_composition_invariant(lib):
         q = S.normal_bf16((len(lens), hq, d), 1.0, seed=seed + 3)
         q[pos] = qx
         offs, total = lib.bi_decode_plan(lens_t)
-        out = lib.bi_decode_attention(q.to(DEV), kp.to(DEV), vp.to(DEV), table.to(DEV), lens_t.to(DEV),
+        out = lib.bi_decode_attention(q.to(DEV), kp.to(DEV), d_major(vp).to(DEV), table.to(DEV), lens_t.to(DEV),
                                       offs.to(DEV), total)
         return out[pos].cpu()
 
@@ -240,7 +240,7 @@ def test_decode_repeat_100(lib):
     table, npages = S.paged_kv_layout(lens_t, 16, seed=301)
     q = S.normal_bf16((32, 32, 128), 1.0, seed=302, device=DEV)
     kp = S.normal_bf16((npages, 8, 16, 128), 1.0, seed=303, device=DEV)
-    vp = S.normal_bf16((npages, 8, 16, 128), 1.0, seed=304, device=DEV)
+    vp = d_major(S.normal_bf16((npages, 8, 16, 128), 1.0, seed=304, device=DEV))
     offs, total = lib.bi_decode_plan(lens_t)
     args = (q, kp, vp, table.to(DEV), lens_t.to(DEV), offs.to(DEV), total)
     first = lib.bi_decode_attention(*args)

@@ -20,7 +20,7 @@ import torch
 
 import oracle as O
 import synthetic as S
-from helpers import assert_close, bits, f32, rne_bf16, same_bits
+from helpers import assert_close, bits, d_major, f32, rne_bf16, same_bits
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -257,7 +257,7 @@ def make_decode(lens, seed, hkv=8, hq=32, d=128, page=16):
     table, npages = S.paged_kv_layout(lens_t, page, seed=seed)
     q = S.normal_bf16((len(lens), hq, d), 1.0, seed=seed + 1)
     kp = S.normal_bf16((npages, hkv, page, d), 1.0, seed=seed + 2)
-    vp = S.normal_bf16((npages, hkv, page, d), 1.0, seed=seed + 3)
+    vp = d_major(S.normal_bf16((npages, hkv, page, d), 1.0, seed=seed + 3))
     return lens_t, table, q, kp, vp
 
 
@@ -284,7 +284,7 @@ def test_decode_attention_single_token_is_v0(lib):
     out = run_decode(lib, lens_t, table, q, kp, vp)
     for b in range(3):
         for h in range(32):
-            v0 = vp[table[b, 0], h // 4, 0].float()
+            v0 = vp[table[b, 0], h // 4, :, 0].float()
             assert same_bits(out[b, h].cpu(), v0)
 
 
@@ -295,7 +295,7 @@ def test_decode_attention_config_batch(lib):
     table, npages = S.paged_kv_layout(lens_t, 16, seed=121)
     q = S.normal_bf16((64, 32, 128), 1.0, seed=122, device=DEV)
     kp = S.normal_bf16((npages, 8, 16, 128), 1.0, seed=123, device=DEV)
-    vp = S.normal_bf16((npages, 8, 16, 128), 1.0, seed=124, device=DEV)
+    vp = d_major(S.normal_bf16((npages, 8, 16, 128), 1.0, seed=124, device=DEV))
     offs, total = lib.bi_decode_plan(lens_t)
     out = lib.bi_decode_attention(q, kp, vp, table.to(DEV), lens_t.to(DEV), offs.to(DEV), total)
     seqs = [0, 1, int(torch.argmax(lens_t)), int(torch.argmin(lens_t)), 63]

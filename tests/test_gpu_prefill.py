@@ -15,7 +15,7 @@ import torch
 
 import oracle as O
 import synthetic as S
-from helpers import assert_close, bits, f32, same_bits
+from helpers import assert_close, bits, d_major, f32, same_bits
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -31,7 +31,7 @@ def cache_for(total_lens, seed):
     lens = torch.tensor(total_lens, dtype=torch.int32)
     table, npages = S.paged_kv_layout(lens, PAGE, seed=seed)
     kp = S.normal_bf16((npages, HKV, PAGE, D), 1.0, seed=seed + 1, device=DEV)
-    vp = S.normal_bf16((npages, HKV, PAGE, D), 1.0, seed=seed + 2, device=DEV)
+    vp = d_major(S.normal_bf16((npages, HKV, PAGE, D), 1.0, seed=seed + 2, device=DEV))
     return table, kp, vp
 
 

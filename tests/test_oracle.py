@@ -15,6 +15,7 @@ import numpy as np
 import pytest
 
 import oracle as O
+from helpers import d_major
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -245,7 +246,7 @@ def test_attention_single_token_returns_v0():
     hq, hkv, d, page = 8, 2, 16, 4
     K, V, table = paged(rng, [1, 1], hkv, d, page)
     q = rand_bf16(rng, (2, hq, d))
-    out = O.decode_attention(q, K, V, table, [1, 1], scale=0.25)
+    out = O.decode_attention(q, K, d_major(V), table, [1, 1], scale=0.25)
     for b in range(2):
         for h in range(hq):
             v0 = O.bf16_bits_to_f64(V[table[b, 0], h // (hq // hkv), 0])
@@ -257,7 +258,7 @@ def test_attention_zero_query_is_mean_of_v():
     hq, hkv, d, page, L = 4, 2, 8, 4, 11
     K, V, table = paged(rng, [L], hkv, d, page)
     q = bits(np.zeros((1, hq, d)))
-    out = O.decode_attention(q, K, V, table, [L], scale=1.0)
+    out = O.decode_attention(q, K, d_major(V), table, [L], scale=1.0)
     for h in range(hq):
         g = h // 2
         v = np.stack([O.bf16_bits_to_f64(V[table[0, t // page], g, t % page]) for t in range(L)])
@@ -271,7 +272,7 @@ def test_attention_brute_force_tiny():
     K, V, table = paged(rng, lens, hkv, d, page)
     q = rand_bf16(rng, (4, hq, d))
     scale = 1 / math.sqrt(d)
-    out = O.decode_attention(q, K, V, table, lens, scale)
+    out = O.decode_attention(q, K, d_major(V), table, lens, scale)
     qq = O.bf16_bits_to_f64(q)
     for b, L in enumerate(lens):
         for h in range(hq):
@@ -298,7 +299,7 @@ def test_attention_two_token_closed_form_pins_scale():
     q = np.zeros((1, hq, d))
     q[0, 0, 0] = 3.0
     scale = 0.125
-    out = O.decode_attention(bits(q), bits(K), bits(V), np.zeros((1, 1), np.int32), [2], scale)
+    out = O.decode_attention(bits(q), bits(K), d_major(bits(V)), np.zeros((1, 1), np.int32), [2], scale)
     e = math.exp(6 * scale)
     expect = (np.array([1, 2, 3, 4]) + e * np.array([-1, 0, 0.5, 8])) / (1 + e)
     assert np.allclose(out[0, 0], expect, rtol=1e-15, atol=1e-15)
@@ -323,7 +324,7 @@ def test_attention_gqa_head_map_and_page_gather():
     K[perm[tstar // page], :, tstar % page, 0] = 64.0
     q = np.zeros((1, hq, d))
     q[0, :, 0] = 64.0
-    out = O.decode_attention(bits(q), bits(K), bits(V), table, [L], scale=1.0)
+    out = O.decode_attention(bits(q), bits(K), d_major(bits(V)), table, [L], scale=1.0)
     for h in range(hq):
         assert np.allclose(out[0, h], tstar + 64 * (h // 2), rtol=0, atol=1e-9)
 
@@ -334,9 +335,9 @@ def test_attention_split_form_equals_single_pass():
     lens = [1, 255, 256, 257, 700, 1024]
     K, V, table = paged(rng, lens, hkv, d, page)
     q = rand_bf16(rng, (len(lens), hq, d))
-    a = O.decode_attention(q, K, V, table, lens, 1 / math.sqrt(d))
+    a = O.decode_attention(q, K, d_major(V), table, lens, 1 / math.sqrt(d))
     for split in (16, 256):
-        b = O.decode_attention_split(q, K, V, table, lens, 1 / math.sqrt(d), split)
+        b = O.decode_attention_split(q, K, d_major(V), table, lens, 1 / math.sqrt(d), split)
         assert O.relative_frobenius(b, a) < 1e-13
         assert np.max(np.abs(b - a)) < 1e-13
 
@@ -396,7 +397,7 @@ def test_pins_catch_planted_mistakes():
         for b in range(q.shape[0]):
             for h in range(q.shape[1]):
                 k = O.gather_kv(Kp, table, lens[b], h % hkv, b)
-                v = O.gather_kv(Vp, table, lens[b], h % hkv, b)
+                v = O.gather_kv(Vp, table, lens[b], h % hkv, b, d_major=True)
                 s = scale * (k @ q[b, h])
                 p = np.exp(s - s.max())
                 out[b, h] = p @ v / p.sum()
@@ -408,6 +409,6 @@ def test_pins_catch_planted_mistakes():
         V[:, g] = 64 * g
     q = np.zeros((1, hq, dd))
     table = np.array([[0, 1]], np.int32)
-    good = O.decode_attention(bits(q), bits(K), bits(V), table, [L], 1.0)
-    bad = attn_wrong_group(bits(q), bits(K), bits(V), table, [L], 1.0)
+    good = O.decode_attention(bits(q), bits(K), d_major(bits(V)), table, [L], 1.0)
+    bad = attn_wrong_group(bits(q), bits(K), d_major(bits(V)), table, [L], 1.0)
     assert np.allclose(good[0, 1], 0.0) and not np.allclose(bad[0, 1], 0.0)

@@ -13,6 +13,7 @@ import numpy as np
 
 import oracle as O
 from oracle.decode_step import OracleDecoder
+from helpers import d_major
 
 
 def bits(x):
@@ -211,13 +212,13 @@ def test_prefill_first_token_sees_only_itself_and_rows_equal_decode():
     kp, vp, table = _paged(rng, [40, 300])
     q_seq, q_pos = [0, 0, 0, 1, 1], [0, 17, 39, 255, 299]
     q = rand_bf16(rng, (5, 4, 128))
-    out = O.prefill_attention(q, kp, vp, table, q_seq, q_pos, 128 ** -0.5)
+    out = O.prefill_attention(q, kp, d_major(vp), table, q_seq, q_pos, 128 ** -0.5)
     v0 = O.bf16_bits_to_f64(vp[table[0, 0], 0, 0])
     for h in range(4):
         assert np.array_equal(out[0, h], v0)  # softmax over one token is exactly 1
     # each row is the decode attention of its sequence truncated to p + 1 tokens
     for r in range(5):
-        one = O.decode_attention(q[r:r + 1], kp, vp, table[q_seq[r]:q_seq[r] + 1], [q_pos[r] + 1], 128 ** -0.5)
+        one = O.decode_attention(q[r:r + 1], kp, d_major(vp), table[q_seq[r]:q_seq[r] + 1], [q_pos[r] + 1], 128 ** -0.5)
         assert np.allclose(out[r], one[0], rtol=1e-13, atol=1e-13)
 
 
@@ -226,7 +227,7 @@ def test_prefill_brute_force_causal_mask():
     rng = np.random.default_rng(7)
     kp, vp, table = _paged(rng, [2])
     q = rand_bf16(rng, (2, 4, 128))
-    out = O.prefill_attention(q, kp, vp, table, [0, 0], [0, 1], 0.125)
+    out = O.prefill_attention(q, kp, d_major(vp), table, [0, 0], [0, 1], 0.125)
     K = O.bf16_bits_to_f64(kp[table[0, 0], 0, :2])
     V = O.bf16_bits_to_f64(vp[table[0, 0], 0, :2])
     qq = O.bf16_bits_to_f64(q)
