@@ -78,13 +78,16 @@ typedef enum { BI_BF16 = 0, BI_F32 = 1 } bi_dtype;
  *           weight layout) and C = A @ B^T.
  *   c       [m, n], row stride ldc, dtype c_dtype (BI_F32 or BI_BF16).
  * Reduction order: for every C element, k runs in increasing order in
- * 16-wide MFMA steps, accumulated in fp32, one chain per element; no split-K,
- * stream-K or atomics. The tile configuration is chosen from (n, k, b_is_nk)
- * only, never from m (bi_gemm_config reports it).
- * Requirements: k % 8 == 0; with b_is_nk == 0 also n % 8 == 0; one tile's
- * rows of A (tile_m * lda * 2 bytes) and of B (tile_n * ldb * 2 bytes when
- * b_is_nk, else tile_k * ldb * 2) below 2^31 bytes (BI_ERR_UNSUPPORTED
- * otherwise). k == 0 with m, n > 0: C = beta * bias (addmm) or zeros (mm).
+ * 16-wide MFMA steps (v_mfma_f32_32x32x16_bf16, k padded with zeros to a
+ * multiple of 64), accumulated in fp32 from 0, one chain per element; no
+ * split-K, stream-K or atomics. The tile configuration depends on
+ * (m, n, k, b_is_nk) (bi_gemm_config reports it), but every configuration
+ * runs that same chain with the same operands, so a row of C has the same
+ * bits whatever m is and wherever the row sits.
+ * Requirements: k % 8 == 0; with b_is_nk == 0 also n % 8 == 0;
+ * 256 * lda * 2 and (b_is_nk ? 256 : 64) * ldb * 2 below 2^31 bytes (the
+ * largest tile's byte range; BI_ERR_UNSUPPORTED otherwise).
+ * k == 0 with m, n > 0: C = beta * bias (addmm) or zeros (mm).
  * ------------------------------------------------------------------------ */
 bi_status bi_mm(const void* a, int64_t lda, const void* b, int64_t ldb, int b_is_nk,
                 void* c, int64_t ldc, bi_dtype c_dtype,
@@ -103,11 +106,13 @@ bi_status bi_addmm(const void* bias, bi_dtype bias_dtype, float beta, float alph
                    void* c, int64_t ldc, bi_dtype c_dtype,
                    int64_t m, int64_t n, int64_t k, hipStream_t stream);
 
-/* Tile configuration the GEMM uses for (n, k, b_is_nk): writes
- * {tile_m, tile_n, tile_k, waves_per_workgroup} to out4. It takes no m: the
- * configuration cannot depend on the batch size. Returns BI_ERR_NULL if
- * out4 is NULL, BI_ERR_SHAPE for negative sizes. */
-bi_status bi_gemm_config(int64_t n, int64_t k, int b_is_nk, int32_t* out4);
+/* Tile configuration the GEMM uses for (m, n, k, b_is_nk): writes
+ * {tile_m, tile_n, tile_k, waves_per_workgroup} to out4. One of
+ * {32, 32, 64, 3} and {64, 32, 64, 4} (small m: 32-column strips, a deep
+ * load ring), {128, 128, 64, 4}, {256, 256, 64, 8}. The choice changes which
+ * workgroup computes an element, never how (see bi_mm). Returns BI_ERR_NULL
+ * if out4 is NULL, BI_ERR_SHAPE for negative sizes. */
+bi_status bi_gemm_config(int64_t m, int64_t n, int64_t k, int b_is_nk, int32_t* out4);
 
 /* ------------------------------------------------------------------------
  * bi_rmsnorm: y[i,j] = (x[i,j] * r_i) * w[j], r_i = 1 / sqrt(ss_i / n + eps),

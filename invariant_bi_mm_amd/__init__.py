@@ -46,7 +46,7 @@ lib.bi_mm.argtypes = [_vp, _i64, _vp, _i64, _i32, _vp, _i64, _i32, _i64, _i64, _
 lib.bi_mm.restype = _st
 lib.bi_addmm.argtypes = [_vp, _i32, _f32, _f32, _vp, _i64, _vp, _i64, _i32, _vp, _i64, _i32, _i64, _i64, _i64, _vp]
 lib.bi_addmm.restype = _st
-lib.bi_gemm_config.argtypes = [_i64, _i64, _i32, ctypes.POINTER(ctypes.c_int32)]
+lib.bi_gemm_config.argtypes = [_i64, _i64, _i64, _i32, ctypes.POINTER(ctypes.c_int32)]
 lib.bi_gemm_config.restype = _st
 lib.bi_rmsnorm.argtypes = [_vp, _i64, _vp, _f32, _vp, _i64, _i32, _i64, _i64, _vp]
 lib.bi_rmsnorm.restype = _st
@@ -177,10 +177,11 @@ def bi_addmm(bias: torch.Tensor, a: torch.Tensor, b: torch.Tensor, out: torch.Te
     return out
 
 
-def bi_gemm_config(n: int, k: int, b_is_nk: bool = False) -> tuple:
-    """(tile_m, tile_n, tile_k, waves) the GEMM uses for (n, k, layout); m is not an input."""
+def bi_gemm_config(m: int, n: int, k: int, b_is_nk: bool = False) -> tuple:
+    """(tile_m, tile_n, tile_k, waves) the GEMM uses for (m, n, k, layout). Every
+    configuration gives each output element the same bits."""
     out = (ctypes.c_int32 * 4)()
-    _check(lib.bi_gemm_config(n, k, int(b_is_nk), out))
+    _check(lib.bi_gemm_config(m, n, k, int(b_is_nk), out))
     return tuple(out)
 
 

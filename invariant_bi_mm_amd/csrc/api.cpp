@@ -57,13 +57,16 @@ bi_status check_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, int
   if (k > 0 && (!aligned(a, 16) || !aligned(b, 16) || lda % 8 != 0 || ldb % 8 != 0))
     return fail(BI_ERR_ALIGN, "a/b must be 16-byte aligned with lda, ldb multiples of 8");
   if (!aligned(c, dsize(c_dtype))) return fail(BI_ERR_ALIGN, "c is not aligned to its element size");
-  const bi::GemmConfig cfg = bi::gemm_config(n, k, b_is_nk != 0);
+  const bi::GemmConfig cfg = bi::gemm_config(m, n, k, b_is_nk != 0);
   const int64_t tiles = ((m + cfg.tile_m - 1) / cfg.tile_m) * ((n + cfg.tile_n - 1) / cfg.tile_n);
   if (tiles > INT_MAX) return fail(BI_ERR_UNSUPPORTED, "too many output tiles");
   // the kernels address one tile's rows of A and B through 32-bit buffer
-  // descriptors: a tile's byte extent must stay below 2^31
+  // descriptors: a tile's byte extent must stay below 2^31. Checked for the
+  // largest tile of any configuration (256 rows of A; 256 rows of B stored
+  // [n, k], 64 k-rows stored [k, n]), so whether a call is accepted does not
+  // depend on m.
   const int64_t lim = int64_t(1) << 31;
-  if (2 * cfg.tile_m * lda >= lim || 2 * (b_is_nk ? cfg.tile_n : cfg.tile_k) * ldb >= lim)
+  if (2 * 256 * lda >= lim || 2 * (b_is_nk ? 256 : 64) * ldb >= lim)
     return fail(BI_ERR_UNSUPPORTED, "leading dimension too large for one tile's 32-bit byte range");
   return BI_OK;
 }
@@ -114,10 +117,10 @@ bi_status bi_addmm(const void* bias, bi_dtype bias_dtype, float beta, float alph
   return run_gemm(bias, bias_dtype, beta, alpha, a, lda, b, ldb, b_is_nk, c, ldc, c_dtype, m, n, k, stream);
 }
 
-bi_status bi_gemm_config(int64_t n, int64_t k, int b_is_nk, int32_t* out4) {
+bi_status bi_gemm_config(int64_t m, int64_t n, int64_t k, int b_is_nk, int32_t* out4) {
   if (out4 == nullptr) return fail(BI_ERR_NULL, "out4 is NULL");
-  if (n < 0 || k < 0) return fail(BI_ERR_SHAPE, "negative size");
-  const bi::GemmConfig c = bi::gemm_config(n, k, b_is_nk != 0);
+  if (m < 0 || n < 0 || k < 0) return fail(BI_ERR_SHAPE, "negative size");
+  const bi::GemmConfig c = bi::gemm_config(m, n, k, b_is_nk != 0);
   out4[0] = c.tile_m;
   out4[1] = c.tile_n;
   out4[2] = c.tile_k;

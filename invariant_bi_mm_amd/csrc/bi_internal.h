@@ -14,7 +14,7 @@ struct GemmConfig {
 };
 
 // Tile configuration for (n, k, layout): a pure function of those three.
-GemmConfig gemm_config(int64_t n, int64_t k, bool b_is_nk);
+GemmConfig gemm_config(int64_t m, int64_t n, int64_t k, bool b_is_nk);
 
 struct GemmParams {
   const void* a;

@@ -19,6 +19,10 @@
 //   partial -- runs the same instruction stream. There is no split-K,
 //   stream-K or atomic anywhere.
 //
+// Which tile configuration runs is chosen from (M, N, K) -- a skinny kernel
+// for small M (below), 128x128 or 256x256 otherwise -- and, because every
+// configuration runs the chain above, that choice never changes a bit.
+//
 // Structure (one workgroup per TM x TN output tile)
 //   * global -> LDS directly (buffer_load ... lds, 16 bytes per lane): no
 //     register staging and no LDS write instructions. Rows past M or N and k
@@ -344,6 +348,268 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Skinny tiles for small M. With few rows, a 128-column tile gives only
+// N / 128 workgroups, and each walks its k loop one memory round trip per k
+// tile. Here a workgroup owns TM = 32 C rows (C consumer waves, one 32x32
+// output block each) by 32 columns, so N / 32 workgroups stream the weights,
+// and P producer waves move its k tiles through an NS-stage LDS ring, up to
+// NS - 2 tiles ahead of the MFMAs. The per-element chain is the one of
+// gemm_kernel: one v_mfma_f32_32x32x16_bf16 per 16 k, increasing k, fp32
+// accumulator starting at 0, the same operand elements in the same lanes,
+// k padded with zeros to a multiple of 64, the same epilogue -- so every
+// output element has the bits the large tiles give it, and choosing this
+// kernel by M keeps the result independent of M.
+//
+// The ring's loads are written as inline assembly (buffer_load_dwordx4 ...
+// lds, LDS address in M0, restored afterwards): the compiler then does not
+// see them write LDS and does not make every LDS read wait for every load in
+// flight. The kernel orders them itself: before a tile is read, each
+// producer waits until only the later tiles' loads are outstanding and a
+// barrier publishes all parts; a stage is refilled only after the barrier
+// that follows the MFMAs that consumed it; all loads have landed before the
+// producers end. The instruction writes no register.
+// ---------------------------------------------------------------------------
+
+// s_waitcnt immediate waiting for vmcnt <= vm only (expcnt and lgkmcnt at
+// their maxima).
+constexpr int waitcnt_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Buffer descriptor words from workgroup-uniform values (base, stride 0,
+// byte count, format word as in make_rsrc).
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b),
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) & 0xffffu,
+               (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
+}
+
+// Load with the k offset in the instruction's scalar offset (soffset): the
+// per-lane offset stays fixed over the k loop.
+__device__ __forceinline__ void ring_load16_k(const u32x4& rsrc, uint32_t lds_byte, uint32_t voff, uint32_t soff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_byte), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
+
+template <int C, int P, int NS, bool B_NK>
+__global__ __launch_bounds__((C + P) * 64) void gemm_skinny_kernel(GemmArgs g) {
+  // C consumer waves (one 32x32 output block each: TM = 32 C rows by TN = 32
+  // columns) and P producer waves that only move k tiles into the ring.
+  constexpr int TM = 32 * C, TN = 32;
+  // One stage: A as TM rows of 64 k (eight 16-byte chunks, swizzled by swz),
+  // then B: [N,K] as 32 rows of 64 k (swizzled likewise), or [K,N] as 64 k
+  // rows of 32 columns (four chunks, stored as they are).
+  constexpr int A_CH = TM * 8, B_CH = TN * 8;
+  constexpr int ST = A_CH + B_CH;                          // chunks per stage
+  constexpr int A_I = A_CH / 64 / P, B_I = B_CH / 64 / P;  // 1 KB loads per producer per k tile
+  constexpr int LPT = A_I + B_I;
+  static_assert(A_I * 64 * P == A_CH && B_I * 64 * P == B_CH, "tile not evenly split across producers");
+  static_assert(NS >= 4 && NS % 2 == 0 && (NS - 2) * LPT < 64, "ring depth");
+  static_assert(NS * ST * 16 <= 160 * 1024, "ring larger than LDS");
+  __shared__ u32x4 ring[NS * ST];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int tm, tn;
+  tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+  const int m0 = tm * TM, n0 = tn * TN;
+  const int M = g.m, N = g.n, K = g.k;
+  const int nk = (K + TK - 1) / TK;
+
+  // One barrier per k tile in both roles (plus one before the loop). At the
+  // barrier of iteration t the producers' loads of tile t + 1 have landed
+  // (each producer first waits until only the NS - 3 tiles after it are
+  // outstanding), and the consumers have fed every fragment of tile t - 1 to
+  // the MFMAs, so its stage may be refilled. No memory fence (it would wait
+  // for every load in flight); the signal fences keep the compiler from
+  // moving memory operations across.
+  auto bar = [&]() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+
+  if (wave >= C) {
+    // ---------------- producer ----------------
+    const int pw = wave - C;
+    const int nk_full = K / TK;  // tiles with no k past K
+    const uint32_t lda2 = (uint32_t)g.lda * 2u, ldb2 = (uint32_t)g.ldb * 2u;
+    const uint32_t ring_base = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(const void*)ring);
+    // Rows of A past M (and of B past N, [N,K]) lie past their descriptor.
+    const u32x4 a_rsrc = rsrc_words(g.a + (int64_t)m0 * g.lda, (uint32_t)min(TM, M - m0) * lda2);
+    u32x4 bnk_rsrc{};
+    if constexpr (B_NK) bnk_rsrc = rsrc_words(g.b + (int64_t)n0 * g.ldb, (uint32_t)min(TN, N - n0) * ldb2);
+    // Per-lane source of the chunk each lane writes, fixed over the k loop:
+    // producer pw's load i writes chunks (i P + pw) 64 + lane of A (of B).
+    uint32_t a_off[A_I], b_off[B_I];
+    int a_k[A_I], b_k[B_I];  // k of the chunk within the tile (for the tail tile)
+#pragma unroll
+    for (int i = 0; i < A_I; ++i) {
+      const int p = (i * P + pw) * 64 + lane;
+      const int row = p >> 3, ch = (p & 7) ^ ((row ^ (row >> 3)) & 7);
+      a_off[i] = (uint32_t)row * lda2 + (uint32_t)ch * 16u;
+      a_k[i] = ch * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < B_I; ++i) {
+      const int p = (i * P + pw) * 64 + lane;
+      if constexpr (B_NK) {
+        const int row = p >> 3, ch = (p & 7) ^ ((row ^ (row >> 3)) & 7);
+        b_off[i] = (uint32_t)row * ldb2 + (uint32_t)ch * 16u;
+        b_k[i] = ch * 8;
+      } else {
+        // [K,N]: k row p / 4 of the tile, columns n0 + 8 (p % 4) ..; columns
+        // past N read zeros
+        const int row = p >> 2, ch = p & 3;
+        b_off[i] = (n0 + ch * 8 < N) ? (uint32_t)row * ldb2 + (uint32_t)ch * 16u : OOB;
+        b_k[i] = row;
+      }
+    }
+    // k tile t into stage j. Full tiles put k0 in the scalar offset; the tail
+    // tile (and tiles past K, which read zeros) checks every chunk.
+    auto load = [&](int t, int j) {
+      const int k0 = t * TK;
+      const uint32_t sa = ring_base + (uint32_t)(j * ST + pw * 64) * 16u;
+      const uint32_t sb = sa + (uint32_t)A_CH * 16u;
+      if (t < nk_full) {
+#pragma unroll
+        for (int i = 0; i < A_I; ++i)
+          ring_load16_k(a_rsrc, sa + (uint32_t)(i * P * 64) * 16u, a_off[i], (uint32_t)k0 * 2u);
+        if constexpr (B_NK) {
+#pragma unroll
+          for (int i = 0; i < B_I; ++i)
+            ring_load16_k(bnk_rsrc, sb + (uint32_t)(i * P * 64) * 16u, b_off[i], (uint32_t)k0 * 2u);
+        } else {
+          const u32x4 r = rsrc_words(g.b + ((int64_t)k0 * g.ldb + n0), (uint32_t)TK * ldb2);
+#pragma unroll
+          for (int i = 0; i < B_I; ++i) ring_load16_k(r, sb + (uint32_t)(i * P * 64) * 16u, b_off[i], 0u);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < A_I; ++i)
+          ring_load16_k(a_rsrc, sa + (uint32_t)(i * P * 64) * 16u,
+                        (k0 + a_k[i] < K) ? a_off[i] + (uint32_t)k0 * 2u : OOB, 0u);
+        if constexpr (B_NK) {
+#pragma unroll
+          for (int i = 0; i < B_I; ++i)
+            ring_load16_k(bnk_rsrc, sb + (uint32_t)(i * P * 64) * 16u,
+                          (k0 + b_k[i] < K) ? b_off[i] + (uint32_t)k0 * 2u : OOB, 0u);
+        } else {
+          const u32x4 r =
+              rsrc_words(g.b + ((int64_t)min(k0, K) * g.ldb + n0), (uint32_t)max(0, min(TK, K - k0)) * ldb2);
+#pragma unroll
+          for (int i = 0; i < B_I; ++i) ring_load16_k(r, sb + (uint32_t)(i * P * 64) * 16u, b_off[i], 0u);
+        }
+      }
+    };
+    static_for<0, NS - 1>([&](auto J) { load(decltype(J)::value, decltype(J)::value); });
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * LPT));  // tile 0
+    bar();
+    auto iter = [&](auto J, int t) {
+      constexpr int j = decltype(J)::value;
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 3) * LPT));  // tile t + 1
+      bar();
+      load(t + NS - 1, (j + NS - 1) % NS);  // into the stage of tile t - 1
+    };
+    int t = 0;
+    for (; t + NS <= nk; t += NS) static_for<0, NS>([&](auto J) { iter(J, t + decltype(J)::value); });
+    static_for<0, NS - 1>([&](auto J) {
+      if (t + decltype(J)::value < nk) iter(J, t + decltype(J)::value);
+    });
+    __builtin_amdgcn_s_waitcnt(0);  // no load may still write LDS when the workgroup ends
+    return;
+  }
+
+  // ---------------- consumer ----------------
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  const int arow = 32 * wave + (lane & 31);
+  const int khalf = lane >> 5;
+  const int tr_g = lane >> 4, tr_l = lane & 15;
+  const int tr_row = 8 * (tr_g >> 1) + (tr_l >> 2);
+  const int tr_e = tr_row * TN + (2 * (tr_g & 1) + ((tr_l & 3) >> 1)) * 8 + 4 * (tr_l & 1);
+  // the four k steps' fragments of the tile in stage j
+  auto read = [&](int j, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
+    const u32x4* as = ring + j * ST;
+    const u32x4* bs = as + A_CH;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      af[kk] = __builtin_bit_cast(bf16x8, as[swz(arow, kk * 2 + khalf)]);
+      if constexpr (B_NK) {
+        bfr[kk] = __builtin_bit_cast(bf16x8, bs[swz(lane & 31, kk * 2 + khalf)]);
+      } else {
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const __attribute__((address_space(3))) short* bl =
+            (const __attribute__((address_space(3))) short*)(const void*)bs;
+        const int e = kk * 16 * TN + tr_e;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(bl + e));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(bl + e + 4 * TN));
+        bfr[kk] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
+  };
+  auto mma = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4]) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], bfr[kk], acc, 0, 0, 0);
+  };
+  // Software pipeline: the fragments of tile t + 1 are read while the MFMAs
+  // of tile t run (fragment buffers indexed by stage parity; NS is even).
+  bf16x8 fa[2][4], fb[2][4];
+  bar();
+  read(0, fa[0], fb[0]);
+  auto iter = [&](auto J, int t) {
+    constexpr int j = decltype(J)::value;
+    bar();
+    read((j + 1) % NS, fa[(j + 1) & 1], fb[(j + 1) & 1]);  // tile t + 1 (zeros past K)
+    mma(fa[j & 1], fb[j & 1]);
+  };
+  int t = 0;
+  for (; t + NS <= nk; t += NS) static_for<0, NS>([&](auto J) { iter(J, t + decltype(J)::value); });
+  static_for<0, NS - 1>([&](auto J) {
+    if (t + decltype(J)::value < nk) iter(J, t + decltype(J)::value);
+  });
+
+  // Epilogue (as in gemm_kernel): lane holds C[8 (r / 4) + 4 (lane / 32) +
+  // r % 4][lane % 32] of its 32x32 block, r = 0..15.
+  const int gn = n0 + (lane & 31);
+  if (m0 + 32 * wave >= M || gn >= N) return;
+  float bterm = 0.0f;
+  if (g.bias_mode == 1) {
+    bterm = g.beta * __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(g.bias)[gn]) << 16);
+  } else if (g.bias_mode == 2) {
+    bterm = g.beta * reinterpret_cast<const float*>(g.bias)[gn];
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int gm = m0 + 32 * wave + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    if (gm >= M) continue;
+    float v = g.alpha * acc[r];
+    if (g.bias_mode != 0) v = v + bterm;
+    const int64_t off = (int64_t)gm * g.ldc + gn;
+    if (g.out_bf16)
+      reinterpret_cast<uint16_t*>(g.c)[off] = (uint16_t)f32_to_bf16_rne(v);
+    else
+      reinterpret_cast<float*>(g.c)[off] = v;
+  }
+}
+
+template <int C, int P, int NS, bool B_NK>
+hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
+  const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+  hipLaunchKernelGGL((gemm_skinny_kernel<C, P, NS, B_NK>), dim3((unsigned)tiles), dim3((C + P) * 64), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int TM, int TN, int WM, int WN, bool B_NK>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
@@ -353,28 +619,45 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// The configuration table. It is keyed by (n, k, layout) only; m is not an
-// input, so no batch size can select a different tile or instruction. (Every
-// configuration also runs the same per-element chain -- one 32x32x16 MFMA
-// per 16 k, in increasing k -- so the choice moves work between workgroups
-// without changing any output bit.)
-//
-// Choice, measured on MI355X for the Qwen3-8B projection shapes: a 256x256
-// tile with 8 waves (each 128x64) is fastest at M >= 512 but gives only
-// ceil(M/256) * ceil(N/256) workgroups, so for N <= 6144 it leaves most of
-// the 256 CUs idle at M = 512; there, and for the wide LM head where small M
-// dominates, the 128x128 tile (4 waves, 64x64 each, two workgroups per CU)
-// wins on the geometric mean over M = 512 and 4096. Wide-N GEMMs with
-// moderate K (gate+up, N = 24576) have enough 256-wide column tiles at every
-// M >= 512 and take the big tile.
-GemmConfig gemm_config(int64_t n, int64_t k, bool b_is_nk) {
+// Skinny: one consumer wave (32 rows) when the 32-row strips fit in one
+// round over the CUs, else two (64 rows); two producer waves either way.
+static GemmConfig skinny_config(int64_t m, int64_t strips) {
+  if (m <= 32 || ((m + 31) / 32) * strips <= 256) return GemmConfig{32, 32, TK, 3};
+  return GemmConfig{64, 32, TK, 4};
+}
+
+// The configuration table. Every configuration -- skinny, 128x128, 256x256
+// -- computes each output element with the same chain (one 32x32x16 MFMA per
+// 16 k, increasing k, fp32, k padded to a multiple of 64, the same
+// epilogue), so the choice moves work between workgroups without changing
+// any bit, and it may depend on M: the result of a row still does not depend
+// on how many rows there are. (The batch-dependent selection the pages warn
+// about changes the reduction -- split-K, a different instruction -- and
+// nothing here does.) Measured on MI355X for the Qwen3-8B projection shapes:
+//   * skinny (32 or 64 rows x 32 columns, deep ring) while M is small and
+//     its N / 32 column strips fill the chip at most about twice: 2.5-3.6x
+//     faster than 128x128 at M <= 64 (N = 4096, 6144, K = 4096 and 12288),
+//     1.25-1.6x at N = 24576; at the 151936-wide LM head both stream at
+//     ~5.4 TB/s and 128x128 is kept;
+//   * 256x256 (8 waves, 128x64 each) once its tiles fill the chip (M >= 192,
+//     at least 192 tiles, rounds of 256 at least 70 % full on average):
+//     1.25-1.3x faster than 128x128 at M = 4096 (N = 4096, LM head), 1.1x
+//     for the LM head at M = 256, and for the wide N of gate+up at all M;
+//   * 128x128 (4 waves, two workgroups per CU) in between.
+GemmConfig gemm_config(int64_t m, int64_t n, int64_t k, bool b_is_nk) {
   (void)b_is_nk;
+  const int64_t strips = (n + 31) / 32;
+  if (m <= 64 && n <= 32768) return skinny_config(m, strips);
+  if (m <= 256 && ((m + 63) / 64) * strips <= 512) return skinny_config(m, strips);
+  const int64_t t256 = ((m + 255) / 256) * ((n + 255) / 256);
+  const int64_t rounds = (t256 + 255) / 256;  // one 256x256 workgroup per CU
+  if (m >= 192 && t256 >= 192 && 10 * t256 >= 7 * rounds * 256) return GemmConfig{256, 256, TK, 8};
   if (n >= 16384 && n <= 65536 && k <= 8192) return GemmConfig{256, 256, TK, 8};
-  return GemmConfig{128, 128, TK, 4};  // @@TABLE@@
+  return GemmConfig{128, 128, TK, 4};
 }
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
-  const GemmConfig cfg = gemm_config(p.n, p.k, p.b_is_nk);
+  const GemmConfig cfg = gemm_config(p.m, p.n, p.k, p.b_is_nk);
   GemmArgs a;
   a.a = static_cast<const uint16_t*>(p.a);
   a.b = static_cast<const uint16_t*>(p.b);
@@ -392,6 +675,13 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   a.bias_mode = p.bias == nullptr ? 0 : (p.bias_bf16 ? 1 : 2);
   a.tiles_m = (int)((p.m + cfg.tile_m - 1) / cfg.tile_m);
   a.tiles_n = (int)((p.n + cfg.tile_n - 1) / cfg.tile_n);
+  if (cfg.tile_n == 32) {  // skinny: 16-stage ring with one consumer, 12 with two
+    if (cfg.tile_m == 32)
+      return p.b_is_nk ? launch_skinny<1, 2, 16, true>(a, s) : launch_skinny<1, 2, 16, false>(a, s);
+    if (cfg.tile_m == 64)
+      return p.b_is_nk ? launch_skinny<2, 2, 12, true>(a, s) : launch_skinny<2, 2, 12, false>(a, s);
+    return hipErrorInvalidConfiguration;
+  }
 #define BI_GEMM_CASE(TM_, TN_, WM_, WN_)                                                          \
   if (cfg.tile_m == TM_ && cfg.tile_n == TN_ && cfg.waves == WM_ * WN_)                            \
     return p.b_is_nk ? launch_cfg<TM_, TN_, WM_, WN_, true>(a, s) : launch_cfg<TM_, TN_, WM_, WN_, false>(a, s);

@@ -241,16 +241,25 @@ def test_plan_split_count_depends_on_length_only(bi):
     assert (offs2[1:] - offs2[:-1]).tolist() == counts[::-1]
 
 
-def test_gemm_config_has_no_m_and_is_stable(bi):
+def test_gemm_config_table(bi):
+    """The configuration is a pure function of (m, n, k, layout) from a small
+    set; every member computes each element with the same chain (the GPU
+    tests compare rows across the Ms that select different members)."""
+    seen = set()
     for n, k in [(512, 512), (6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288), (151936, 4096)]:
-        for nk in (False, True):
-            cfg = bi.bi_gemm_config(n, k, nk)
-            assert cfg == bi.bi_gemm_config(n, k, nk)
-            tm, tn, tk, waves = cfg
-            assert tm % 32 == 0 and tn % 32 == 0 and tk == 64 and waves in (4, 8)
+        for m in (1, 31, 32, 33, 64, 65, 256, 512, 2048, 4096):
+            for nk in (False, True):
+                cfg = bi.bi_gemm_config(m, n, k, nk)
+                assert cfg == bi.bi_gemm_config(m, n, k, nk)
+                assert cfg in {(32, 32, 64, 3), (64, 32, 64, 4), (128, 128, 64, 4), (256, 256, 64, 8)}, cfg
+                seen.add(cfg)
+    assert len(seen) == 4
+    # small batches of the projection shapes take the skinny tiles, M = 4096 a full-width one
+    assert bi.bi_gemm_config(1, 4096, 4096)[1] == 32 and bi.bi_gemm_config(64, 4096, 12288)[1] == 32
+    assert bi.bi_gemm_config(4096, 4096, 4096)[1] == 256 and bi.bi_gemm_config(1, 151936, 4096)[1] == 128
     with pytest.raises(bi.BiError):
-        bi.bi_gemm_config(-1, 4, False)
-    assert bi.lib.bi_gemm_config(4, 4, 0, None) == NULL
+        bi.bi_gemm_config(-1, 4, 4, False)
+    assert bi.lib.bi_gemm_config(1, 4, 4, 0, None) == NULL
 
 
 def test_binding_rejects_bad_python_args(bi):

@@ -80,21 +80,28 @@ def test_mm_smoke_every_m_up_to_4096(lib):
 
 def test_mm_smoke_every_position_in_tile(lib):
     """The fixed row at every position 0..TM-1 of a tile (and in the next
-    tile): MFMA lane placement must not change its bits."""
-    tm = lib.bi_gemm_config(512, 512)[0]
+    tiles), for each tile configuration the shape takes: MFMA lane placement
+    must not change its bits."""
     w = S.normal_bf16((512, 512), 1 / 512, seed=2, device=DEV)
     row = S.normal_bf16((1, 512), 1.0, seed=1, device=DEV)[0]
     ref = lib.bi_mm(row[None], w)[0].clone()
-    m = 2 * tm + 3
-    base = S.normal_bf16((m, 512), 1.0, seed=4, device=DEV)
+    cfgs = {}
+    for m in range(1, 600):
+        cfgs.setdefault(lib.bi_gemm_config(m, 512, 512), m)
+    assert len(cfgs) >= 2, cfgs
     bad = []
-    for pos in range(m):
-        x = base.clone()
-        x[pos] = row
-        c = lib.bi_mm(x, w)
-        if not same_bits(c[pos], ref):
-            bad.append(pos)
-    assert not bad, f"row changed at positions {bad[:20]}"
+    for cfg in cfgs:
+        tm = cfg[0]
+        m = next(mm for mm in range(2 * tm + 3, 0, -1) if lib.bi_gemm_config(mm, 512, 512) == cfg)
+        say(f"every position: config {cfg}, m={m}")
+        base = S.normal_bf16((m, 512), 1.0, seed=4, device=DEV)
+        for pos in range(m):
+            x = base.clone()
+            x[pos] = row
+            c = lib.bi_mm(x, w)
+            if not same_bits(c[pos], ref):
+                bad.append((cfg, m, pos))
+    assert not bad, f"row changed at {bad[:20]}"
 
 
 @pytest.mark.parametrize("fill", ["zeros", "huge", "nan"])
@@ -114,10 +121,18 @@ QWEN = [(4096, 6144), (4096, 4096), (4096, 24576), (12288, 4096)]
 @pytest.mark.parametrize("k,n", QWEN)
 def test_mm_qwen_shapes_invariant(lib, k, n):
     """Qwen3-8B projection shapes: config Ms, tile boundaries, random Ms."""
-    tm = lib.bi_gemm_config(n, k)[0]
     rng = np.random.default_rng(k + n)
-    ms = sorted({1, 2, 8, 64, 512, 4096, tm - 1, tm, tm + 1, 2 * tm + 1,
-                 *rng.integers(2, 4097, size=4).tolist()})
+    ms = {1, 2, 8, 64, 65, 256, 257, 512, 4096, *rng.integers(2, 4097, size=4).tolist()}
+    # the tile boundaries of every configuration the shape takes, and the Ms where the configuration changes
+    prev = None
+    for m in range(1, 4097):
+        cfg = lib.bi_gemm_config(m, n, k)
+        if cfg != prev:
+            ms |= {m - 1, m}
+            prev = cfg
+    for tm in {lib.bi_gemm_config(m, n, k)[0] for m in (1, 64, 512, 4096)}:
+        ms |= {tm - 1, tm, tm + 1, 2 * tm + 1}
+    ms = sorted(x for x in ms if 1 <= x <= 4096)
     say(f"qwen invariance k={k} n={n} ms={ms}")
     bad = gemm_sweep(lib, k, n, ms)
     assert not bad, bad
