@@ -1,9 +1,9 @@
 """Batch invariance, bit for bit, through the C ABI.
 
-The property ("their numerical output for a given sequence depends on the
-total batch size" is what the pages call the defect; readhandoff.com,
-agent-run reproducibility pinning, "What does temperature zero actually
-guarantee?") is checked directly by memcmp, with no oracle: a fixed row
+The property -- the defect the pages describe is a kernel whose result for
+one sequence changes with the size of the batch it is computed in
+(readhandoff.com, agent-run reproducibility pinning, "What does temperature
+zero actually guarantee?") -- is checked directly by memcmp, with no oracle: a fixed row
 computed alone (M = 1) must have the same bytes inside every batch size, at
 every position, whatever the other rows hold (random, zeros, huge, NaN/Inf),
 and on every repeated run. A negative control runs the same harness on
@@ -13,8 +13,9 @@ import numpy as np
 import pytest
 import torch
 
+import oracle as O
 import synthetic as S
-from helpers import d_major, digest, same_bits
+from helpers import assert_close, bits, d_major, digest, f32, same_bits
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -113,6 +114,36 @@ def test_mm_adversarial_other_rows(lib, fill):
         for pos in (0, m - 1):
             x = with_row(m, 512, row, pos, seed=0, fill=fill)
             assert same_bits(lib.bi_mm(x, w)[pos], ref), (fill, m, pos)
+
+
+@pytest.mark.parametrize("b_is_nk", [False, True])
+def test_mm_every_tile_configuration_same_bits(lib, b_is_nk):
+    """A row's addmm output is the same, bit for bit, at an M of each tile
+    configuration the shape takes (skinny 32 and 64 rows, 128x128,
+    256x256), at the first and last row, for fp32 and bf16 outputs and
+    a ragged K (a 64-tail) -- and it matches the oracle."""
+    k, n = 1032, 4096
+    first = {}
+    for m in range(1, 4097):
+        first.setdefault(lib.bi_gemm_config(m, n, k, b_is_nk), m)
+    say(f"configs for k={k} n={n} nk={b_is_nk}: {first}")
+    assert len(first) == 4, first
+    w = S.normal_bf16((n, k) if b_is_nk else (k, n), 1 / k, seed=71, device=DEV)
+    bias = S.normal_bf16((n,), 0.1, seed=72, device=DEV)
+    row = S.normal_bf16((1, k), 1.0, seed=73, device=DEV)[0]
+    for od in (torch.float32, torch.bfloat16):
+        ref = lib.bi_addmm(bias, row[None], w, b_is_nk=b_is_nk, out_dtype=od, beta=0.5, alpha=1.5)[0].clone()
+        if od == torch.float32:
+            want = 0.5 * O.bf16_bits_to_f64(bits(bias)) + 1.5 * O.mm(bits(row[None]), bits(w), b_is_nk=b_is_nk)[0]
+            assert_close(f32(ref[None]), want[None], "addmm row vs oracle")
+        for cfg, m0 in first.items():
+            for m in sorted({m0, m0 + 1, m0 + cfg[0] + 3}):
+                if lib.bi_gemm_config(m, n, k, b_is_nk) != cfg:
+                    continue
+                for pos in (0, m - 1):
+                    x = with_row(m, k, row, pos, seed=900 + m)
+                    c = lib.bi_addmm(bias, x, w, b_is_nk=b_is_nk, out_dtype=od, beta=0.5, alpha=1.5)
+                    assert same_bits(c[pos], ref), (cfg, m, pos, od)
 
 
 QWEN = [(4096, 6144), (4096, 4096), (4096, 24576), (12288, 4096)]
