@@ -209,7 +209,10 @@ __global__ __launch_bounds__(64) void mean_kernel(const void* __restrict__ x, in
 // order and keeps a running (max, sum of exp(x - max)) pair, rescaled when
 // the max grows, plus the (value, lowest index) of its largest element.
 // The pairs are merged by a wave butterfly and then across waves in wave
-// order. Pass 2 re-reads the row and writes (x - max) - log(sum).
+// order. Pass 2 writes (x - max) - log(sum). Between the passes a thread
+// keeps its first LS_REG chunks in registers and the next LS_KEEP in LDS
+// (25 of the 38 chunks per thread of a 151936-wide row), so pass 2 re-reads
+// only the rest of the row from memory.
 // ---------------------------------------------------------------------------
 constexpr int LS_NT = 1024;
 constexpr float LOG2E = 1.4426950408889634f;
@@ -234,19 +237,22 @@ __device__ __forceinline__ AM am_merge(AM a, AM b) {
   return take_b ? b : a;
 }
 
-// At most one workgroup per CU: the workgroup reserves more than half of the
-// 160 KB LDS, so 256 rows (~155 MB at n = 151936) are in flight at a time and
-// stay inside the 256 MB Infinity Cache; pass 2's re-read of a row is then
-// served from there instead of HBM.
-constexpr int LS_LDS_FLOATS = 22 * 1024;
+// One workgroup per CU (its LDS holds LS_KEEP chunks per thread), so 256
+// rows (~155 MB at n = 151936) are in flight at a time and stay inside the
+// 256 MB Infinity Cache, which serves pass 2's re-read of the part of a row
+// not kept on chip.
+constexpr int LS_REG = 16;   // chunks per thread kept in registers between the passes
+constexpr int LS_KEEP = 9;   // ... and in LDS
+
 __global__ __launch_bounds__(LS_NT) void log_softmax_kernel(const float* __restrict__ x, int64_t ldx,
                                                              float* __restrict__ y, int64_t ldy,
                                                              int64_t* __restrict__ amax, int n) {
-  __shared__ float lds[LS_LDS_FLOATS];  // only the first 4 * 16 words are used (see above)
-  float* sm_m = lds;
-  float* sm_s = lds + LS_NT / 64;
-  float* sm_v = lds + 2 * (LS_NT / 64);
-  int* sm_i = reinterpret_cast<int*>(lds + 3 * (LS_NT / 64));
+  __shared__ f32x4 keep[LS_KEEP][LS_NT];
+  __shared__ float red[4 * (LS_NT / 64)];
+  float* sm_m = red;
+  float* sm_s = red + LS_NT / 64;
+  float* sm_v = red + 2 * (LS_NT / 64);
+  int* sm_i = reinterpret_cast<int*>(red + 3 * (LS_NT / 64));
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -281,17 +287,49 @@ __global__ __launch_bounds__(LS_NT) void log_softmax_kernel(const float* __restr
     fold(v.w, j0 + 3);
   };
 
-  // eight 16-byte loads in flight per thread, folded in increasing chunk order
-  constexpr int U = 8;
-  int c = tid;
+  // The first LS_REG chunks of this thread, all loads in flight together,
+  // folded in increasing chunk order and kept in registers for pass 2.
+  const f32x4* xv = reinterpret_cast<const f32x4*>(xr);
+  f32x4 r[LS_REG];
+#pragma unroll
+  for (int u = 0; u < LS_REG; ++u) {
+    const int cc = tid + u * LS_NT;
+    r[u] = cc < nch ? xv[cc] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+#pragma unroll
+  for (int u = 0; u < LS_REG; ++u)
+    if (tid + u * LS_NT < nch) fold4(r[u], 4 * (tid + u * LS_NT));
+  // the next LS_KEEP chunks, kept in LDS (each thread its own column),
+  // three loads in flight at a time
+  static_assert(LS_KEEP % 3 == 0, "LDS chunks go in groups of three");
+#pragma unroll
+  for (int u0 = 0; u0 < LS_KEEP; u0 += 3) {
+    f32x4 v[3];
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const int cc = tid + (LS_REG + u0 + u) * LS_NT;
+      v[u] = cc < nch ? xv[cc] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      const int cc = tid + (LS_REG + u0 + u) * LS_NT;
+      if (cc < nch) {
+        keep[u0 + u][tid] = v[u];
+        fold4(v[u], 4 * cc);
+      }
+    }
+  }
+  // the rest of the row, four 16-byte loads in flight per thread
+  constexpr int U = 4;
+  int c = tid + (LS_REG + LS_KEEP) * LS_NT;
   for (; c + (U - 1) * LS_NT < nch; c += U * LS_NT) {
     f32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = reinterpret_cast<const f32x4*>(xr)[c + u * LS_NT];
+    for (int u = 0; u < U; ++u) v[u] = xv[c + u * LS_NT];
 #pragma unroll
     for (int u = 0; u < U; ++u) fold4(v[u], 4 * (c + u * LS_NT));
   }
-  for (; c < nch; c += LS_NT) fold4(reinterpret_cast<const f32x4*>(xr)[c], 4 * c);
+  for (; c < nch; c += LS_NT) fold4(xv[c], 4 * c);
   if (tid < tail) {
     const float v = xr[nch * 4 + tid];
     if (v > m) {
@@ -330,15 +368,21 @@ __global__ __launch_bounds__(LS_NT) void log_softmax_kernel(const float* __restr
   auto out4 = [&](int cc, const f32x4 v) {
     reinterpret_cast<f32x4*>(yr)[cc] = f32x4{(v.x - mx) - lg, (v.y - mx) - lg, (v.z - mx) - lg, (v.w - mx) - lg};
   };
+#pragma unroll
+  for (int u = 0; u < LS_REG; ++u)
+    if (tid + u * LS_NT < nch) out4(tid + u * LS_NT, r[u]);
+#pragma unroll
+  for (int u = 0; u < LS_KEEP; ++u)
+    if (tid + (LS_REG + u) * LS_NT < nch) out4(tid + (LS_REG + u) * LS_NT, keep[u][tid]);
   constexpr int U2 = 4;
-  for (c = tid; c + (U2 - 1) * LS_NT < nch; c += U2 * LS_NT) {
+  for (c = tid + (LS_REG + LS_KEEP) * LS_NT; c + (U2 - 1) * LS_NT < nch; c += U2 * LS_NT) {
     f32x4 v[U2];
 #pragma unroll
-    for (int u = 0; u < U2; ++u) v[u] = reinterpret_cast<const f32x4*>(xr)[c + u * LS_NT];
+    for (int u = 0; u < U2; ++u) v[u] = xv[c + u * LS_NT];
 #pragma unroll
     for (int u = 0; u < U2; ++u) out4(c + u * LS_NT, v[u]);
   }
-  for (; c < nch; c += LS_NT) out4(c, reinterpret_cast<const f32x4*>(xr)[c]);
+  for (; c < nch; c += LS_NT) out4(c, xv[c]);
   if (tid < tail) yr[nch * 4 + tid] = (xr[nch * 4 + tid] - mx) - lg;
 }
 
