@@ -186,10 +186,29 @@ def time_step(torch, ops, steps, warmup):
             e1.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps * 1e3
-    per = {}
+    per, dist = {}, {}
     for i, (name, *_) in enumerate(ops):
-        per[name] = sum(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(steps)) / steps
+        xs = sorted(evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(steps))
+        per[name] = sum(xs) / steps
+        dist[name] = {"median": round(xs[len(xs) // 2], 4), "min": round(xs[0], 4),
+                      "p90": round(xs[min(len(xs) - 1, int(0.9 * len(xs)))], 4)}
+    time_step.last_dist = dist
     return wall, per
+
+
+def gpu_clocks():
+    """Shader and memory clocks as rocm-smi reports them (None where it is not available)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout)
+    except Exception:
+        return None
+    out = {}
+    for card, v in d.items():
+        if isinstance(v, dict):
+            out[card] = {k: v[k] for k in v if "sclk" in k.lower() or "mclk" in k.lower()}
+    return out or None
 
 
 def cpu_baseline(wl, S):
@@ -496,7 +515,10 @@ def main():
         return
     wl = Workload(torch, S, bi, dev)
     ops = wl.ops()
+    clocks_before = gpu_clocks()
     ms_step, per = time_step(torch, ops, args.steps, args.warmup)
+    dist = time_step.last_dist
+    clocks_after = gpu_clocks()
     tmin = {name: t_min(f, b) for name, _, f, b in ops}
     work = {name: (f, b) for name, _, f, b in ops}
     sum_tmin_ms = sum(tmin.values()) * 1e3
@@ -589,6 +611,8 @@ def main():
             "decode_attention": {"GB/s": round(a_bw / 1e9, 1), "frac": round(a_frac, 4)},
         },
         "per_kernel_ms": {k: round(v, 4) for k, v in per.items()},
+        "per_kernel_ms_dist": dist,
+        "clocks": {"before": clocks_before, "after": clocks_after},
         "roofline": roof,
         "e2e_decode_step": e2e,
         "prefill_attention": pre,
