@@ -93,21 +93,18 @@ __device__ __forceinline__ void load_k_frags(const uint16_t* kp, const int32_t* 
   }
 }
 
-// q fragments (the MFMA A operand): row block rb holds query rows
-// r = 16 rb + l % 16 (token r / GQA, head r % GQA), d 8 (l / 16) .. +7 of each
-// 32-wide step. Rows of tokens >= ntok repeat token 0 (in bounds; those rows
-// of the products are never stored).
-template <int RB>
-__device__ __forceinline__ void load_q_frags(const uint16_t* q0, int64_t q_tok_stride, int ntok, int lane,
-                                             u32x4 (&qa)[RB][4]) {
+// q fragments (the MFMA A operand) of one block of 16 query rows -- 4
+// tokens from q0 on, the GQA heads of each: lane l feeds row r = l % 16
+// (token r / GQA, head r % GQA), d 8 (l / 16) .. +7 of each 32-wide step.
+// Rows of tokens >= ntok repeat the block's first token (in bounds; those
+// rows of the products are never stored).
+__device__ __forceinline__ void load_q_block(const uint16_t* q0, int64_t q_tok_stride, int ntok, int lane,
+                                             u32x4 (&qa)[4]) {
+  const int r = lane & 15;
+  const int t = r / GQA < ntok ? r / GQA : 0;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = 16 * rb + (lane & 15);
-    const int t = r / GQA < ntok ? r / GQA : 0;
-#pragma unroll
-    for (int ds = 0; ds < 4; ++ds)
-      qa[rb][ds] = *reinterpret_cast<const u32x4*>(q0 + t * q_tok_stride + (r % GQA) * HD + 32 * ds + 8 * (lane >> 4));
-  }
+  for (int ds = 0; ds < 4; ++ds)
+    qa[ds] = *reinterpret_cast<const u32x4*>(q0 + t * q_tok_stride + (r % GQA) * HD + 32 * ds + 8 * (lane >> 4));
 }
 
 // V fragments, the B operand of phase 3: V pages are stored d-major
@@ -128,63 +125,96 @@ __device__ __forceinline__ void load_v_frags(const uint16_t* vp, const int32_t* 
   }
 }
 
-// Phase 1: scores S[t][h][key] of the split's SPLIT keys for query rows
-// r = GQA t + h, t < ntok tokens, on the matrix cores:
+// Phase 1 for one block of 16 query rows (4 tokens x the GQA heads): the
+// scores S[t][h][key] of the split's SPLIT keys, t < ntok tokens of the
+// block, on the matrix cores:
 //   S = (sum_d q[r][d] k[key][d]) * qscale   (qscale = scale * log2(e)),
 // the sum taken by v_mfma_f32_16x16x32_bf16 over d in four steps of 32
 // (exact bf16 products, fp32 accumulation, increasing d), then one fp32
 // multiply; keys at or past nt_of(t) get -inf. Rows past GQA ntok are not
 // stored. The element (r, key) gets the same chain whichever row of the MFMA
 // holds r, so a token's scores do not depend on the other tokens of the block.
-template <int RB, typename NtOf>
-__device__ __forceinline__ void split_scores(const u32x4 (&qa)[RB][4], const u32x4 (&kf)[4][4], int ntok, NtOf nt_of,
+template <typename NtOf>
+__device__ __forceinline__ void scores_block(const u32x4 (&qa)[4], const u32x4 (&kf)[4][4], int ntok, NtOf nt_of,
                                              int wave, int lane, float qscale, float (*S)[GQA][SROW]) {
+  const int t_out = lane >> 4;  // token of the 4 rows this lane receives (GQA == 4)
+  const int nt_t = t_out < ntok ? nt_of(t_out) : 0;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int t_out = 4 * rb + (lane >> 4);  // token of the 4 rows this lane receives (GQA == 4)
-    const int nt_t = t_out < ntok ? nt_of(t_out) : 0;
+  for (int kt = 0; kt < 4; ++kt) {
+    f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int ds = 0; ds < 4; ++ds)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[ds]),
+                                                    __builtin_bit_cast(bf16x8, kf[kt][ds]), acc, 0, 0, 0);
+    const int key = 64 * wave + 16 * kt + (lane & 15);
+    if (t_out < ntok) {
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[rb][ds]),
-                                                      __builtin_bit_cast(bf16x8, kf[kt][ds]), acc, 0, 0, 0);
-      const int key = 64 * wave + 16 * kt + (lane & 15);
-      if (t_out < ntok) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[t_out][i][key] = key < nt_t ? acc[i] * qscale : -INFINITY;
-      }
+      for (int i = 0; i < 4; ++i) S[t_out][i][key] = key < nt_t ? acc[i] * qscale : -INFINITY;
     }
   }
 }
 
-// Phase 2, one row (query, head) by one wave: exact max, p = 2^(s - max),
-// l = sum p in fp32 (per-lane order, then the wave butterfly). p is written
-// back over the row as two bf16 parts, hi = RNE(p) and lo = RNE(p - hi) (the
-// difference is exact in fp32), the A operand of phase 3. The whole row is in
-// registers (mx depends on every element) before the first write.
-__device__ __forceinline__ void split_softmax_row(float* row, int lane, float& mx_out, float& l_out) {
-  float v[SPLIT / 64];
-  float mx = -INFINITY;
+// Reduction over a full wave without LDS traffic: DPP moves pair lanes
+// inside each 16-lane row (xor 1, xor 2, then i <-> 7 - i within 8, then
+// i <-> 15 - i within 16), readlane takes the four row totals, combined as
+// (r0 op r1) op (r2 op r3). op is commutative, so every lane ends with the
+// same bits, and the order is fixed.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  v = op(v, dpp_move<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = op(v, dpp_move<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = op(v, dpp_move<0x141>(v));  // row_half_mirror
+  v = op(v, dpp_move<0x140>(v));  // row_mirror
+  auto lane_v = [&](int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l)); };
+  return op(op(lane_v(0), lane_v(16)), op(lane_v(32), lane_v(48)));
+}
+
+// Phase 2, R rows (query, head) by one wave: for each row, the exact max,
+// p = 2^(s - max), l = sum p in fp32 (per-lane order, then wave_reduce).
+// p is written back over the row as two bf16 parts, hi = RNE(p)
+// and lo = RNE(p - hi) (the difference is exact in fp32), the A operand of
+// phase 3. A row's whole contents are in registers (mx depends on every
+// element) before its first write. The cross-lane steps are wave_reduce's;
+// each row's arithmetic is the same whatever R is.
+template <int R>
+__device__ __forceinline__ void split_softmax_rows(float* const (&row)[R], int lane, float (&mx_out)[R],
+                                                   float (&l_out)[R]) {
+  float v[R][SPLIT / 64], mx[R], l[R];
 #pragma unroll
-  for (int r = 0; r < SPLIT / 64; ++r) {
-    v[r] = row[lane + 64 * r];
-    mx = fmaxf(mx, v[r]);
-  }
-  mx = wave_max(mx);
-  float l = 0.0f;
-  uint16_t* pb = reinterpret_cast<uint16_t*>(row);
+  for (int i = 0; i < R; ++i) {
+    mx[i] = -INFINITY;
 #pragma unroll
-  for (int r = 0; r < SPLIT / 64; ++r) {
-    const float pr = __builtin_amdgcn_exp2f(v[r] - mx);  // 2^-inf = 0 for masked slots
-    const uint32_t hb = f32_to_bf16_rne(pr);
-    pb[lane + 64 * r] = (uint16_t)hb;
-    pb[PLO + lane + 64 * r] = (uint16_t)f32_to_bf16_rne(pr - __uint_as_float(hb << 16));
-    l = l + pr;
+    for (int r = 0; r < SPLIT / 64; ++r) {
+      v[i][r] = row[i][lane + 64 * r];
+      mx[i] = fmaxf(mx[i], v[i][r]);
+    }
   }
-  mx_out = mx;
-  l_out = wave_sum(l);
+#pragma unroll
+  for (int i = 0; i < R; ++i) mx[i] = wave_reduce(mx[i], [](float x, float y) { return fmaxf(x, y); });
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    l[i] = 0.0f;
+    uint16_t* pb = reinterpret_cast<uint16_t*>(row[i]);
+#pragma unroll
+    for (int r = 0; r < SPLIT / 64; ++r) {
+      const float pr = __builtin_amdgcn_exp2f(v[i][r] - mx[i]);  // 2^-inf = 0 for masked slots
+      const uint32_t hb = f32_to_bf16_rne(pr);
+      pb[lane + 64 * r] = (uint16_t)hb;
+      pb[PLO + lane + 64 * r] = (uint16_t)f32_to_bf16_rne(pr - __uint_as_float(hb << 16));
+      l[i] = l[i] + pr;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i) l[i] = wave_reduce(l[i], [](float x, float y) { return x + y; });
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    mx_out[i] = mx[i];
+    l_out[i] = l[i];
+  }
 }
 
 // Phase 3 on the matrix cores: the split's partial output
@@ -281,20 +311,21 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
   const int64_t page_stride = (int64_t)a.hkv * head_stride;  // one physical page
   const int64_t head_off = (int64_t)g * head_stride;
 
-  u32x4 qa[1][4], kf[4][4], vf[8][2];
-  load_q_frags<1>(a.q + ((int64_t)b * a.hq + g * GQA) * HD, 0, 1, lane, qa);
+  u32x4 qa[4], kf[4][4], vf[8][2];
+  load_q_block(a.q + ((int64_t)b * a.hq + g * GQA) * HD, 0, 1, lane, qa);
   load_k_frags(a.kp, bt, npg, page_stride, head_off, wave, lane, kf);
   load_v_frags(a.vp, bt, npg, page_stride, head_off, wave, lane, vf);
   __builtin_amdgcn_sched_barrier(0);  // every load issued before the first MFMA waits
-  split_scores<1>(qa, kf, 1, [&](int) { return nt; }, wave, lane, a.qscale, S);
+  scores_block(qa, kf, 1, [&](int) { return nt; }, wave, lane, a.qscale, S);
   __syncthreads();
   const int64_t base = (int64_t)w * a.hq + g * GQA;  // partial row of (split w, query head g GQA)
   {
-    float mx, l;
-    split_softmax_row(S[0][wave], lane, mx, l);  // wave h: query head h
+    float mx[1], l[1];
+    float* const rows[1] = {S[0][wave]};
+    split_softmax_rows<1>(rows, lane, mx, l);  // wave h: query head h
     if (lane == 0) {
-      a.ws_ml[(base + wave) * 2 + 0] = mx;
-      a.ws_ml[(base + wave) * 2 + 1] = l;
+      a.ws_ml[(base + wave) * 2 + 0] = mx[0];
+      a.ws_ml[(base + wave) * 2 + 1] = l[0];
     }
   }
   __syncthreads();
@@ -314,11 +345,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
 //
 // One workgroup per (work item, kv head); a work item is up to QB
 // consecutive query rows of one sequence and one split they see. The split's
-// K and V are loaded once for all of them (keys past the last row's nt read
-// 0); for an earlier row, the keys it must not see carry p = 0, and their
-// products (0 times a finite cached value) add exact zeros.
+// K and V are loaded once into registers for all of them (keys past the last
+// row's nt read 0); the rows then go through the three phases 4 tokens (16
+// query rows) at a time, through one block-sized score array in LDS. For an
+// earlier row, the keys it must not see carry p = 0, and their products (0
+// times a finite cached value) add exact zeros.
 // ---------------------------------------------------------------------------
-constexpr int QB = 8;
+constexpr int QB = 32;
 
 struct PrefillArgs {
   const uint16_t* q;  // [rows, hq, HD]
@@ -336,7 +369,7 @@ struct PrefillArgs {
 };
 
 __global__ __launch_bounds__(256) void prefill_split_kernel(PrefillArgs a) {
-  __shared__ float S[QB][GQA][SROW];
+  __shared__ float S[4][GQA][SROW];  // one block of 4 tokens
 
   const int wi = blockIdx.x / a.hkv, g = blockIdx.x % a.hkv;
   const int tid = threadIdx.x;
@@ -349,39 +382,60 @@ __global__ __launch_bounds__(256) void prefill_split_kernel(PrefillArgs a) {
   const int64_t head_stride = (int64_t)PAGE * HD;
   const int64_t page_stride = (int64_t)a.hkv * head_stride;
   const int64_t head_off = (int64_t)g * head_stride;
+  const int64_t q_tok = (int64_t)a.hq * HD;
+  const uint16_t* q0 = a.q + ((int64_t)row0 * a.hq + g * GQA) * HD;
+  // the item's row positions and split offsets, read once into LDS (each
+  // row block needs them three times)
+  __shared__ int spos[QB], soff[QB];
+  if (tid < nq) {
+    spos[tid] = a.pos[row0 + tid];
+    soff[tid] = a.qoffs[row0 + tid];
+  }
   // partial row of (chunk row row0 + t, split s, query head g GQA), or -1
   // when that row's position is before the split (it does not see it)
   auto part_row = [&](int t) -> int64_t {
-    const int row = row0 + t;
-    return a.pos[row] + 1 - t0 > 0 ? (int64_t)(a.qoffs[row] + s) * a.hq + g * GQA : -1;
+    return spos[t] + 1 - t0 > 0 ? (int64_t)(soff[t] + s) * a.hq + g * GQA : -1;
   };
 
-  constexpr int RB = QB * GQA / 16;
-  u32x4 qa[RB][4], kf[4][4], vf[8][2];
-  load_q_frags<RB>(a.q + ((int64_t)row0 * a.hq + g * GQA) * HD, (int64_t)a.hq * HD, nq, lane, qa);
+  u32x4 qa[4], qn[4], kf[4][4], vf[8][2];
+  load_q_block(q0, q_tok, min(4, nq), lane, qa);
   load_k_frags(a.kp, bt, npg, page_stride, head_off, wave, lane, kf);
   load_v_frags(a.vp, bt, npg, page_stride, head_off, wave, lane, vf);
   __builtin_amdgcn_sched_barrier(0);  // every load issued before the first MFMA waits
-  split_scores<RB>(qa, kf, nq, [&](int t) { return min(SPLIT, a.pos[row0 + t] + 1 - t0); }, wave, lane, a.qscale, S);
-  __syncthreads();
-  for (int r = wave; r < nq * GQA; r += 4) {
-    float mx, l;
-    split_softmax_row(S[r / GQA][r % GQA], lane, mx, l);
-    const int64_t base = part_row(r / GQA);
-    if (lane == 0 && base >= 0) {
-      a.ws_ml[(base + r % GQA) * 2 + 0] = mx;
-      a.ws_ml[(base + r % GQA) * 2 + 1] = l;
+  __syncthreads();                    // spos, soff
+  for (int tb = 0; tb < nq; tb += 4) {  // tokens tb .. tb + 3 of the item
+    const int nb = min(4, nq - tb);
+    if (tb + 4 < nq) load_q_block(q0 + (tb + 4) * q_tok, q_tok, min(4, nq - tb - 4), lane, qn);  // next block
+    scores_block(qa, kf, nb, [&](int t) { return min(SPLIT, spos[tb + t] + 1 - t0); }, wave, lane, a.qscale, S);
+    __syncthreads();
+    {
+      // wave h: head h of the block's 4 tokens (rows of tokens >= nb hold
+      // nothing of use; they are processed and never read)
+      float mx[4], l[4];
+      float* const rows[4] = {S[0][wave], S[1][wave], S[2][wave], S[3][wave]};
+      split_softmax_rows<4>(rows, lane, mx, l);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t < nb) {
+          const int64_t base = part_row(tb + t);
+          if (lane == 0 && base >= 0) {
+            a.ws_ml[(base + wave) * 2 + 0] = mx[t];
+            a.ws_ml[(base + wave) * 2 + 1] = l[t];
+          }
+        }
+      }
     }
-  }
-  __syncthreads();
-  for (int rb = 0; rb < (nq * GQA + 15) / 16; ++rb) {
+    __syncthreads();
     f32x4 acc[2];
-    split_pv(vf, S, rb, nq, nt_max, lane, acc);
-    const int t = 4 * rb + (lane >> 4);
-    if (t < nq) {
-      const int64_t base = part_row(t);
+    split_pv(vf, S, 0, nb, nt_max, lane, acc);
+    const int t = lane >> 4;
+    if (t < nb) {
+      const int64_t base = part_row(tb + t);
       if (base >= 0) store_pv(acc, wave, lane, a.ws_o + base * HD);
     }
+    __syncthreads();  // the next block's scores overwrite S
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) qa[ds] = qn[ds];
   }
 }
 
