@@ -501,8 +501,8 @@ def main():
         print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 5}))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this library has no multi-GPU path "
-              "(see the sharding paragraph in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: this library has no multi-GPU path (each GPU would run it "
+              "on its own shard of rows, columns or sequences). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
