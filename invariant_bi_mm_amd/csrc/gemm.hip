@@ -349,17 +349,19 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// Skinny tiles for small M. With few rows, a 128-column tile gives only
-// N / 128 workgroups, and each walks its k loop one memory round trip per k
-// tile. Here a workgroup owns TM = 32 C rows (C consumer waves, one 32x32
-// output block each) by 32 columns, so N / 32 workgroups stream the weights,
-// and P producer waves move its k tiles through an NS-stage LDS ring, up to
-// NS - 2 tiles ahead of the MFMAs. The per-element chain is the one of
-// gemm_kernel: one v_mfma_f32_32x32x16_bf16 per 16 k, increasing k, fp32
-// accumulator starting at 0, the same operand elements in the same lanes,
-// k padded with zeros to a multiple of 64, the same epilogue -- so every
-// output element has the bits the large tiles give it, and choosing this
-// kernel by M keeps the result independent of M.
+// Ring kernels for small and medium M. With few rows, a 128-column tile of
+// gemm_kernel gives only N / 128 workgroups, and each walks its k loop one
+// memory round trip per k tile. gemm_ring_kernel splits a workgroup into C
+// consumer waves, each owning a (32 FM) x (32 FN) block of the tile, and P
+// producer waves that move its k tiles through an NS-stage LDS ring, up to
+// NS - 2 tiles ahead of the MFMAs. The skinny form (one 32x32 block per
+// consumer, 32 columns per workgroup) gives N / 32 workgroups for M <= 64;
+// the 128x128 form (2x2 consumers of 64x64) serves medium M. The
+// per-element chain is the one of gemm_kernel: one v_mfma_f32_32x32x16_bf16
+// per 16 k, increasing k, fp32 accumulator starting at 0, the same operand
+// elements in the same lanes, k padded with zeros to a multiple of 64, the
+// same epilogue -- so every output element has the bits the other tiles
+// give it, and choosing these kernels by M keeps the result independent of M.
 //
 // The ring's loads are written as inline assembly (buffer_load_dwordx4 ...
 // lds, LDS address in M0, restored afterwards): the compiler then does not
@@ -398,20 +400,27 @@ __device__ __forceinline__ void ring_load16_k(const u32x4& rsrc, uint32_t lds_by
       : "memory");
 }
 
-template <int C, int P, int NS, bool B_NK>
-__global__ __launch_bounds__((C + P) * 64) void gemm_skinny_kernel(GemmArgs g) {
-  // C consumer waves (one 32x32 output block each: TM = 32 C rows by TN = 32
-  // columns) and P producer waves that only move k tiles into the ring.
-  constexpr int TM = 32 * C, TN = 32;
+template <int CM, int CN, int FM, int FN, int P, int NS, bool B_NK>
+__global__ __launch_bounds__((CM * CN + P) * 64) void gemm_ring_kernel(GemmArgs g) {
+  // C = CM x CN consumer waves, each owning a (32 FM) x (32 FN) block of the
+  // TM x TN output tile, and P producer waves that only move k tiles into
+  // the ring.
+  constexpr int C = CM * CN;
+  constexpr int WTM = 32 * FM, WTN = 32 * FN;
+  constexpr int TM = CM * WTM, TN = CN * WTN;
   // One stage: A as TM rows of 64 k (eight 16-byte chunks, swizzled by swz),
-  // then B: [N,K] as 32 rows of 64 k (swizzled likewise), or [K,N] as 64 k
-  // rows of 32 columns (four chunks, stored as they are).
+  // then B: [N,K] as TN rows of 64 k (swizzled likewise), or [K,N] as 64 k
+  // rows of TN columns (TN / 8 chunks; for TN >= 128 chunk c of row r stored
+  // at c ^ 4 (r % 4) as in gemm_kernel, for TN = 32 as they are).
+  static_assert(B_NK || TN == 32 || TN % 128 == 0, "[K,N] stage layout needs TN = 32 or a multiple of 128");
+  constexpr bool BSW = !B_NK && TN >= 128;
+  constexpr int CPR = TN / 8;  // [K,N]: chunks per k row
   constexpr int A_CH = TM * 8, B_CH = TN * 8;
   constexpr int ST = A_CH + B_CH;                          // chunks per stage
   constexpr int A_I = A_CH / 64 / P, B_I = B_CH / 64 / P;  // 1 KB loads per producer per k tile
   constexpr int LPT = A_I + B_I;
   static_assert(A_I * 64 * P == A_CH && B_I * 64 * P == B_CH, "tile not evenly split across producers");
-  static_assert(NS >= 4 && NS % 2 == 0 && (NS - 2) * LPT < 64, "ring depth");
+  static_assert(NS >= 4 && (FM * FN > 1 || NS % 2 == 0) && (NS - 2) * LPT < 64, "ring depth");
   static_assert(NS * ST * 16 <= 160 * 1024, "ring larger than LDS");
   __shared__ u32x4 ring[NS * ST];
 
@@ -466,9 +475,10 @@ __global__ __launch_bounds__((C + P) * 64) void gemm_skinny_kernel(GemmArgs g) {
         b_off[i] = (uint32_t)row * ldb2 + (uint32_t)ch * 16u;
         b_k[i] = ch * 8;
       } else {
-        // [K,N]: k row p / 4 of the tile, columns n0 + 8 (p % 4) ..; columns
-        // past N read zeros
-        const int row = p >> 2, ch = p & 3;
+        // [K,N]: k row p / CPR of the tile, the chunk stored at position
+        // p % CPR; columns past N read zeros
+        const int row = p / CPR, c = p % CPR;
+        const int ch = BSW ? (c ^ (4 * (row & 3))) : c;
         b_off[i] = (n0 + ch * 8 < N) ? (uint32_t)row * ldb2 + (uint32_t)ch * 16u : OOB;
         b_k[i] = row;
       }
@@ -529,84 +539,131 @@ __global__ __launch_bounds__((C + P) * 64) void gemm_skinny_kernel(GemmArgs g) {
   }
 
   // ---------------- consumer ----------------
-  f32x16 acc;
+  const int wm = wave / CN, wn = wave % CN;
+  f32x16 acc[FM][FN];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-  const int arow = 32 * wave + (lane & 31);
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  const int arow0 = wm * WTM + (lane & 31);
+  const int brow0 = wn * WTN + (lane & 31);
   const int khalf = lane >> 5;
   const int tr_g = lane >> 4, tr_l = lane & 15;
   const int tr_row = 8 * (tr_g >> 1) + (tr_l >> 2);
-  const int tr_e = tr_row * TN + (2 * (tr_g & 1) + ((tr_l & 3) >> 1)) * 8 + 4 * (tr_l & 1);
-  // the four k steps' fragments of the tile in stage j
-  auto read = [&](int j, bf16x8 (&af)[4], bf16x8 (&bfr)[4]) {
+  const int tr_sw = BSW ? 4 * (tr_l >> 2) : 0;
+  const int tr_lo = 2 * (tr_g & 1) + ((tr_l & 3) >> 1);
+  const int tr_in = 4 * (tr_l & 1);
+  // fragments of k step kk of the tile in stage j
+  auto read = [&](int j, int kk, bf16x8 (&af)[FM], bf16x8 (&bfr)[FN]) {
     const u32x4* as = ring + j * ST;
     const u32x4* bs = as + A_CH;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      af[kk] = __builtin_bit_cast(bf16x8, as[swz(arow, kk * 2 + khalf)]);
+    for (int i = 0; i < FM; ++i) af[i] = __builtin_bit_cast(bf16x8, as[swz(arow0 + 32 * i, kk * 2 + khalf)]);
+#pragma unroll
+    for (int jj = 0; jj < FN; ++jj) {
       if constexpr (B_NK) {
-        bfr[kk] = __builtin_bit_cast(bf16x8, bs[swz(lane & 31, kk * 2 + khalf)]);
+        bfr[jj] = __builtin_bit_cast(bf16x8, bs[swz(brow0 + 32 * jj, kk * 2 + khalf)]);
       } else {
         typedef short s16x4 __attribute__((ext_vector_type(4)));
         typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
         const __attribute__((address_space(3))) short* bl =
             (const __attribute__((address_space(3))) short*)(const void*)bs;
-        const int e = kk * 16 * TN + tr_e;
+        const int chunk = (((wn * WTN + 32 * jj) >> 3) ^ tr_sw) + tr_lo;
+        const int e = (kk * 16 + tr_row) * TN + chunk * 8 + tr_in;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(bl + e));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(bl + e + 4 * TN));
-        bfr[kk] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        bfr[jj] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
   };
-  auto mma = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[4]) {
+  auto mma = [&](const bf16x8 (&af)[FM], const bf16x8 (&bfr)[FN]) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], bfr[kk], acc, 0, 0, 0);
-  };
-  // Software pipeline: the fragments of tile t + 1 are read while the MFMAs
-  // of tile t run (fragment buffers indexed by stage parity; NS is even).
-  bf16x8 fa[2][4], fb[2][4];
-  bar();
-  read(0, fa[0], fb[0]);
-  auto iter = [&](auto J, int t) {
-    constexpr int j = decltype(J)::value;
-    bar();
-    read((j + 1) % NS, fa[(j + 1) & 1], fb[(j + 1) & 1]);  // tile t + 1 (zeros past K)
-    mma(fa[j & 1], fb[j & 1]);
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int jj = 0; jj < FN; ++jj)
+        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[jj], acc[i][jj], 0, 0, 0);
   };
   int t = 0;
-  for (; t + NS <= nk; t += NS) static_for<0, NS>([&](auto J) { iter(J, t + decltype(J)::value); });
-  static_for<0, NS - 1>([&](auto J) {
-    if (t + decltype(J)::value < nk) iter(J, t + decltype(J)::value);
-  });
+  if constexpr (FM * FN == 1) {
+    // One block per wave: its four MFMAs per tile form a dependent chain, so
+    // the next tile's fragments are read while they run (fragment buffers
+    // indexed by stage parity; NS is even).
+    bf16x8 fa[2][4][1], fb[2][4][1];
+    bar();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) read(0, kk, fa[0][kk], fb[0][kk]);
+    auto iter = [&](auto J, int) {
+      constexpr int j = decltype(J)::value;
+      bar();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) read((j + 1) % NS, kk, fa[(j + 1) & 1][kk], fb[(j + 1) & 1][kk]);  // tile t + 1
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) mma(fa[j & 1][kk], fb[j & 1][kk]);
+    };
+    for (; t + NS <= nk; t += NS) static_for<0, NS>([&](auto J) { iter(J, t + decltype(J)::value); });
+    static_for<0, NS - 1>([&](auto J) {
+      if (t + decltype(J)::value < nk) iter(J, t + decltype(J)::value);
+    });
+  } else {
+    // Several blocks per wave: the k steps of a tile are pipelined inside it
+    // (step kk + 1's fragments read while step kk's MFMAs run).
+    bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+    bar();
+    auto iter = [&](auto J, int) {
+      constexpr int j = decltype(J)::value;
+      bar();  // tile t is in stage j; every wave is done with tile t - 1
+      read(j, 0, fa0, fb0);
+      read(j, 1, fa1, fb1);
+      mma(fa0, fb0);
+      read(j, 2, fa0, fb0);
+      mma(fa1, fb1);
+      read(j, 3, fa1, fb1);
+      mma(fa0, fb0);
+      mma(fa1, fb1);
+    };
+    for (; t + NS <= nk; t += NS) static_for<0, NS>([&](auto J) { iter(J, t + decltype(J)::value); });
+    static_for<0, NS - 1>([&](auto J) {
+      if (t + decltype(J)::value < nk) iter(J, t + decltype(J)::value);
+    });
+  }
 
   // Epilogue (as in gemm_kernel): lane holds C[8 (r / 4) + 4 (lane / 32) +
-  // r % 4][lane % 32] of its 32x32 block, r = 0..15.
-  const int gn = n0 + (lane & 31);
-  if (m0 + 32 * wave >= M || gn >= N) return;
-  float bterm = 0.0f;
-  if (g.bias_mode == 1) {
-    bterm = g.beta * __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(g.bias)[gn]) << 16);
-  } else if (g.bias_mode == 2) {
-    bterm = g.beta * reinterpret_cast<const float*>(g.bias)[gn];
-  }
+  // r % 4][lane % 32] of each 32x32 block, r = 0..15.
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int gm = m0 + 32 * wave + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    if (gm >= M) continue;
-    float v = g.alpha * acc[r];
-    if (g.bias_mode != 0) v = v + bterm;
-    const int64_t off = (int64_t)gm * g.ldc + gn;
-    if (g.out_bf16)
-      reinterpret_cast<uint16_t*>(g.c)[off] = (uint16_t)f32_to_bf16_rne(v);
-    else
-      reinterpret_cast<float*>(g.c)[off] = v;
+  for (int jj = 0; jj < FN; ++jj) {
+    const int gn = n0 + wn * WTN + 32 * jj + (lane & 31);
+    if (gn >= N) continue;
+    float bterm = 0.0f;
+    if (g.bias_mode == 1) {
+      bterm = g.beta * __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(g.bias)[gn]) << 16);
+    } else if (g.bias_mode == 2) {
+      bterm = g.beta * reinterpret_cast<const float*>(g.bias)[gn];
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int gm = m0 + wm * WTM + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (gm >= M) continue;
+        float v = g.alpha * acc[i][jj][r];
+        if (g.bias_mode != 0) v = v + bterm;
+        const int64_t off = (int64_t)gm * g.ldc + gn;
+        if (g.out_bf16)
+          reinterpret_cast<uint16_t*>(g.c)[off] = (uint16_t)f32_to_bf16_rne(v);
+        else
+          reinterpret_cast<float*>(g.c)[off] = v;
+      }
+    }
   }
 }
 
-template <int C, int P, int NS, bool B_NK>
-hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
+template <int CM, int CN, int FM, int FN, int P, int NS, bool B_NK>
+hipError_t launch_ring(const GemmArgs& a, hipStream_t s) {
   const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
-  hipLaunchKernelGGL((gemm_skinny_kernel<C, P, NS, B_NK>), dim3((unsigned)tiles), dim3((C + P) * 64), 0, s, a);
+  hipLaunchKernelGGL((gemm_ring_kernel<CM, CN, FM, FN, P, NS, B_NK>), dim3((unsigned)tiles),
+                     dim3((CM * CN + P) * 64), 0, s, a);
   return hipGetLastError();
 }
 
@@ -619,8 +676,9 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Skinny: one consumer wave (32 rows) when the 32-row strips fit in one
-// round over the CUs, else two (64 rows); two producer waves either way.
+// Skinny (M <= 64): one consumer wave (32 rows) when the 32-row strips fit
+// in one round over the CUs, else two (64 rows); two producer waves either
+// way.
 static GemmConfig skinny_config(int64_t m, int64_t strips) {
   if (m <= 32 || ((m + 31) / 32) * strips <= 256) return GemmConfig{32, 32, TK, 3};
   return GemmConfig{64, 32, TK, 4};
@@ -634,11 +692,14 @@ static GemmConfig skinny_config(int64_t m, int64_t strips) {
 // on how many rows there are. (The batch-dependent selection the pages warn
 // about changes the reduction -- split-K, a different instruction -- and
 // nothing here does.) Measured on MI355X for the Qwen3-8B projection shapes:
-//   * skinny (32 or 64 rows x 32 columns, deep ring) while M is small and
-//     its N / 32 column strips fill the chip at most about twice: 2.5-3.6x
-//     faster than 128x128 at M <= 64 (N = 4096, 6144, K = 4096 and 12288),
-//     1.25-1.6x at N = 24576; at the 151936-wide LM head both stream at
-//     ~5.4 TB/s and 128x128 is kept;
+//   * skinny (32 or 64 rows x 32 columns, deep ring) for M <= 64: 2.5-3.6x
+//     faster than 128x128 (N = 4096, 6144, K = 4096 and 12288), 1.25-1.6x
+//     at N = 24576; at the 151936-wide LM head both stream at ~5.4 TB/s and
+//     128x128 is kept;
+//   * the same deep ring with a 128x128 tile (2x2 consumer waves of 64x64)
+//     for M > 64 while its tiles fit one round over the CUs: 1.15-1.35x
+//     faster than 128x128 or skinny at M = 128-1024, 1.6x than 256x256 at
+//     M = 128, N = 24576;
 //   * 256x256 (8 waves, 128x64 each) once its tiles fill the chip (M >= 192,
 //     at least 192 tiles, rounds of 256 at least 70 % full on average):
 //     1.25-1.3x faster than 128x128 at M = 4096 (N = 4096, LM head), 1.1x
@@ -648,7 +709,7 @@ GemmConfig gemm_config(int64_t m, int64_t n, int64_t k, bool b_is_nk) {
   (void)b_is_nk;
   const int64_t strips = (n + 31) / 32;
   if (m <= 64 && n <= 32768) return skinny_config(m, strips);
-  if (m <= 256 && ((m + 63) / 64) * strips <= 512) return skinny_config(m, strips);
+  if (m > 64 && ((m + 127) / 128) * ((n + 127) / 128) <= 256) return GemmConfig{128, 128, TK, 6};
   const int64_t t256 = ((m + 255) / 256) * ((n + 255) / 256);
   const int64_t rounds = (t256 + 255) / 256;  // one 256x256 workgroup per CU
   if (m >= 192 && t256 >= 192 && 10 * t256 >= 7 * rounds * 256) return GemmConfig{256, 256, TK, 8};
@@ -677,11 +738,13 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   a.tiles_n = (int)((p.n + cfg.tile_n - 1) / cfg.tile_n);
   if (cfg.tile_n == 32) {  // skinny: 16-stage ring with one consumer, 12 with two
     if (cfg.tile_m == 32)
-      return p.b_is_nk ? launch_skinny<1, 2, 16, true>(a, s) : launch_skinny<1, 2, 16, false>(a, s);
+      return p.b_is_nk ? launch_ring<1, 1, 1, 1, 2, 16, true>(a, s) : launch_ring<1, 1, 1, 1, 2, 16, false>(a, s);
     if (cfg.tile_m == 64)
-      return p.b_is_nk ? launch_skinny<2, 2, 12, true>(a, s) : launch_skinny<2, 2, 12, false>(a, s);
+      return p.b_is_nk ? launch_ring<2, 1, 1, 1, 2, 12, true>(a, s) : launch_ring<2, 1, 1, 1, 2, 12, false>(a, s);
     return hipErrorInvalidConfiguration;
   }
+  if (cfg.tile_m == 128 && cfg.tile_n == 128 && cfg.waves == 6)  // 2x2 consumers of 64x64, 4-stage ring
+    return p.b_is_nk ? launch_ring<2, 2, 2, 2, 2, 4, true>(a, s) : launch_ring<2, 2, 2, 2, 2, 4, false>(a, s);
 #define BI_GEMM_CASE(TM_, TN_, WM_, WN_)                                                          \
   if (cfg.tile_m == TM_ && cfg.tile_n == TN_ && cfg.waves == WM_ * WN_)                            \
     return p.b_is_nk ? launch_cfg<TM_, TN_, WM_, WN_, true>(a, s) : launch_cfg<TM_, TN_, WM_, WN_, false>(a, s);

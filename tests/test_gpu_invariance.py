@@ -116,18 +116,22 @@ def test_mm_adversarial_other_rows(lib, fill):
             assert same_bits(lib.bi_mm(x, w)[pos], ref), (fill, m, pos)
 
 
+ALL_CONFIGS = {(32, 32, 64, 3), (64, 32, 64, 4), (128, 128, 64, 6), (128, 128, 64, 4), (256, 256, 64, 8)}
+
+
 @pytest.mark.parametrize("b_is_nk", [False, True])
-def test_mm_every_tile_configuration_same_bits(lib, b_is_nk):
+@pytest.mark.parametrize("n", [4096, 6144])
+def test_mm_every_tile_configuration_same_bits(lib, b_is_nk, n):
     """A row's addmm output is the same, bit for bit, at an M of each tile
-    configuration the shape takes (skinny 32 and 64 rows, 128x128,
-    256x256), at the first and last row, for fp32 and bf16 outputs and
-    a ragged K (a 64-tail) -- and it matches the oracle."""
-    k, n = 1032, 4096
+    configuration the shape takes (skinny 32 or 64 rows, the 128x128 ring,
+    128x128, 256x256), at the first and last row, for fp32 and bf16
+    outputs and a ragged K (a 64-tail) -- and it matches the oracle."""
+    k = 1032
     first = {}
     for m in range(1, 4097):
         first.setdefault(lib.bi_gemm_config(m, n, k, b_is_nk), m)
     say(f"configs for k={k} n={n} nk={b_is_nk}: {first}")
-    assert len(first) == 4, first
+    assert len(first) >= 4, first
     w = S.normal_bf16((n, k) if b_is_nk else (k, n), 1 / k, seed=71, device=DEV)
     bias = S.normal_bf16((n,), 0.1, seed=72, device=DEV)
     row = S.normal_bf16((1, k), 1.0, seed=73, device=DEV)[0]
@@ -144,6 +148,12 @@ def test_mm_every_tile_configuration_same_bits(lib, b_is_nk):
                     x = with_row(m, k, row, pos, seed=900 + m)
                     c = lib.bi_addmm(bias, x, w, b_is_nk=b_is_nk, out_dtype=od, beta=0.5, alpha=1.5)
                     assert same_bits(c[pos], ref), (cfg, m, pos, od)
+
+
+def test_every_tile_configuration_is_exercised(lib):
+    """The shapes of the test above take every configuration of the table between them."""
+    seen = {lib.bi_gemm_config(m, n, 1032, nk) for n in (4096, 6144) for nk in (False, True) for m in range(1, 4097)}
+    assert seen == ALL_CONFIGS, seen
 
 
 QWEN = [(4096, 6144), (4096, 4096), (4096, 24576), (12288, 4096)]
