@@ -318,6 +318,45 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
 
   // Epilogue: lane holds C[8*(r/4) + 4*(lane/32) + r%4][lane%32] of each
   // 32x32 tile, r = 0..15.
+  // Interior fp32 tiles leave as 16-byte row chunks: each wave passes its
+  // 32x32 blocks, alpha and bias already applied, through 4 KB of the (now
+  // idle) first A stage -- column groups of 4 XOR-swizzled by row -- and
+  // stores every row chunk with one 16-byte store. Same values, fewer and
+  // wider stores.
+  if (!g.out_bf16 && m0 + TM <= M && n0 + TN <= N && (g.ldc & 3) == 0 &&
+      (reinterpret_cast<uintptr_t>(g.c) & 15) == 0) {
+    static_assert(TM * 8 * 16 >= NW * 4096, "first A stage too small for the epilogue blocks");
+    float* blk = reinterpret_cast<float*>(As0) + wave * 1024;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int gn0 = n0 + wn * WTN + j * 32;
+      float bterm = 0.0f;
+      if (g.bias_mode == 1) {
+        bterm = g.beta * __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(g.bias)[gn0 + (lane & 31)]) << 16);
+      } else if (g.bias_mode == 2) {
+        bterm = g.beta * reinterpret_cast<const float*>(g.bias)[gn0 + (lane & 31)];
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          float t = g.alpha * acc[i][j][r];
+          if (g.bias_mode != 0) t = t + bterm;
+          blk[row * 32 + ((lane & 31) ^ ((row & 7) << 2))] = t;
+        }
+        const int64_t gm0 = m0 + wm * WTM + i * 32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ch = lane + 64 * q;  // 32 rows x 8 chunks of 4 floats
+          const int row = ch >> 3, c4 = ch & 7;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(blk + row * 32 + 4 * (c4 ^ (row & 7)));
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(g.c) + (gm0 + row) * g.ldc + gn0 + 4 * c4) = v;
+        }
+      }
+    }
+    return;
+  }
   const int col_in = lane & 31;
   const int row_in = 4 * (lane >> 5);
 #pragma unroll
