@@ -230,6 +230,9 @@ def time_step_graph(torch, ops, steps, warmup, check=()):
         g.replay()
     e1.record()
     torch.cuda.synchronize()
+    for t, e in zip(check, eager):  # and still equal after the timed replays
+        if not torch.equal(t.view(torch.uint8), e.view(torch.uint8)):
+            raise RuntimeError("graph replay of the step differs from the eager step")
     return e0.elapsed_time(e1) / steps
 
 
