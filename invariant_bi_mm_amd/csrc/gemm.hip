@@ -20,8 +20,10 @@
 //   stream-K or atomic anywhere.
 //
 // Which tile configuration runs is chosen from (M, N, K) -- a skinny kernel
-// for small M (below), 128x128 or 256x256 otherwise -- and, because every
-// configuration runs the chain above, that choice never changes a bit.
+// for small M (below), 128x128 or 256x256 otherwise, the last with its
+// leftover columns on 256x128 tiles when its final round over the CUs would
+// be part-empty -- and, because every configuration runs the chain above,
+// that choice never changes a bit.
 //
 // Structure (one workgroup per TM x TN output tile)
 //   * global -> LDS directly (buffer_load ... lds, 16 bytes per lane): no
@@ -49,6 +51,8 @@
 //     This only permutes which workgroup computes which tile.
 #include "bi_internal.h"
 #include "device_common.h"
+
+#include <numeric>
 
 namespace bi {
 namespace {
@@ -756,6 +760,24 @@ GemmConfig gemm_config(int64_t m, int64_t n, int64_t k, bool b_is_nk) {
   return GemmConfig{128, 128, TK, 4};
 }
 
+// Columns of a 256x256 GEMM left to full rounds of 256x256 tiles; the rest
+// (if any) goes to 256x128 tiles in a second launch. Whole rounds of 256 CUs
+// need tiles_m * n1 to be a multiple of 256. A round of 256x128 tiles takes
+// ~0.65 of a 256x256 round (measured, K = 4096); the split is taken only
+// when that predicts fewer rounds. Measured on MI355X: q+kv at M = 4096
+// (384 tiles, 1.5 rounds) 7-8 % faster, gate+up at M = 1024 4-7 %, the LM
+// head at M = 256 (594 tiles) 3-4 %. Both parts compute every element with
+// the chain above, so the bits do not change.
+static int64_t full_round_columns(int64_t tiles_m, int64_t tiles_n, int64_t m, int64_t n) {
+  const int64_t g = 256 / std::gcd(tiles_m, (int64_t)256);  // tiles_m * n1 % 256 == 0 iff g divides n1
+  const int64_t n1 = (tiles_n / g) * g;
+  if (n1 == 0 || n1 == tiles_n) return tiles_n;
+  const int64_t t_tail = ((m + 255) / 256) * ((n - n1 * 256 + 127) / 128);
+  const double split = (double)(tiles_m * n1 / 256) + 0.65 * (double)((t_tail + 255) / 256);
+  const double whole = (double)((tiles_m * tiles_n + 255) / 256);
+  return split < whole - 0.05 ? n1 : tiles_n;
+}
+
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   const GemmConfig cfg = gemm_config(p.m, p.n, p.k, p.b_is_nk);
   GemmArgs a;
@@ -784,6 +806,24 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   }
   if (cfg.tile_m == 128 && cfg.tile_n == 128 && cfg.waves == 6)  // 2x2 consumers of 64x64, 4-stage ring
     return p.b_is_nk ? launch_ring<2, 2, 2, 2, 2, 4, true>(a, s) : launch_ring<2, 2, 2, 2, 2, 4, false>(a, s);
+  if (cfg.tile_m == 256 && cfg.tile_n == 256) {
+    const int64_t n1 = full_round_columns(a.tiles_m, a.tiles_n, p.m, p.n);
+    if (n1 < a.tiles_n) {
+      const int64_t off = n1 * 256;  // first column of the 256x128 part
+      GemmArgs a2 = a;
+      a.n = (int)off;
+      a.tiles_n = (int)n1;
+      a2.b = p.b_is_nk ? a2.b + off * p.ldb : a2.b + off;
+      a2.c = p.c_bf16 ? (void*)(static_cast<uint16_t*>(p.c) + off) : (void*)(static_cast<float*>(p.c) + off);
+      if (a2.bias_mode == 1) a2.bias = static_cast<const uint16_t*>(p.bias) + off;
+      if (a2.bias_mode == 2) a2.bias = static_cast<const float*>(p.bias) + off;
+      a2.n = (int)(p.n - off);
+      a2.tiles_n = (int)((p.n - off + 127) / 128);
+      const hipError_t e = p.b_is_nk ? launch_cfg<256, 256, 2, 4, true>(a, s) : launch_cfg<256, 256, 2, 4, false>(a, s);
+      if (e != hipSuccess) return e;
+      return p.b_is_nk ? launch_cfg<256, 128, 4, 2, true>(a2, s) : launch_cfg<256, 128, 4, 2, false>(a2, s);
+    }
+  }
 #define BI_GEMM_CASE(TM_, TN_, WM_, WN_)                                                          \
   if (cfg.tile_m == TM_ && cfg.tile_n == TN_ && cfg.waves == WM_ * WN_)                            \
     return p.b_is_nk ? launch_cfg<TM_, TN_, WM_, WN_, true>(a, s) : launch_cfg<TM_, TN_, WM_, WN_, false>(a, s);
