@@ -9,7 +9,8 @@ up"); the cost is measured on Qwen3-8B decoding ("Key takeaways"). This
 module chains the library's kernels into that per-token computation so a
 sequence's stream can be checked bit for bit across batch compositions.
 
-Per layer (activations bf16, weights [K, N] bf16, fp32 accumulation):
+Per layer (activations bf16, weights bf16 stored [K, N] or, with the
+weights' "b_is_nk" flag, [N, K] as nn.Linear keeps them; fp32 accumulation):
 
     h = rmsnorm(x)                          bi_rmsnorm / bi_add_rmsnorm
     qkv = h @ W_qkv                         bi_mm
@@ -67,6 +68,8 @@ class Decoder:
     lists over layers of w_in [H], w_qkv [H, (Hq + 2 Hkv) D], q_norm [D],
     k_norm [D], w_o [Hq D, H], w_post [H], w_gu [H, 2 I], w_down [I, H];
     w_final [H]; w_lm [H, V]; b_lm [V]; cos, sin fp32 [max_pos, D / 2].
+    The matrices are given [K, N] as listed, or transposed ([N, K], the
+    nn.Linear layout) when weights["b_is_nk"] is true.
     """
 
     def __init__(self, shape: Qwen3Shape, weights: dict, num_pages: int, device="cuda"):
@@ -84,21 +87,22 @@ class Decoder:
     def _layers(self, x, positions, lens_dev, offs_dev, total, ws, block_table):
         """The kernels of one step after the embedding; returns (logits, log-probs, greedy tokens)."""
         s, w = self.s, self.w
+        nk = bool(w.get("b_is_nk", False))
         bsz = x.shape[0]
         h = bi_rmsnorm(x, w["w_in"][0], s.eps)
         for l in range(s.layers):
-            qkv = bi_mm(h, w["w_qkv"][l], out_dtype=torch.bfloat16)
+            qkv = bi_mm(h, w["w_qkv"][l], b_is_nk=nk, out_dtype=torch.bfloat16)
             q = bi_qknorm_rope_append(qkv, w["q_norm"][l], w["k_norm"][l], w["cos"], w["sin"], positions,
                                       block_table, self.k_pages[l], self.v_pages[l],
                                       num_q_heads=s.num_q_heads, num_kv_heads=s.num_kv_heads, eps=s.eps)
             a = bi_decode_attention(q, self.k_pages[l], self.v_pages[l], block_table, lens_dev, offs_dev, total,
                                     workspace=ws, out_dtype=torch.bfloat16, split_tokens=s.split_tokens)
-            o = bi_mm(a.view(bsz, s.hidden), w["w_o"][l], out_dtype=torch.bfloat16)
+            o = bi_mm(a.view(bsz, s.hidden), w["w_o"][l], b_is_nk=nk, out_dtype=torch.bfloat16)
             h = bi_add_rmsnorm(x, o, w["w_post"][l], s.eps)
-            gu = bi_mm(h, w["w_gu"][l], out_dtype=torch.bfloat16)
-            dn = bi_mm(bi_silu_mul(gu), w["w_down"][l], out_dtype=torch.bfloat16)
+            gu = bi_mm(h, w["w_gu"][l], b_is_nk=nk, out_dtype=torch.bfloat16)
+            dn = bi_mm(bi_silu_mul(gu), w["w_down"][l], b_is_nk=nk, out_dtype=torch.bfloat16)
             h = bi_add_rmsnorm(x, dn, w["w_in"][l + 1] if l + 1 < s.layers else w["w_final"], s.eps)
-        logits = bi_addmm(w["b_lm"], h, w["w_lm"])
+        logits = bi_addmm(w["b_lm"], h, w["w_lm"], b_is_nk=nk)
         logp, nxt = bi_log_softmax(logits)
         return logits, logp, nxt
 

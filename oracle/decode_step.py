@@ -51,7 +51,9 @@ class OracleDecoder:
       embed [V, H]; per layer l: w_in[l] [H], w_qkv[l] [H, (Hq + 2 Hkv) D],
       q_norm[l] [D], k_norm[l] [D], w_o[l] [Hq D, H], w_post[l] [H],
       w_gu[l] [H, 2 I], w_down[l] [I, H]; w_final [H]; w_lm [H, V];
-      b_lm [V]; cos, sin [max_pos, D / 2].
+      b_lm [V]; cos, sin [max_pos, D / 2]. The matrices are [K, N] as
+      listed, or [N, K] (nn.Linear's layout, C = A B^T) when
+      weights["b_is_nk"] is true.
     caches: per sequence, per layer, (K, V) bf16 bits [L, Hkv, D] of the
       tokens already cached (the prompt).
     """
@@ -66,13 +68,14 @@ class OracleDecoder:
     def step(self, tokens, seqs=None):
         """Feed tokens[i] to sequence seqs[i] (default: all, in order); return fp64 logits [B, V]."""
         w, eps, hq, hkv = self.w, self.eps, self.hq, self.hkv
+        nk = bool(w.get("b_is_nk", False))
         seqs = list(range(len(tokens))) if seqs is None else list(seqs)
         bsz, d = len(tokens), 128
         group = hq // hkv
         x = _bits(embed(w["embed"], tokens))
         h = _bits(rmsnorm(x, w["w_in"][0], eps))
         for l in range(self.layers):
-            qkv = _bits(mm(h, w["w_qkv"][l]))
+            qkv = _bits(mm(h, w["w_qkv"][l], b_is_nk=nk))
             pos = [len(self.kv[s][l][0]) for s in seqs]
             q, k, v = qknorm_rope(qkv, w["q_norm"][l], w["k_norm"][l], eps, w["cos"], w["sin"], pos, hq, hkv)
             q, k = round_bf16(q), round_bf16(k)
@@ -87,12 +90,12 @@ class OracleDecoder:
                     sc = (K[:, g, :] @ q[i, hh]) / np.sqrt(d)
                     p = np.exp(sc - sc.max())
                     att[i, hh] = (p / p.sum()) @ V[:, g, :]
-            o = _bits(mm(_bits(att.reshape(bsz, hq * d)), w["w_o"][l]))
+            o = _bits(mm(_bits(att.reshape(bsz, hq * d)), w["w_o"][l], b_is_nk=nk))
             x, y = add_rmsnorm(x, o, w["w_post"][l], eps)
             h = _bits(y)
-            gu = _bits(mm(h, w["w_gu"][l]))
-            dn = _bits(mm(_bits(silu_mul(gu)), w["w_down"][l]))
+            gu = _bits(mm(h, w["w_gu"][l], b_is_nk=nk))
+            dn = _bits(mm(_bits(silu_mul(gu)), w["w_down"][l], b_is_nk=nk))
             w_next = w["w_in"][l + 1] if l + 1 < self.layers else w["w_final"]
             x, y = add_rmsnorm(x, dn, w_next, eps)
             h = _bits(y)
-        return addmm(w["b_lm"], h, w["w_lm"])
+        return addmm(w["b_lm"], h, w["w_lm"], b_is_nk=nk)

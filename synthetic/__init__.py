@@ -125,27 +125,30 @@ def rope_tables(max_pos: int, head_dim: int = 128, theta: float = 1.0e6):
 
 
 def qwen3_weights(hidden: int, num_q_heads: int, num_kv_heads: int, head_dim: int, intermediate: int, vocab: int,
-                  layers: int, seed: int, device="cpu", max_pos: int = 40000, qk_norm=(0.5, 1.5)):
-    """Random weights of a Qwen3-style decoder, every matrix stored [K, N]:
-    projections N(0, 0.02) (the projection-GEMM workloads' draw), embedding
-    N(0, 1), LM-head bias N(0, 0.1), RMSNorm weights U(0.5, 1.5) (the q/k
-    ones U(qk_norm)), and the rotary tables of ``rope_tables``. Keys are the
-    ones the decode step takes (embed, w_in, w_qkv, q_norm, k_norm, w_o,
-    w_post, w_gu, w_down, w_final, w_lm, b_lm, cos, sin); per-layer entries
-    are lists."""
+                  layers: int, seed: int, device="cpu", max_pos: int = 40000, qk_norm=(0.5, 1.5), b_is_nk: bool = True):
+    """Random weights of a Qwen3-style decoder: projections N(0, 0.02) (the
+    projection-GEMM workloads' draw), embedding N(0, 1), LM-head bias
+    N(0, 0.1), RMSNorm weights U(0.5, 1.5) (the q/k ones U(qk_norm)), and
+    the rotary tables of ``rope_tables``. Every projection and the LM head
+    is stored [N, K] (nn.Linear's [out, in]) when ``b_is_nk``, else [K, N];
+    the dict's "b_is_nk" entry says which. Other keys are the ones the
+    decode step takes (embed, w_in, w_qkv, q_norm, k_norm, w_o, w_post,
+    w_gu, w_down, w_final, w_lm, b_lm, cos, sin); per-layer entries are
+    lists."""
     h, d = hidden, head_dim
     qkv_n = (num_q_heads + 2 * num_kv_heads) * d
     r = lambda shape, var, k: normal_bf16(shape, var, seed=seed + k, device=device)  # noqa: E731
+    m = (lambda k_, n_, var, k: r((n_, k_), var, k)) if b_is_nk else (lambda k_, n_, var, k: r((k_, n_), var, k))  # noqa: E731
     u = lambda n, k, lo=0.5, hi=1.5: uniform_bf16((n,), lo, hi, seed=seed + k, device=device)  # noqa: E731
     w = {"embed": r((vocab, h), 1.0, 1),
          "w_in": [u(h, 100 + l) for l in range(layers)], "w_post": [u(h, 200 + l) for l in range(layers)],
          "q_norm": [u(d, 300 + l, *qk_norm) for l in range(layers)],
          "k_norm": [u(d, 400 + l, *qk_norm) for l in range(layers)],
-         "w_qkv": [r((h, qkv_n), 0.02, 500 + l) for l in range(layers)],
-         "w_o": [r((num_q_heads * d, h), 0.02, 600 + l) for l in range(layers)],
-         "w_gu": [r((h, 2 * intermediate), 0.02, 700 + l) for l in range(layers)],
-         "w_down": [r((intermediate, h), 0.02, 800 + l) for l in range(layers)],
-         "w_final": u(h, 2), "w_lm": r((h, vocab), 0.02, 3), "b_lm": r((vocab,), 0.1, 4)}
+         "w_qkv": [m(h, qkv_n, 0.02, 500 + l) for l in range(layers)],
+         "w_o": [m(num_q_heads * d, h, 0.02, 600 + l) for l in range(layers)],
+         "w_gu": [m(h, 2 * intermediate, 0.02, 700 + l) for l in range(layers)],
+         "w_down": [m(intermediate, h, 0.02, 800 + l) for l in range(layers)],
+         "w_final": u(h, 2), "w_lm": m(h, vocab, 0.02, 3), "b_lm": r((vocab,), 0.1, 4), "b_is_nk": b_is_nk}
     cos, sin = rope_tables(max_pos, d)
     w["cos"], w["sin"] = cos.to(device), sin.to(device)
     return w

@@ -182,7 +182,9 @@ def test_decode_step_matches_oracle_small_model(lib):
     dec = Decoder(shape, w, num_pages=64)
     batch = place(dec, caches, lens, room=4, seed=9200)
     npw = {k: ([S.bf16_bits_numpy(t) for t in v] if isinstance(v, list) else
+               v if not isinstance(v, torch.Tensor) else
                (S.bf16_bits_numpy(v) if v.dtype == torch.bfloat16 else v.cpu().numpy())) for k, v in w.items()}
+    assert npw["b_is_nk"] is True  # the nn.Linear layout the decode step is benchmarked with
     ocaches = [[(S.bf16_bits_numpy(k), S.bf16_bits_numpy(v)) for (k, v) in c] for c in caches]
     orc = OracleDecoder(npw, 2, 8, 2, shape.eps, ocaches)
     g = torch.Generator().manual_seed(9300)

@@ -10,6 +10,7 @@ wrong kv head.
 import math
 
 import numpy as np
+import pytest
 
 import oracle as O
 from oracle.decode_step import OracleDecoder
@@ -193,6 +194,26 @@ def test_decoder_rows_are_independent_and_one_token_cache_attends_to_itself():
     d1.step(np.array([1]))
     assert np.array_equal(d1.kv[0][0][1][0, 0], O.bf16_bits_to_f64(qkv)[0, 5 * 128:6 * 128])
 
+
+
+def test_decoder_nn_linear_layout_gives_the_same_logits():
+    # the same model with every matrix stored transposed ([N, K], nn.Linear's
+    # layout) and the b_is_nk flag set must decode to the same logits: pins
+    # that the oracle applies the flag to every projection and the LM head
+    rng = np.random.default_rng(6)
+    w = _tiny_weights(rng, layers=2)
+    wt = dict(w, b_is_nk=True)
+    for k in ("w_qkv", "w_o", "w_gu", "w_down"):
+        wt[k] = [np.ascontiguousarray(x.T) for x in w[k]]
+    wt["w_lm"] = np.ascontiguousarray(w["w_lm"].T)
+    caches = [[(rand_bf16(rng, (L, 1, 128)), rand_bf16(rng, (L, 1, 128))) for _ in range(2)] for L in (2, 7)]
+    a, b = OracleDecoder(w, 2, 4, 1, 1e-6, caches), OracleDecoder(wt, 2, 4, 1, 1e-6, caches)
+    for toks in ([3, 11], [30, 0]):
+        la, lb = a.step(np.array(toks)), b.step(np.array(toks))
+        assert np.allclose(la, lb, rtol=1e-12, atol=1e-12)
+    # [K, N] weights flagged [N, K] are rejected (q+kv's inner dimension no longer matches)
+    with pytest.raises(ValueError):
+        OracleDecoder(dict(w, b_is_nk=True), 2, 4, 1, 1e-6, caches).step(np.array([3, 11]))
 
 # ------------------------------------------------------------------ prefill attention
 def _paged(rng, lens, hkv=1, page=16):
