@@ -34,6 +34,8 @@
 #include "bi_internal.h"
 #include "device_common.h"
 
+#include <type_traits>
+
 namespace bi {
 namespace {
 
@@ -444,8 +446,11 @@ __global__ __launch_bounds__(256) void prefill_split_kernel(PrefillArgs a) {
 // splits s = r, r + 8, r + 16, ... in increasing order (m, l, o weighted by
 // 2^(m_s - M)); the 8 group sums are then added as
 // ((g0 + g1) + (g2 + g3)) + ((g4 + g5) + (g6 + g7)). The order depends only on
-// the sequence's split count, and the 8 chains cut the dependent-load chain of
-// a 128-split sequence to 16 steps.
+// the sequence's split count. A row of up to 8 splits (a context of up to
+// 2048 tokens; every prefill row of a short prompt) loads its partials at
+// once, one per group, and takes the exact max from the loaded values: one
+// memory round trip. Longer rows first take the max, then walk the same
+// order four splits per trip.
 __global__ __launch_bounds__(256) void decode_combine_kernel(const int32_t* __restrict__ offs,
                                                               const float* __restrict__ ws_o,
                                                               const float* __restrict__ ws_ml, int hq,
@@ -456,16 +461,16 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const int32_t* __re
   const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int r = tid >> 5, c = tid & 31;
   const int w0 = offs[b], ns = offs[b + 1] - w0;
-  // exact max of the split maxima (max is order-free)
-  float M = -INFINITY;
-  for (int s = tid; s < ns; s += 256) M = fmaxf(M, ws_ml[((int64_t)(w0 + s) * hq + h) * 2]);
-  M = wave_max(M);
-  if ((tid & 63) == 0) red[tid >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-
   float l = 0.0f;
   float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float M = -INFINITY;
+  // exact max of the split maxima (max is order-free) over the workgroup
+  auto wg_max = [&](float v) {
+    v = wave_max(v);
+    if ((tid & 63) == 0) red[tid >> 6] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  };
   auto fold = [&](const float2 ml, const float4 ov) {
     const float w = __builtin_amdgcn_exp2f(ml.x - M);
     l = l + w * ml.y;
@@ -479,20 +484,42 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const int32_t* __re
     ml = *reinterpret_cast<const float2*>(ws_ml + ph * 2);
     ov = *reinterpret_cast<const float4*>(ws_o + ph * HD + 4 * c);
   };
-  int s = r;
-  for (; s + 8 < ns; s += 16) {  // two splits of this group per trip, folded in order
-    float2 ml0, ml1;
-    float4 o0, o1;
-    part(s, ml0, o0);
-    part(s + 8, ml1, o1);
-    fold(ml0, o0);
-    fold(ml1, o1);
-  }
-  if (s < ns) {
-    float2 ml0;
-    float4 o0;
-    part(s, ml0, o0);
-    fold(ml0, o0);
+  // rows of up to 8 * PER splits: all partials in registers, loaded at once
+  // (split indices clamped to the last one, so every load is unconditional)
+  auto in_registers = [&](auto PERC) {
+    constexpr int PER = decltype(PERC)::value;
+    float2 mls[PER];
+    float4 ovs[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) part(min(r + 8 * i, ns - 1), mls[i], ovs[i]);
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) m = fmaxf(m, mls[i].x);  // clamped copies repeat a real split
+    M = wg_max(m);
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (r + 8 * i < ns) fold(mls[i], ovs[i]);
+  };
+  if (ns >= 1 && ns <= 8) {
+    in_registers(std::integral_constant<int, 1>{});
+  } else {
+    for (int s = tid; s < ns; s += 256) M = fmaxf(M, ws_ml[((int64_t)(w0 + s) * hq + h) * 2]);
+    M = wg_max(M);
+    int s = r;
+    for (; s + 24 < ns; s += 32) {  // four splits of this group per trip, folded in order
+      float2 ml[4];
+      float4 ov[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part(s + 8 * i, ml[i], ov[i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fold(ml[i], ov[i]);
+    }
+    for (; s < ns; s += 8) {
+      float2 ml0;
+      float4 o0;
+      part(s, ml0, o0);
+      fold(ml0, o0);
+    }
   }
   po[r][c] = o;
   if (c == 0) pl[r] = l;

@@ -53,6 +53,7 @@
 #include "device_common.h"
 
 #include <numeric>
+#include <type_traits>
 
 namespace bi {
 namespace {
