@@ -365,8 +365,11 @@ __global__ __launch_bounds__(LS_NT) void log_softmax_kernel(const float* __restr
 
   const float mx = tot.m;
   const float lg = __builtin_amdgcn_logf(tot.s) * LN2;  // log2 -> ln
+  // the output streams past the caches (non-temporal stores): it is not read
+  // again here, and the row's chunks left for the second pass stay cached
   auto out4 = [&](int cc, const f32x4 v) {
-    reinterpret_cast<f32x4*>(yr)[cc] = f32x4{(v.x - mx) - lg, (v.y - mx) - lg, (v.z - mx) - lg, (v.w - mx) - lg};
+    __builtin_nontemporal_store(f32x4{(v.x - mx) - lg, (v.y - mx) - lg, (v.z - mx) - lg, (v.w - mx) - lg},
+                                reinterpret_cast<f32x4*>(yr) + cc);
   };
 #pragma unroll
   for (int u = 0; u < LS_REG; ++u)
@@ -383,7 +386,7 @@ __global__ __launch_bounds__(LS_NT) void log_softmax_kernel(const float* __restr
     for (int u = 0; u < U2; ++u) out4(c + u * LS_NT, v[u]);
   }
   for (; c < nch; c += LS_NT) out4(c, xv[c]);
-  if (tid < tail) yr[nch * 4 + tid] = (xr[nch * 4 + tid] - mx) - lg;
+  if (tid < tail) __builtin_nontemporal_store((xr[nch * 4 + tid] - mx) - lg, yr + nch * 4 + tid);
 }
 
 // Chunks-per-lane template choice for one-wave-per-row kernels: a function
