@@ -84,36 +84,41 @@ __global__ __launch_bounds__(64) void qknorm_rope_append_kernel(RopeArgs a) {
   const int nq = a.hq, nk = a.hkv;
   const uint16_t* src = a.qkv + (int64_t)b * a.ldqkv + (int64_t)h * HD;
   const int64_t pos = a.pos[b];
-  int64_t page = -1;
-  if (pos >= 0 && pos < a.max_pos && pos < a.max_pages * a.page) {
-    page = a.bt[(int64_t)b * a.max_pages + pos / a.page];
-    if (page < 0 || page >= a.num_pages) page = -1;
-  }
+  // Out-of-range positions are clamped to 0 for the loads below, which are
+  // then all issued together (no load waits behind a branch); the results
+  // are masked with ok.
+  const bool pos_ok = pos >= 0 && pos < a.max_pos && pos < a.max_pages * a.page;
+  const int64_t pc = pos_ok ? pos : 0;
+  int64_t page = a.bt[(int64_t)b * a.max_pages + pc / a.page];
+  if (!pos_ok || page < 0 || page >= a.num_pages) page = -1;
   const bool ok = page >= 0;
+  const uint16_t s0 = src[l], s1 = src[l + HALF];
+  const bool is_q = h < nq;
+  const uint16_t* w = is_q ? a.qw : a.kw;
+  const uint16_t w0 = w[l], w1 = w[l + HALF];
+  const float cl = a.cos_t[pc * HALF + l], sl = a.sin_t[pc * HALF + l];
+  // keeps the loads above together, ahead of the head-kind branch (the
+  // compiler would otherwise sink the weight and table loads past it and
+  // wait for the row first)
+  asm volatile("" ::"v"(s0), "v"(s1), "v"(w0), "v"(w1), "v"(cl), "v"(sl));
   if (h >= nq + nk) {  // v head: copy
     if (ok) {
       const int g = h - nq - nk;
       // V pages are d-major: [page][kv head][d][slot]
       uint16_t* dst = a.vp + (page * nk + g) * HD * a.page + pos % a.page;
-      dst[(int64_t)l * a.page] = src[l];
-      dst[(int64_t)(l + HALF) * a.page] = src[l + HALF];
+      dst[(int64_t)l * a.page] = s0;
+      dst[(int64_t)(l + HALF) * a.page] = s1;
     }
     return;
   }
-  const bool is_q = h < nq;
-  const uint16_t* w = is_q ? a.qw : a.kw;
-  const float x0 = __uint_as_float(uint32_t(src[l]) << 16);
-  const float x1 = __uint_as_float(uint32_t(src[l + HALF]) << 16);
+  const float x0 = __uint_as_float(uint32_t(s0) << 16);
+  const float x1 = __uint_as_float(uint32_t(s1) << 16);
   float ss = __builtin_fmaf(x0, x0, x1 * x1);
   ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / (float)HD + a.eps);
-  const float t0 = (x0 * r) * __uint_as_float(uint32_t(w[l]) << 16);
-  const float t1 = (x1 * r) * __uint_as_float(uint32_t(w[l + HALF]) << 16);
-  float c = 0.0f, s = 0.0f;
-  if (ok) {
-    c = a.cos_t[pos * HALF + l];
-    s = a.sin_t[pos * HALF + l];
-  }
+  const float t0 = (x0 * r) * __uint_as_float(uint32_t(w0) << 16);
+  const float t1 = (x1 * r) * __uint_as_float(uint32_t(w1) << 16);
+  const float c = ok ? cl : 0.0f, s = ok ? sl : 0.0f;
   const float o0 = t0 * c - t1 * s;
   const float o1 = t1 * c + t0 * s;
   const uint16_t b0 = (uint16_t)f32_to_bf16_rne(o0), b1 = (uint16_t)f32_to_bf16_rne(o1);

@@ -75,11 +75,27 @@ __global__ __launch_bounds__(64) void rmsnorm_kernel(uint16_t* __restrict__ x, i
   u32x4 wcache[CPT > 0 ? CPT : 1];  // the weight chunks, fetched with x (no second round trip)
   float ss = 0.0f;
   if constexpr (CPT > 0) {
+    // Every load is unconditional (chunk index clamped to the row's last
+    // chunk, the result masked afterwards): a load whose value feeds the add
+    // under a per-chunk branch is waited for at the branch's join, which
+    // made each chunk a round trip of its own.
+    u32x4 xv[CPT], dv[CPT];
+    if (nch > 0) {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int cc = min(lane + 64 * i, nch - 1);
+        xv[i] = reinterpret_cast<const u32x4*>(xr)[cc];
+        if constexpr (ADD) dv[i] = reinterpret_cast<const u32x4*>(dr)[cc];
+        wcache[i] = reinterpret_cast<const u32x4*>(w)[cc];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = lane + 64 * i;
-      cache[i] = c < nch ? chunk(c) : u32x4{0u, 0u, 0u, 0u};
-      wcache[i] = c < nch ? reinterpret_cast<const u32x4*>(w)[c] : u32x4{0u, 0u, 0u, 0u};
+      const bool ok = lane + 64 * i < nch;
+      u32x4 v = xv[i];
+      if constexpr (ADD) v = add_bf16x8(v, dv[i]);
+      cache[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+      if (!ok) wcache[i] = u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
