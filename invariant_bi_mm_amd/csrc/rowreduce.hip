@@ -387,12 +387,8 @@ __global__ __launch_bounds__(LS_NT) void log_softmax_kernel(const float* __restr
     __builtin_nontemporal_store(f32x4{(v.x - mx) - lg, (v.y - mx) - lg, (v.z - mx) - lg, (v.w - mx) - lg},
                                 reinterpret_cast<f32x4*>(yr) + cc);
   };
-#pragma unroll
-  for (int u = 0; u < LS_REG; ++u)
-    if (tid + u * LS_NT < nch) out4(tid + u * LS_NT, r[u]);
-#pragma unroll
-  for (int u = 0; u < LS_KEEP; ++u)
-    if (tid + (LS_REG + u) * LS_NT < nch) out4(tid + (LS_REG + u) * LS_NT, keep[u][tid]);
+  // the re-read part first, while the end of pass 1 may still hold it in
+  // the caches; then the chunks kept in registers and LDS
   constexpr int U2 = 4;
   for (c = tid + (LS_REG + LS_KEEP) * LS_NT; c + (U2 - 1) * LS_NT < nch; c += U2 * LS_NT) {
     f32x4 v[U2];
@@ -402,6 +398,12 @@ __global__ __launch_bounds__(LS_NT) void log_softmax_kernel(const float* __restr
     for (int u = 0; u < U2; ++u) out4(c + u * LS_NT, v[u]);
   }
   for (; c < nch; c += LS_NT) out4(c, xv[c]);
+#pragma unroll
+  for (int u = 0; u < LS_REG; ++u)
+    if (tid + u * LS_NT < nch) out4(tid + u * LS_NT, r[u]);
+#pragma unroll
+  for (int u = 0; u < LS_KEEP; ++u)
+    if (tid + (LS_REG + u) * LS_NT < nch) out4(tid + (LS_REG + u) * LS_NT, keep[u][tid]);
   if (tid < tail) __builtin_nontemporal_store((xr[nch * 4 + tid] - mx) - lg, yr + nch * 4 + tid);
 }
 
