@@ -728,8 +728,8 @@ static GemmConfig skinny_config(int64_t m, int64_t strips) {
   return GemmConfig{64, 32, TK, 4};
 }
 
-// The configuration table. Every configuration -- skinny, 128x128, 256x256
-// -- computes each output element with the same chain (one 32x32x16 MFMA per
+// The configuration table. Every configuration -- skinny, 64x128, 128x128,
+// 256x256 -- computes each output element with the same chain (one 32x32x16 MFMA per
 // 16 k, increasing k, fp32, k padded to a multiple of 64, the same
 // epilogue), so the choice moves work between workgroups without changing
 // any bit, and it may depend on M: the result of a row still does not depend
@@ -740,6 +740,11 @@ static GemmConfig skinny_config(int64_t m, int64_t strips) {
 //     faster than 128x128 (N = 4096, 6144, K = 4096 and 12288), 1.25-1.6x
 //     at N = 24576; at the 151936-wide LM head both stream at ~5.4 TB/s and
 //     128x128 is kept;
+//   * the same deep ring with a 64x128 tile (1x2 consumer waves of 64x64,
+//     6 stages) for M > 64 while 128x128 tiles would fill at most half the
+//     CUs and the 64x128 ones still fit one round: 6-14 % faster than the
+//     128x128 ring at M = 128-512 for N = 4096 (K = 4096 and 12288) and
+//     3-5 % for N = 6144 at M <= 256;
 //   * the same deep ring with a 128x128 tile (2x2 consumer waves of 64x64)
 //     for M > 64 while its tiles fit one round over the CUs: 1.15-1.35x
 //     faster than 128x128 or skinny at M = 128-1024, 1.6x than 256x256 at
@@ -753,7 +758,9 @@ GemmConfig gemm_config(int64_t m, int64_t n, int64_t k, bool b_is_nk) {
   (void)b_is_nk;
   const int64_t strips = (n + 31) / 32;
   if (m <= 64 && n <= 32768) return skinny_config(m, strips);
-  if (m > 64 && ((m + 127) / 128) * ((n + 127) / 128) <= 256) return GemmConfig{128, 128, TK, 6};
+  const int64_t t128 = ((m + 127) / 128) * ((n + 127) / 128);
+  if (m > 64 && t128 <= 128 && ((m + 63) / 64) * ((n + 127) / 128) <= 256) return GemmConfig{64, 128, TK, 4};
+  if (m > 64 && t128 <= 256) return GemmConfig{128, 128, TK, 6};
   const int64_t t256 = ((m + 255) / 256) * ((n + 255) / 256);
   const int64_t rounds = (t256 + 255) / 256;  // one 256x256 workgroup per CU
   if (m >= 192 && t256 >= 192 && 10 * t256 >= 7 * rounds * 256) return GemmConfig{256, 256, TK, 8};
@@ -807,6 +814,8 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   }
   if (cfg.tile_m == 128 && cfg.tile_n == 128 && cfg.waves == 6)  // 2x2 consumers of 64x64, 4-stage ring
     return p.b_is_nk ? launch_ring<2, 2, 2, 2, 2, 4, true>(a, s) : launch_ring<2, 2, 2, 2, 2, 4, false>(a, s);
+  if (cfg.tile_m == 64 && cfg.tile_n == 128)  // 1x2 consumers of 64x64, 6-stage ring
+    return p.b_is_nk ? launch_ring<1, 2, 2, 2, 2, 6, true>(a, s) : launch_ring<1, 2, 2, 2, 2, 6, false>(a, s);
   if (cfg.tile_m == 256 && cfg.tile_n == 256) {
     const int64_t n1 = full_round_columns(a.tiles_m, a.tiles_n, p.m, p.n);
     if (n1 < a.tiles_n) {

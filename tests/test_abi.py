@@ -251,9 +251,10 @@ def test_gemm_config_table(bi):
             for nk in (False, True):
                 cfg = bi.bi_gemm_config(m, n, k, nk)
                 assert cfg == bi.bi_gemm_config(m, n, k, nk)
-                assert cfg in {(32, 32, 64, 3), (64, 32, 64, 4), (128, 128, 64, 6), (128, 128, 64, 4), (256, 256, 64, 8)}, cfg
+                assert cfg in {(32, 32, 64, 3), (64, 32, 64, 4), (64, 128, 64, 4), (128, 128, 64, 6), (128, 128, 64, 4),
+                               (256, 256, 64, 8)}, cfg
                 seen.add(cfg)
-    assert len(seen) == 5
+    assert len(seen) == 6
     # small batches of the projection shapes take the skinny tiles, M = 4096 a full-width one
     assert bi.bi_gemm_config(1, 4096, 4096)[1] == 32 and bi.bi_gemm_config(64, 4096, 12288)[1] == 32
     assert bi.bi_gemm_config(4096, 4096, 4096)[1] == 256 and bi.bi_gemm_config(1, 151936, 4096)[1] == 128

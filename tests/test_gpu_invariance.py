@@ -116,15 +116,15 @@ def test_mm_adversarial_other_rows(lib, fill):
             assert same_bits(lib.bi_mm(x, w)[pos], ref), (fill, m, pos)
 
 
-ALL_CONFIGS = {(32, 32, 64, 3), (64, 32, 64, 4), (128, 128, 64, 6), (128, 128, 64, 4), (256, 256, 64, 8)}
+ALL_CONFIGS = {(32, 32, 64, 3), (64, 32, 64, 4), (64, 128, 64, 4), (128, 128, 64, 6), (128, 128, 64, 4), (256, 256, 64, 8)}
 
 
 @pytest.mark.parametrize("b_is_nk", [False, True])
 @pytest.mark.parametrize("n", [4096, 6144])
 def test_mm_every_tile_configuration_same_bits(lib, b_is_nk, n):
     """A row's addmm output is the same, bit for bit, at an M of each tile
-    configuration the shape takes (skinny 32 or 64 rows, the 128x128 ring,
-    128x128, 256x256), at the first and last row, for fp32 and bf16
+    configuration the shape takes (skinny 32 or 64 rows, the 64x128 and
+    128x128 rings, 128x128, 256x256), at the first and last row, for fp32 and bf16
     outputs and a ragged K (a 64-tail) -- and it matches the oracle."""
     k = 1032
     first = {}
