@@ -1,6 +1,6 @@
 """One greedy decode step of a Qwen3-style model, end to end on the library.
 
-The pages judge batch invariance by a token stream: temperature-0
+The pages assess batch invariance by a token stream: temperature-0
 completions of one prompt that agree for a long prefix and then fork,
 because the batch a request lands in changes the kernels' reduction order
 (readhandoff.com, agent-run reproducibility pinning, sections "What does
