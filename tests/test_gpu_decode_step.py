@@ -59,6 +59,21 @@ def test_add_rmsnorm_parity(lib, m, n):
     assert same_bits(yb.cpu(), y.cpu().to(torch.bfloat16)) and same_bits(x1, x)
 
 
+
+def test_add_rmsnorm_row_shorter_than_a_chunk(lib):
+    """n < 8: the row has no full 16-byte chunk, only the tail (rows padded to
+    a stride of 8, as the alignment rule asks)."""
+    m, n, ld = 3, 5, 8
+    say("add_rmsnorm n=5")
+    x = S.normal_bf16((m, ld), 1.0, seed=731, device=DEV)[:, :n]
+    d = S.normal_bf16((m, ld), 1.0, seed=732, device=DEV)[:, :n]
+    w = S.uniform_bf16((ld,), 0.5, 1.5, seed=733, device=DEV)[:n]
+    x0 = x.clone()
+    y = lib.bi_add_rmsnorm(x, d, w, 1e-6, out_dtype=torch.float32, out=torch.empty((m, ld), device=DEV)[:, :n])
+    want_x = (x0.cpu().float() + d.cpu().float()).to(torch.bfloat16)
+    assert same_bits(x.cpu(), want_x)
+    assert_close(f32(y), O.add_rmsnorm(bits(x0), bits(d), bits(w), 1e-6)[1], "add_rmsnorm n=5 vs oracle")
+
 def test_embed_is_an_exact_gather(lib):
     table = S.normal_bf16((1000, 4096), 1.0, seed=730, device=DEV)
     tok = torch.tensor([5, 999, 0, 5, -3, 1000, 123], dtype=torch.int64, device=DEV)

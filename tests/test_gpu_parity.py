@@ -173,7 +173,7 @@ def test_rmsnorm(lib, m):
     assert O.elementwise_ratio(f32(yb.float()), ref) <= 4e-3
 
 
-@pytest.mark.parametrize("n", [4100, 8, 13, 20000, 4096 * 5])
+@pytest.mark.parametrize("n", [4100, 5, 8, 13, 20000, 4096 * 5])
 def test_rmsnorm_other_widths(lib, n):
     """Widths with a tail (n % 8 != 0), tiny rows and rows past the register
     cache (streaming variant)."""
