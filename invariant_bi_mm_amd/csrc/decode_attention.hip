@@ -441,98 +441,103 @@ __global__ __launch_bounds__(256) void prefill_split_kernel(PrefillArgs a) {
   }
 }
 
-// Combine: one workgroup of 256 threads per (sequence, query head), as 8
-// groups of 32 lanes; lane c of a group owns o[4c .. 4c+3]. Group r folds the
-// splits s = r, r + 8, r + 16, ... in increasing order (m, l, o weighted by
-// 2^(m_s - M)); the 8 group sums are then added as
+// Combine: one workgroup of two waves per (sequence, query head). The split
+// partials are folded in 8 groups: group g takes the splits s = g, g + 8,
+// g + 16, ... in increasing order (m, l, o weighted by 2^(m_s - M), M the
+// exact max of the split maxima), and the 8 group sums are added as
 // ((g0 + g1) + (g2 + g3)) + ((g4 + g5) + (g6 + g7)). The order depends only on
-// the sequence's split count. A row of up to 8 splits (a context of up to
-// 2048 tokens; every prefill row of a short prompt) loads its partials at
-// once, one per group, and takes the exact max from the loaded values: one
-// memory round trip. Longer rows first take the max, then walk the same
-// order four splits per trip.
-__global__ __launch_bounds__(256) void decode_combine_kernel(const int32_t* __restrict__ offs,
+// the sequence's split count. The 32-lane quarter q of the workgroup holds
+// groups q and q + 4, lane c owning o[4c .. 4c+3]; the tree's first level
+// pairs quarters inside a wave, the second goes through LDS. A row of up to
+// 8 splits (a context of up to 2048 tokens; almost every prefill row) loads
+// its partials at once and takes the max from the loaded values: one memory
+// round trip. Longer rows first take the max, then fold 32 splits per trip.
+// Two waves per row keep 12 rows per CU in flight (76 VGPRs).
+__global__ __launch_bounds__(128) void decode_combine_kernel(const int32_t* __restrict__ offs,
                                                               const float* __restrict__ ws_o,
                                                               const float* __restrict__ ws_ml, int hq,
                                                               void* __restrict__ out, int out_bf16) {
-  __shared__ float red[4];
-  __shared__ float4 po[8][HD / 4];
-  __shared__ float pl[8];
+  __shared__ float red[2];
+  __shared__ float4 po[2][HD / 4];
+  __shared__ float pl[2];
   const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int r = tid >> 5, c = tid & 31;
+  const int pg = tid >> 5, c = tid & 31, wv = tid >> 6;
   const int w0 = offs[b], ns = offs[b + 1] - w0;
-  float l = 0.0f;
-  float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float l[2] = {0.0f, 0.0f};
+  float4 o[2] = {make_float4(0.0f, 0.0f, 0.0f, 0.0f), make_float4(0.0f, 0.0f, 0.0f, 0.0f)};
   float M = -INFINITY;
-  // exact max of the split maxima (max is order-free) over the workgroup
   auto wg_max = [&](float v) {
     v = wave_max(v);
-    if ((tid & 63) == 0) red[tid >> 6] = v;
+    if ((tid & 63) == 0) red[wv] = v;
     __syncthreads();
-    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  };
-  auto fold = [&](const float2 ml, const float4 ov) {
-    const float w = __builtin_amdgcn_exp2f(ml.x - M);
-    l = l + w * ml.y;
-    o.x = o.x + w * ov.x;
-    o.y = o.y + w * ov.y;
-    o.z = o.z + w * ov.z;
-    o.w = o.w + w * ov.w;
+    return fmaxf(red[0], red[1]);
   };
   auto part = [&](int s, float2& ml, float4& ov) {
     const int64_t ph = (int64_t)(w0 + s) * hq + h;
     ml = *reinterpret_cast<const float2*>(ws_ml + ph * 2);
     ov = *reinterpret_cast<const float4*>(ws_o + ph * HD + 4 * c);
   };
-  // rows of up to 8 * PER splits: all partials in registers, loaded at once
-  // (split indices clamped to the last one, so every load is unconditional)
-  auto in_registers = [&](auto PERC) {
-    constexpr int PER = decltype(PERC)::value;
-    float2 mls[PER];
-    float4 ovs[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) part(min(r + 8 * i, ns - 1), mls[i], ovs[i]);
-    float m = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) m = fmaxf(m, mls[i].x);  // clamped copies repeat a real split
-    M = wg_max(m);
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (r + 8 * i < ns) fold(mls[i], ovs[i]);
+  auto fold = [&](int j, const float2 ml, const float4 ov) {
+    const float w = __builtin_amdgcn_exp2f(ml.x - M);
+    l[j] = l[j] + w * ml.y;
+    o[j].x = o[j].x + w * ov.x;
+    o[j].y = o[j].y + w * ov.y;
+    o[j].z = o[j].z + w * ov.z;
+    o[j].w = o[j].w + w * ov.w;
   };
   if (ns >= 1 && ns <= 8) {
-    in_registers(std::integral_constant<int, 1>{});
+    float2 mls[2];
+    float4 ovs[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) part(min(pg + 4 * j, ns - 1), mls[j], ovs[j]);
+    M = wg_max(fmaxf(mls[0].x, mls[1].x));
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (pg + 4 * j < ns) fold(j, mls[j], ovs[j]);
   } else {
-    for (int s = tid; s < ns; s += 256) M = fmaxf(M, ws_ml[((int64_t)(w0 + s) * hq + h) * 2]);
-    M = wg_max(M);
-    int s = r;
-    for (; s + 24 < ns; s += 32) {  // four splits of this group per trip, folded in order
-      float2 ml[4];
-      float4 ov[4];
+    float m = -INFINITY;
+    for (int s = tid; s < ns; s += 128) m = fmaxf(m, ws_ml[((int64_t)(w0 + s) * hq + h) * 2]);
+    M = wg_max(m);
+    for (int t0 = 0; t0 < ns; t0 += 32) {  // splits t0 .. t0 + 31: four per group, in order
+      float2 mls[4][2];
+      float4 ovs[4][2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part(s + 8 * i, ml[i], ov[i]);
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fold(ml[i], ov[i]);
-    }
-    for (; s < ns; s += 8) {
-      float2 ml0;
-      float4 o0;
-      part(s, ml0, o0);
-      fold(ml0, o0);
+        for (int j = 0; j < 2; ++j) part(min(t0 + 8 * u + pg + 4 * j, ns - 1), mls[u][j], ovs[u][j]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          if (t0 + 8 * u + pg + 4 * j < ns) fold(j, mls[u][j], ovs[u][j]);
     }
   }
-  po[r][c] = o;
-  if (c == 0) pl[r] = l;
-  __syncthreads();
-  if (tid < HD / 4) {
-    float4 t[8];
+  // wave 0 holds groups 0, 1, 4, 5, wave 1 groups 2, 3, 6, 7
+  float lt[2];
+  float4 ot[2];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) t[q] = po[q][tid];
+  for (int j = 0; j < 2; ++j) {  // g(4j + 2wv) + g(4j + 2wv + 1)
+    lt[j] = l[j] + xor_shfl(l[j], 32);
+    ot[j].x = o[j].x + xor_shfl(o[j].x, 32);
+    ot[j].y = o[j].y + xor_shfl(o[j].y, 32);
+    ot[j].z = o[j].z + xor_shfl(o[j].z, 32);
+    ot[j].w = o[j].w + xor_shfl(o[j].w, 32);
+  }
+  if (wv == 1 && (tid & 63) < 32) {
+    po[0][c] = ot[0];
+    po[1][c] = ot[1];
+    if (c == 0) {
+      pl[0] = lt[0];
+      pl[1] = lt[1];
+    }
+  }
+  __syncthreads();
+  if (tid < 32) {
     auto add = [](float4 x, float4 y) { return make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w); };
-    const float4 os = add(add(add(t[0], t[1]), add(t[2], t[3])), add(add(t[4], t[5]), add(t[6], t[7])));
-    const float ls = ((pl[0] + pl[1]) + (pl[2] + pl[3])) + ((pl[4] + pl[5]) + (pl[6] + pl[7]));
+    const float4 os = add(add(ot[0], po[0][c]), add(ot[1], po[1][c]));
+    const float ls = (lt[0] + pl[0]) + (lt[1] + pl[1]);
     const float res[4] = {os.x / ls, os.y / ls, os.z / ls, os.w / ls};
-    const int64_t at = ((int64_t)b * hq + h) * HD + 4 * tid;
+    const int64_t at = ((int64_t)b * hq + h) * HD + 4 * c;
     // element stores: out need only be aligned to its element size
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -564,7 +569,7 @@ hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t s) {
   hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)(p.total_splits * p.num_kv_heads)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)p.batch, (unsigned)p.num_q_heads), dim3(256), 0, s,
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)p.batch, (unsigned)p.num_q_heads), dim3(128), 0, s,
                      p.split_offsets, p.ws_o, p.ws_ml, p.num_q_heads, p.out, p.out_bf16 ? 1 : 0);
   return hipGetLastError();
 }
@@ -587,7 +592,7 @@ hipError_t launch_prefill_attention(const PrefillParams& p, hipStream_t s) {
   hipLaunchKernelGGL(prefill_split_kernel, dim3((unsigned)(p.n_work * p.num_kv_heads)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)p.n_rows, (unsigned)p.num_q_heads), dim3(256), 0, s,
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)p.n_rows, (unsigned)p.num_q_heads), dim3(128), 0, s,
                      p.q_offsets, p.ws_o, p.ws_ml, p.num_q_heads, p.out, p.out_bf16 ? 1 : 0);
   return hipGetLastError();
 }
