@@ -13,7 +13,9 @@ struct GemmConfig {
   int tile_m, tile_n, tile_k, waves;
 };
 
-// Tile configuration for (n, k, layout): a pure function of those three.
+// Tile configuration for (m, n, k, layout): a pure function of those four.
+// Every configuration computes each element with the same chain, so the
+// choice never changes a bit (see gemm.hip).
 GemmConfig gemm_config(int64_t m, int64_t n, int64_t k, bool b_is_nk);
 
 struct GemmParams {
