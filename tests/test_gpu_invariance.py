@@ -172,12 +172,13 @@ def full_round_columns(m, n):
 
 
 @pytest.mark.parametrize("b_is_nk", [False, True])
-@pytest.mark.parametrize("m,k,n,slab", [(4096, 1032, 6144, 2048), (256, 4096, 151936, 131072)])
+@pytest.mark.parametrize("m,k,n,slab", [(4096, 1032, 6144, 2048), (4096, 1032, 6136, 2048), (256, 4096, 151936, 131072)])
 def test_mm_column_split_same_bits(lib, b_is_nk, m, k, n, slab):
     """A 256x256 GEMM whose last round over the CUs would be part-empty runs
-    its leftover columns as 256x128 tiles. Each column block of its output
-    must have the bits of the same block computed on its own (no split), for
-    fp32 and bf16 outputs with a bias, and sampled rows match the oracle."""
+    its leftover columns as 256x128 tiles (N = 6136: the last of them ragged,
+    120 columns). Each column block of its output must have the bits of the
+    same block computed on its own (no split), for fp32 and bf16 outputs with
+    a bias, and sampled rows match the oracle."""
     assert lib.bi_gemm_config(m, n, k, b_is_nk)[:2] == (256, 256)
     assert full_round_columns(m, n) * 256 < n, "shape does not split"
     w = S.normal_bf16((n, k) if b_is_nk else (k, n), 1 / k, seed=81, device=DEV)
