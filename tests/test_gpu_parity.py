@@ -160,7 +160,7 @@ def test_addmm_lm_head_then_log_softmax(lib):
 
 
 # ------------------------------------------------------------------ reductions
-@pytest.mark.parametrize("m", [1, 7, 64, 513])
+@pytest.mark.parametrize("m", [1, 7, 64, 513, 2048])
 def test_rmsnorm(lib, m):
     say(f"rmsnorm m={m}")
     x = S.normal_bf16((m, 4096), 1.0, seed=60 + m).to(DEV)
@@ -196,7 +196,7 @@ def test_rmsnorm_constant_rows(lib):
     assert_close(f32(y), O.rmsnorm(bits(x), bits(w), 1e-6), "rmsnorm const")
 
 
-@pytest.mark.parametrize("m", [1, 7, 64, 513])
+@pytest.mark.parametrize("m", [1, 7, 64, 513, 2048])
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
 def test_mean(lib, m, dt):
     say(f"mean m={m} {dt}")
@@ -229,6 +229,19 @@ def test_log_softmax(lib, m):
     s = np.exp(f32(y).astype(np.float64)).sum(axis=1)
     assert np.all(np.abs(s - 1.0) < 1e-4)
 
+
+
+def test_log_softmax_benchmark_size_sampled(lib):
+    """The benchmark's 2048 x 151936 log_softmax + argmax (its inputs, same
+    seed and launch), sampled rows against the oracle."""
+    say("log_softmax 2048 x 151936")
+    x = S.normal_f32((2048, 151936), 4.0, seed=1002, device=DEV)
+    y, am = lib.bi_log_softmax(x)
+    rows = [0, 1, 777, 1024, 2047]
+    xc = f32(x[rows])
+    assert_close(f32(y[rows]), O.log_softmax(xc), "log_softmax 2048 rows")
+    assert am[rows].cpu().tolist() == O.argmax(xc).tolist()
+    del x, y
 
 def test_log_softmax_edges(lib):
     say("log_softmax edges")
@@ -301,3 +314,19 @@ def test_decode_attention_config_batch(lib):
     seqs = [0, 1, int(torch.argmax(lens_t)), int(torch.argmin(lens_t)), 63]
     ref = O.decode_attention(bits(q), bits(kp), bits(vp), table.numpy(), lens_t.numpy(), 128 ** -0.5, seqs=seqs)
     assert_close(f32(out[seqs]), ref[seqs], "decode batch")
+
+
+def test_decode_attention_benchmark_batch_sampled(lib):
+    """The benchmark's decode attention (B = 256, lengths log-uniform in
+    [1, 32768], its seeds and launch), sampled sequences against the oracle."""
+    lens_t = S.context_lens(256, seed=5000)
+    say("decode batch256 total tokens", int(lens_t.sum()))
+    table, npages = S.paged_kv_layout(lens_t, 16, seed=5001)
+    q = S.normal_bf16((256, 32, 128), 1.0, seed=5002, device=DEV)
+    kp = S.normal_bf16((npages, 8, 16, 128), 1.0, seed=5003, device=DEV)
+    vp = S.normal_bf16((npages, 8, 128, 16), 1.0, seed=5004, device=DEV)  # d-major, as the benchmark draws it
+    offs, total = lib.bi_decode_plan(lens_t)
+    out = lib.bi_decode_attention(q, kp, vp, table.to(DEV), lens_t.to(DEV), offs.to(DEV), total)
+    seqs = [0, 100, int(torch.argmax(lens_t)), int(torch.argmin(lens_t)), 255]
+    ref = O.decode_attention(bits(q), bits(kp), bits(vp), table.numpy(), lens_t.numpy(), 128 ** -0.5, seqs=seqs)
+    assert_close(f32(out[seqs]), ref[seqs], "decode batch 256")
