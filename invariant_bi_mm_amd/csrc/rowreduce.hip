@@ -304,13 +304,16 @@ __global__ __launch_bounds__(LS_NT) void log_softmax_kernel(const float* __restr
   };
 
   // The first LS_REG chunks of this thread, all loads in flight together,
-  // folded in increasing chunk order and kept in registers for pass 2.
+  // folded in increasing chunk order and kept in registers for pass 2. The
+  // chunks kept on chip (registers, LDS) are loaded non-temporal: they are
+  // not read from memory again, and the caches keep more of the part that
+  // pass 2 re-reads.
   const f32x4* xv = reinterpret_cast<const f32x4*>(xr);
   f32x4 r[LS_REG];
 #pragma unroll
   for (int u = 0; u < LS_REG; ++u) {
     const int cc = tid + u * LS_NT;
-    r[u] = cc < nch ? xv[cc] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    r[u] = cc < nch ? __builtin_nontemporal_load(xv + cc) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 #pragma unroll
   for (int u = 0; u < LS_REG; ++u)
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(LS_NT) void log_softmax_kernel(const float* __restr
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
       const int cc = tid + (LS_REG + u0 + u) * LS_NT;
-      v[u] = cc < nch ? xv[cc] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      v[u] = cc < nch ? __builtin_nontemporal_load(xv + cc) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
