@@ -338,8 +338,8 @@ __global__ __launch_bounds__(LS_NT) void log_softmax_kernel(const float* __restr
       }
     }
   }
-  // the rest of the row, four 16-byte loads in flight per thread
-  constexpr int U = 4;
+  // the rest of the row, six 16-byte loads in flight per thread (eight spill)
+  constexpr int U = 6;
   int c = tid + (LS_REG + LS_KEEP) * LS_NT;
   for (; c + (U - 1) * LS_NT < nch; c += U * LS_NT) {
     f32x4 v[U];
@@ -392,7 +392,7 @@ __global__ __launch_bounds__(LS_NT) void log_softmax_kernel(const float* __restr
   };
   // the re-read part first, while the end of pass 1 may still hold it in
   // the caches; then the chunks kept in registers and LDS
-  constexpr int U2 = 4;
+  constexpr int U2 = 6;
   for (c = tid + (LS_REG + LS_KEEP) * LS_NT; c + (U2 - 1) * LS_NT < nch; c += U2 * LS_NT) {
     f32x4 v[U2];
 #pragma unroll
