@@ -124,7 +124,6 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, const void*
 
 template <int TM, int TN, int WM, int WN, bool B_NK>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
-  constexpr int NT = WM * WN * 64;
   constexpr int WTM = TM / WM, WTN = TN / WN;  // wave tile
   constexpr int FM = WTM / 32, FN = WTN / 32;  // 32x32 MFMA tiles per wave
   // LDS stages. A (and B stored [N,K]): rows of 64 bf16 = eight 16-byte
