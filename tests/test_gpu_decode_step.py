@@ -16,7 +16,7 @@ import torch
 
 import oracle as O
 import synthetic as S
-from helpers import ELEM_TOL, assert_close, bits, d_major, f32, same_bits
+from helpers import ELEM_TOL, assert_close, bits, f32, same_bits
 from oracle.decode_step import OracleDecoder
 
 pytestmark = pytest.mark.gpu
