@@ -159,6 +159,26 @@ def test_addmm_lm_head_then_log_softmax(lib):
     assert am[rows].cpu().tolist() == O.argmax(lg).tolist()
 
 
+def test_addmm_lm_head_benchmark_size_sampled(lib):
+    """The benchmark's LM head (X[256,4096], W[4096,151936], bias; its seeded
+    inputs) in its own launch configuration: at M = 256 the first 131072
+    columns run on 256x256 tiles and the rest on 256x128 tiles, so the
+    sampled columns come from both parts."""
+    m, k, n, split = 256, 4096, 151936, 131072
+    say("lm head 256 x 151936")
+    x = S.normal_bf16((m, k), 1.0, seed=4000, device=DEV)
+    w = S.normal_bf16((k, n), 0.02, seed=4001, device=DEV)
+    bias = S.normal_bf16((n,), 0.1, seed=4002, device=DEV)
+    logits = lib.bi_addmm(bias, x, w)
+    rows = [0, 101, 255]
+    g = np.random.default_rng(1)
+    cols = np.unique(np.concatenate([g.choice(split, 1024, replace=False),
+                                     split + g.choice(n - split, 1024, replace=False), [split - 1, split, n - 1]]))
+    colst = torch.from_numpy(cols).to(DEV)
+    ref = O.addmm(bits(bias[colst]), bits(x[rows]), bits(w[:, colst]))
+    assert_close(f32(logits[rows][:, colst]), ref, "lm head 256 rows")
+
+
 # ------------------------------------------------------------------ reductions
 @pytest.mark.parametrize("m", [1, 7, 64, 513, 2048])
 def test_rmsnorm(lib, m):
