@@ -214,7 +214,13 @@ size_t bi_decode_workspace_bytes(int64_t total_splits, int num_q_heads, int head
  * num_kv_heads >= 1. Device-side contents (lengths, table entries, offsets)
  * are the caller's responsibility: the host cannot read them without a
  * synchronisation, which this call never performs.
+ *   flags         0, or BI_DECODE_STREAM_KV: load K and V non-temporal, a
+ *                 cache hint only (the results are the same bits). Measured
+ *                 on MI355X it makes this call alone 1-5 % slower but a
+ *                 decode step whose other kernels keep their cache lines
+ *                 ~3 % faster. Any other bit: BI_ERR_UNSUPPORTED.
  */
+#define BI_DECODE_STREAM_KV 1
 bi_status bi_decode_attention(const void* q, const void* k_pages, const void* v_pages,
                               const int32_t* block_table, int64_t max_pages,
                               const int32_t* context_lens, const int32_t* split_offsets,
@@ -222,7 +228,7 @@ bi_status bi_decode_attention(const void* q, const void* k_pages, const void* v_
                               int num_q_heads, int num_kv_heads, int head_dim,
                               int page_size, int split_tokens, float scale,
                               void* workspace, size_t workspace_bytes,
-                              void* out, bi_dtype out_dtype, hipStream_t stream);
+                              void* out, bi_dtype out_dtype, int flags, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Prefill / extend attention with the decode split structure.

@@ -59,7 +59,7 @@ lib.bi_decode_plan.restype = _i64
 lib.bi_decode_workspace_bytes.argtypes = [_i64, _i32, _i32]
 lib.bi_decode_workspace_bytes.restype = _sz
 lib.bi_decode_attention.argtypes = [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
-                                    _f32, _vp, _sz, _vp, _i32, _vp]
+                                    _f32, _vp, _sz, _vp, _i32, _i32, _vp]
 lib.bi_decode_attention.restype = _st
 lib.bi_add_rmsnorm.argtypes = [_vp, _i64, _vp, _i64, _vp, _f32, _vp, _i64, _i32, _i64, _i64, _vp]
 lib.bi_add_rmsnorm.restype = _st
@@ -253,8 +253,10 @@ def v_pages_shape(k_pages) -> tuple:
 
 def bi_decode_attention(q, k_pages, v_pages, block_table, context_lens, split_offsets, total_splits: int, *,
                         scale: float | None = None, split_tokens: int = 256, workspace=None, out=None,
-                        out_dtype: torch.dtype = torch.float32, stream=None):
+                        out_dtype: torch.dtype = torch.float32, stream_kv: bool = False, stream=None):
     """Split-KV decode attention over a paged cache.
+
+    stream_kv loads K and V non-temporal (a cache hint; same bits).
 
     q [B, Hq, D] bf16; k_pages [P, Hkv, page, D] and v_pages [P, Hkv, D, page]
     (d-major) bf16; block_table
@@ -283,7 +285,7 @@ def bi_decode_attention(q, k_pages, v_pages, block_table, context_lens, split_of
     _check(lib.bi_decode_attention(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), block_table.shape[1],
                                    _ptr(context_lens), _ptr(split_offsets), int(total_splits), bsz, hq, hkv, d,
                                    page, int(split_tokens), float(scale), _ptr(workspace), workspace.numel(),
-                                   _ptr(out), _dtype_code(out.dtype), _stream(stream)))
+                                   _ptr(out), _dtype_code(out.dtype), 1 if stream_kv else 0, _stream(stream)))
     return out
 
 

@@ -210,8 +210,9 @@ bi_status bi_decode_attention(const void* q, const void* k_pages, const void* v_
                               int64_t max_pages, const int32_t* context_lens, const int32_t* split_offsets,
                               int64_t total_splits, int64_t batch, int num_q_heads, int num_kv_heads, int head_dim,
                               int page_size, int split_tokens, float scale, void* workspace, size_t workspace_bytes,
-                              void* out, bi_dtype out_dtype, hipStream_t stream) {
+                              void* out, bi_dtype out_dtype, int flags, hipStream_t stream) {
   if (batch < 0 || total_splits < 0 || max_pages < 0) return fail(BI_ERR_SHAPE, "negative size");
+  if ((flags & ~BI_DECODE_STREAM_KV) != 0) return fail(BI_ERR_UNSUPPORTED, "unknown flags 0x%x", (unsigned)flags);
   if (!valid_dtype(out_dtype)) return fail(BI_ERR_DTYPE, "out_dtype %d is not BI_BF16 or BI_F32", (int)out_dtype);
   if (head_dim != 128 || page_size != 16 || split_tokens != 256 || num_kv_heads < 1 ||
       num_q_heads != 4 * num_kv_heads)
@@ -254,6 +255,7 @@ bi_status bi_decode_attention(const void* q, const void* k_pages, const void* v_
   p.ws_ml = p.ws_o + total_splits * num_q_heads * head_dim;
   p.out = out;
   p.out_bf16 = out_dtype == BI_BF16;
+  p.stream_kv = (flags & BI_DECODE_STREAM_KV) != 0;
   return hip_status(bi::launch_decode_attention(p, stream), "decode attention launch");
 }
 

@@ -57,6 +57,7 @@ struct DecodeParams {
   float* ws_ml;  // [total_splits, num_q_heads, 2]
   void* out;
   bool out_bf16;
+  bool stream_kv;  // K/V loaded non-temporal
 };
 hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t stream);
 

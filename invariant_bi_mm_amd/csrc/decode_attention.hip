@@ -84,6 +84,8 @@ struct SplitArgs {
 // tile kt being slots 0..15 of page 4 w + kt. The MFMA B operand of a 32-wide
 // d step (lane l: key l % 16, d 8 (l / 16) .. +7) is one 16-byte load of the
 // key row.
+// NT: non-temporal loads (the BI_DECODE_STREAM_KV hint of bi_decode_attention).
+template <bool NT>
 __device__ __forceinline__ void load_k_frags(const uint16_t* kp, const int32_t* bt, int npg, int64_t page_stride,
                                              int64_t head_off, int wave, int lane, u32x4 (&kf)[4][4]) {
 #pragma unroll
@@ -91,7 +93,11 @@ __device__ __forceinline__ void load_k_frags(const uint16_t* kp, const int32_t* 
     const uint16_t* base = kp + (int64_t)bt[min(4 * wave + kt, npg - 1)] * page_stride + head_off +
                            (lane & 15) * HD + 8 * (lane >> 4);
 #pragma unroll
-    for (int ds = 0; ds < 4; ++ds) kf[kt][ds] = *reinterpret_cast<const u32x4*>(base + 32 * ds);
+    for (int ds = 0; ds < 4; ++ds) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(base + 32 * ds);
+      if constexpr (NT) kf[kt][ds] = __builtin_nontemporal_load(p);
+      else kf[kt][ds] = *p;
+    }
   }
 }
 
@@ -114,6 +120,7 @@ __device__ __forceinline__ void load_q_block(const uint16_t* q0, int64_t q_tok_s
 // pages 2 ks and 2 ks + 1) lane l's operand -- column d, keys 8 (l / 16) .. +7
 // -- is one 16-byte load of a d-row of one page. Wave w owns the columns
 // d in [32 w, 32 w + 32), two 16-wide tiles, over all the split's keys.
+template <bool NT>
 __device__ __forceinline__ void load_v_frags(const uint16_t* vp, const int32_t* bt, int npg, int64_t page_stride,
                                              int64_t head_off, int wave, int lane, u32x4 (&vf)[8][2]) {
   const int q4 = lane >> 4;
@@ -123,7 +130,11 @@ __device__ __forceinline__ void load_v_frags(const uint16_t* vp, const int32_t* 
     const int32_t p0 = bt[min(2 * ks, npg - 1)], p1 = bt[min(2 * ks + 1, npg - 1)];
     const uint16_t* base = vp + (int64_t)((q4 >> 1) ? p1 : p0) * page_stride + head_off + d * PAGE + 8 * (q4 & 1);
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt) vf[ks][dt] = *reinterpret_cast<const u32x4*>(base + 16 * dt * PAGE);
+    for (int dt = 0; dt < 2; ++dt) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(base + 16 * dt * PAGE);
+      if constexpr (NT) vf[ks][dt] = __builtin_nontemporal_load(p);
+      else vf[ks][dt] = *p;
+    }
   }
 }
 
@@ -265,6 +276,7 @@ __device__ __forceinline__ void store_pv(const f32x4 (&acc)[2], int wave, int la
     for (int i = 0; i < 4; ++i) out[i * HD + 32 * wave + 16 * dt + (lane & 15)] = acc[dt][i];
 }
 
+template <bool NT>
 __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
   __shared__ float S[1][GQA][SROW];
 
@@ -315,8 +327,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
 
   u32x4 qa[4], kf[4][4], vf[8][2];
   load_q_block(a.q + ((int64_t)b * a.hq + g * GQA) * HD, 0, 1, lane, qa);
-  load_k_frags(a.kp, bt, npg, page_stride, head_off, wave, lane, kf);
-  load_v_frags(a.vp, bt, npg, page_stride, head_off, wave, lane, vf);
+  load_k_frags<NT>(a.kp, bt, npg, page_stride, head_off, wave, lane, kf);
+  load_v_frags<NT>(a.vp, bt, npg, page_stride, head_off, wave, lane, vf);
   __builtin_amdgcn_sched_barrier(0);  // every load issued before the first MFMA waits
   scores_block(qa, kf, 1, [&](int) { return nt; }, wave, lane, a.qscale, S);
   __syncthreads();
@@ -401,8 +413,8 @@ __global__ __launch_bounds__(256) void prefill_split_kernel(PrefillArgs a) {
 
   u32x4 qa[4], qn[4], kf[4][4], vf[8][2];
   load_q_block(q0, q_tok, min(4, nq), lane, qa);
-  load_k_frags(a.kp, bt, npg, page_stride, head_off, wave, lane, kf);
-  load_v_frags(a.vp, bt, npg, page_stride, head_off, wave, lane, vf);
+  load_k_frags<false>(a.kp, bt, npg, page_stride, head_off, wave, lane, kf);
+  load_v_frags<false>(a.vp, bt, npg, page_stride, head_off, wave, lane, vf);
   __builtin_amdgcn_sched_barrier(0);  // every load issued before the first MFMA waits
   __syncthreads();                    // spos, soff
   for (int tb = 0; tb < nq; tb += 4) {  // tokens tb .. tb + 3 of the item
@@ -566,7 +578,10 @@ hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t s) {
   a.qscale = p.scale * LOG2E;
   a.ws_o = p.ws_o;
   a.ws_ml = p.ws_ml;
-  hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)(p.total_splits * p.num_kv_heads)), dim3(256), 0, s, a);
+  if (p.stream_kv)
+    hipLaunchKernelGGL(decode_split_kernel<true>, dim3((unsigned)(p.total_splits * p.num_kv_heads)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(decode_split_kernel<false>, dim3((unsigned)(p.total_splits * p.num_kv_heads)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)p.batch, (unsigned)p.num_q_heads), dim3(128), 0, s,

@@ -96,7 +96,8 @@ class Decoder:
                                       block_table, self.k_pages[l], self.v_pages[l],
                                       num_q_heads=s.num_q_heads, num_kv_heads=s.num_kv_heads, eps=s.eps)
             a = bi_decode_attention(q, self.k_pages[l], self.v_pages[l], block_table, lens_dev, offs_dev, total,
-                                    workspace=ws, out_dtype=torch.bfloat16, split_tokens=s.split_tokens)
+                                    workspace=ws, out_dtype=torch.bfloat16, split_tokens=s.split_tokens,
+                                    stream_kv=True)
             o = bi_mm(a.view(bsz, s.hidden), w["w_o"][l], b_is_nk=nk, out_dtype=torch.bfloat16)
             h = bi_add_rmsnorm(x, o, w["w_post"][l], s.eps)
             gu = bi_mm(h, w["w_gu"][l], b_is_nk=nk, out_dtype=torch.bfloat16)

@@ -117,17 +117,18 @@ def test_rmsnorm_f32_out_ldy_multiple_of_4_is_not_misaligned(bi):
 
 def attn(bi, **kw):
     args = dict(q=A16, k=A16, v=A16, bt=A16, maxp=2048, lens=A16, offs=A16, total=256, batch=2, hq=32, hkv=8,
-                d=128, page=16, split=256, scale=0.088, ws=A16, wsb=1 << 30, out=A16, dt=1)
+                d=128, page=16, split=256, scale=0.088, ws=A16, wsb=1 << 30, out=A16, dt=1, flags=0)
     args.update(kw)
     a = args
     return bi.lib.bi_decode_attention(a["q"], a["k"], a["v"], a["bt"], a["maxp"], a["lens"], a["offs"], a["total"],
                                       a["batch"], a["hq"], a["hkv"], a["d"], a["page"], a["split"], a["scale"],
-                                      a["ws"], a["wsb"], a["out"], a["dt"], None)
+                                      a["ws"], a["wsb"], a["out"], a["dt"], a["flags"], None)
 
 
 def test_decode_validation(bi):
     assert attn(bi, d=64) == UNSUPPORTED
     assert attn(bi, page=32) == UNSUPPORTED
+    assert attn(bi, flags=2) == UNSUPPORTED
     assert attn(bi, split=128) == UNSUPPORTED
     assert attn(bi, hq=16) == UNSUPPORTED
     assert attn(bi, dt=3) == DTYPE

@@ -350,3 +350,6 @@ def test_decode_attention_benchmark_batch_sampled(lib):
     seqs = [0, 100, int(torch.argmax(lens_t)), int(torch.argmin(lens_t)), 255]
     ref = O.decode_attention(bits(q), bits(kp), bits(vp), table.numpy(), lens_t.numpy(), 128 ** -0.5, seqs=seqs)
     assert_close(f32(out[seqs]), ref[seqs], "decode batch 256")
+    # the streaming hint changes how K/V are loaded, not what is computed
+    out_nt = lib.bi_decode_attention(q, kp, vp, table.to(DEV), lens_t.to(DEV), offs.to(DEV), total, stream_kv=True)
+    assert same_bits(out_nt, out)
