@@ -113,9 +113,33 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream=None) -> ctypes.c_void_p:
-    s = torch.cuda.current_stream() if stream is None else stream
+def _on_device(stream, **tensors):
+    """Every tensor the kernels dereference must be GPU memory on the device
+    whose stream runs them: a host pointer reaching a kernel is a GPU memory
+    fault, so this is checked (before anything is launched) rather than left
+    to the caller. None entries (optional arguments) are skipped."""
+    for name, t in tensors.items():
+        if t is not None and (not isinstance(t, torch.Tensor) or not t.is_cuda):
+            raise ValueError(f"{name} must be a CUDA (GPU) tensor")
+    devs = {t.device for t in tensors.values() if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"tensors are on different devices: {sorted(str(d) for d in devs)}")
+    if stream is not None and devs and stream.device not in devs:
+        raise ValueError(f"stream is on {stream.device}, tensors on {devs.pop()}")
+
+
+def _stream(stream=None, device=None) -> ctypes.c_void_p:
+    s = (torch.cuda.current_stream(device) if stream is None else stream)
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _out_ok(out, shape, dtypes, name="out"):
+    """A caller-supplied output must have the shape and dtype the kernel
+    writes (it writes every element of that shape)."""
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(out.shape)}, expected {tuple(shape)}")
+    if out.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {out.dtype}, expected one of {dtypes}")
 
 
 def _mat(t: torch.Tensor, name: str):
@@ -150,13 +174,15 @@ def bi_mm(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None, *, 
           out_dtype: torch.dtype = torch.float32, stream=None) -> torch.Tensor:
     """C = a @ b (b [K, N]) or a @ b.T (b [N, K], b_is_nk=True); bf16 in, fp32 accumulate."""
     m, n, k = _gemm_shapes(a, b, b_is_nk)
+    _on_device(stream, a=a, b=b, out=out)
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    _out_ok(out, (m, n), (torch.float32, torch.bfloat16))
     a, lda = _mat(a, "a")
     b, ldb = _mat(b, "b")
     out, ldc = _mat(out, "out")
     _check(lib.bi_mm(_ptr(a), lda, _ptr(b), ldb, int(b_is_nk), _ptr(out), ldc, _dtype_code(out.dtype),
-                     m, n, k, _stream(stream)))
+                     m, n, k, _stream(stream, a.device)))
     return out
 
 
@@ -167,13 +193,15 @@ def bi_addmm(bias: torch.Tensor, a: torch.Tensor, b: torch.Tensor, out: torch.Te
     m, n, k = _gemm_shapes(a, b, b_is_nk)
     if bias.dim() != 1 or bias.shape[0] != n or not bias.is_contiguous():
         raise ValueError("bias must be a contiguous [N] vector")
+    _on_device(stream, bias=bias, a=a, b=b, out=out)
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    _out_ok(out, (m, n), (torch.float32, torch.bfloat16))
     a, lda = _mat(a, "a")
     b, ldb = _mat(b, "b")
     out, ldc = _mat(out, "out")
     _check(lib.bi_addmm(_ptr(bias), _dtype_code(bias.dtype), float(beta), float(alpha), _ptr(a), lda, _ptr(b), ldb,
-                        int(b_is_nk), _ptr(out), ldc, _dtype_code(out.dtype), m, n, k, _stream(stream)))
+                        int(b_is_nk), _ptr(out), ldc, _dtype_code(out.dtype), m, n, k, _stream(stream, a.device)))
     return out
 
 
@@ -193,22 +221,28 @@ def bi_rmsnorm(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, out: torch.T
     m, n = x.shape
     if w.dim() != 1 or w.shape[0] != n or not w.is_contiguous():
         raise ValueError("w must be a contiguous [N] vector")
+    _on_device(stream, x=x, w=w, out=out)
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    _out_ok(out, (m, n), (torch.float32, torch.bfloat16))
     x, ldx = _mat(x, "x")
     out, ldy = _mat(out, "out")
     _check(lib.bi_rmsnorm(_ptr(x), ldx, _ptr(w), float(eps), _ptr(out), ldy, _dtype_code(out.dtype), m, n,
-                          _stream(stream)))
+                          _stream(stream, x.device)))
     return out
 
 
 def bi_mean(x: torch.Tensor, out: torch.Tensor | None = None, *, stream=None) -> torch.Tensor:
     """y[i] = mean_j x[i, j] in fp32; x bf16 or fp32 [M, N]."""
     m, n = x.shape
+    _on_device(stream, x=x, out=out)
     if out is None:
         out = torch.empty((m,), dtype=torch.float32, device=x.device)
+    _out_ok(out, (m,), (torch.float32,))
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
     x, ldx = _mat(x, "x")
-    _check(lib.bi_mean(_ptr(x), _dtype_code(x.dtype), ldx, _ptr(out), m, n, _stream(stream)))
+    _check(lib.bi_mean(_ptr(x), _dtype_code(x.dtype), ldx, _ptr(out), m, n, _stream(stream, x.device)))
     return out
 
 
@@ -218,14 +252,20 @@ def bi_log_softmax(x: torch.Tensor, out: torch.Tensor | None = None, argmax: tor
     if x.dtype != torch.float32:
         raise TypeError("x must be float32")
     m, n = x.shape
+    _on_device(stream, x=x, out=out, argmax=argmax if want_argmax else None)
     if out is None:
         out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _out_ok(out, (m, n), (torch.float32,))
     if want_argmax and argmax is None:
         argmax = torch.empty((m,), dtype=torch.int64, device=x.device)
+    if want_argmax:
+        _out_ok(argmax, (m,), (torch.int64,), "argmax")
+        if not argmax.is_contiguous():
+            raise ValueError("argmax must be contiguous")
     x, ldx = _mat(x, "x")
     out, ldy = _mat(out, "out")
     _check(lib.bi_log_softmax(_ptr(x), ldx, _ptr(out), ldy, _ptr(argmax if want_argmax else None), m, n,
-                              _stream(stream)))
+                              _stream(stream, x.device)))
     return out, (argmax if want_argmax else None)
 
 
@@ -275,6 +315,13 @@ def bi_decode_attention(q, k_pages, v_pages, block_table, context_lens, split_of
             raise ValueError(f"{nm} must be contiguous")
     if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32 or split_offsets.dtype != torch.int32:
         raise TypeError("block_table, context_lens, split_offsets must be int32")
+    if block_table.dim() != 2 or block_table.shape[0] != bsz:
+        raise ValueError(f"block_table must be [B={bsz}, max_pages], got {tuple(block_table.shape)}")
+    if context_lens.numel() != bsz or split_offsets.numel() != bsz + 1:
+        raise ValueError(f"context_lens must hold B={bsz} entries and split_offsets B+1={bsz + 1} "
+                         f"(got {context_lens.numel()} and {split_offsets.numel()})")
+    _on_device(stream, q=q, k_pages=k_pages, v_pages=v_pages, block_table=block_table, context_lens=context_lens,
+               split_offsets=split_offsets, workspace=workspace, out=out)
     if scale is None:
         scale = d ** -0.5
     need = bi_decode_workspace_bytes(total_splits, hq, d)
@@ -282,10 +329,15 @@ def bi_decode_attention(q, k_pages, v_pages, block_table, context_lens, split_of
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((bsz, hq, d), dtype=out_dtype, device=q.device)
+    _out_ok(out, (bsz, hq, d), (torch.float32, torch.bfloat16))
+    if not out.is_contiguous() or not workspace.is_contiguous():
+        raise ValueError("out and workspace must be contiguous")
     _check(lib.bi_decode_attention(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), block_table.shape[1],
                                    _ptr(context_lens), _ptr(split_offsets), int(total_splits), bsz, hq, hkv, d,
-                                   page, int(split_tokens), float(scale), _ptr(workspace), workspace.numel(),
-                                   _ptr(out), _dtype_code(out.dtype), 1 if stream_kv else 0, _stream(stream)))
+                                   page, int(split_tokens), float(scale), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(),
+                                   _ptr(out), _dtype_code(out.dtype), 1 if stream_kv else 0,
+                                   _stream(stream, q.device)))
     return out
 
 
@@ -300,13 +352,15 @@ def bi_add_rmsnorm(x: torch.Tensor, d: torch.Tensor, w: torch.Tensor, eps: float
         raise ValueError("d must have x's shape")
     if w.dim() != 1 or w.shape[0] != n or not w.is_contiguous():
         raise ValueError("w must be a contiguous [N] vector")
+    _on_device(stream, x=x, d=d, w=w, out=out)
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    _out_ok(out, (m, n), (torch.float32, torch.bfloat16))
     x, ldx = _mat(x, "x")
     d, ldd = _mat(d, "d")
     out, ldy = _mat(out, "out")
     _check(lib.bi_add_rmsnorm(_ptr(x), ldx, _ptr(d), ldd, _ptr(w), float(eps), _ptr(out), ldy,
-                              _dtype_code(out.dtype), m, n, _stream(stream)))
+                              _dtype_code(out.dtype), m, n, _stream(stream, x.device)))
     return out
 
 
@@ -317,11 +371,13 @@ def bi_embed(table: torch.Tensor, tokens: torch.Tensor, out: torch.Tensor | None
         raise TypeError("tokens must be a contiguous int64 vector")
     vocab, n = table.shape
     m = tokens.shape[0]
+    _on_device(stream, table=table, tokens=tokens, out=out)
     if out is None:
         out = torch.empty((m, n), dtype=torch.bfloat16, device=table.device)
+    _out_ok(out, (m, n), (torch.bfloat16,))
     table, ld = _mat(table, "table")
     out, ldo = _mat(out, "out")
-    _check(lib.bi_embed(_ptr(table), ld, vocab, _ptr(tokens), _ptr(out), ldo, m, n, _stream(stream)))
+    _check(lib.bi_embed(_ptr(table), ld, vocab, _ptr(tokens), _ptr(out), ldo, m, n, _stream(stream, table.device)))
     return out
 
 
@@ -332,11 +388,13 @@ def bi_silu_mul(gu: torch.Tensor, out: torch.Tensor | None = None, *, stream=Non
     if n2 % 2:
         raise ValueError("gu must have an even number of columns")
     n = n2 // 2
+    _on_device(stream, gu=gu, out=out)
     if out is None:
         out = torch.empty((m, n), dtype=torch.bfloat16, device=gu.device)
+    _out_ok(out, (m, n), (torch.bfloat16,))
     gu, ldg = _mat(gu, "gu")
     out, ldo = _mat(out, "out")
-    _check(lib.bi_silu_mul(_ptr(gu), ldg, _ptr(out), ldo, m, n, _stream(stream)))
+    _check(lib.bi_silu_mul(_ptr(gu), ldg, _ptr(out), ldo, m, n, _stream(stream, gu.device)))
     return out
 
 
@@ -358,13 +416,24 @@ def bi_qknorm_rope_append(qkv, q_norm_w, k_norm_w, cos_tab, sin_tab, positions, 
     num_pages, hkv, page, d = k_pages.shape
     if hkv != num_kv_heads or v_pages.shape != v_pages_shape(k_pages):
         raise ValueError("cache shape disagrees with num_kv_heads (k [P, Hkv, page, D], v [P, Hkv, D, page])")
+    if qkv.dim() != 2 or qkv.shape[1] < (num_q_heads + 2 * num_kv_heads) * d:
+        raise ValueError("qkv must be [B, (Hq + 2 Hkv) D]")
+    if positions.numel() != bsz or block_table.dim() != 2 or block_table.shape[0] != bsz:
+        raise ValueError(f"positions must hold B={bsz} entries and block_table be [B, max_pages]")
+    if cos_tab.dim() != 2 or cos_tab.shape[1] != d // 2 or q_norm_w.numel() != d or k_norm_w.numel() != d:
+        raise ValueError("cos/sin tables must be [max_pos, D/2] and the norm weights [D]")
+    _on_device(stream, qkv=qkv, q_norm_w=q_norm_w, k_norm_w=k_norm_w, cos_tab=cos_tab, sin_tab=sin_tab,
+               positions=positions, block_table=block_table, k_pages=k_pages, v_pages=v_pages, q_out=q_out)
     if q_out is None:
         q_out = torch.empty((bsz, num_q_heads, d), dtype=torch.bfloat16, device=qkv.device)
+    _out_ok(q_out, (bsz, num_q_heads, d), (torch.bfloat16,), "q_out")
+    if not q_out.is_contiguous():
+        raise ValueError("q_out must be contiguous")
     qkv, ldq = _mat(qkv, "qkv")
     _check(lib.bi_qknorm_rope_append(_ptr(qkv), ldq, _ptr(q_norm_w), _ptr(k_norm_w), float(eps), _ptr(cos_tab),
                                      _ptr(sin_tab), cos_tab.shape[0], _ptr(positions), _ptr(block_table),
                                      block_table.shape[1], num_pages, _ptr(k_pages), _ptr(v_pages), _ptr(q_out), bsz,
-                                     num_q_heads, num_kv_heads, d, page, _stream(stream)))
+                                     num_q_heads, num_kv_heads, d, page, _stream(stream, qkv.device)))
     return q_out
 
 
@@ -405,6 +474,15 @@ def bi_prefill_attention(q, k_pages, v_pages, block_table, q_pos, q_offsets, wor
                   (q_pos, "q_pos"), (q_offsets, "q_offsets"), (work, "work")):
         if not t.is_contiguous():
             raise ValueError(f"{nm} must be contiguous")
+    for t, nm in ((block_table, "block_table"), (q_pos, "q_pos"), (q_offsets, "q_offsets"), (work, "work")):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{nm} must be int32")
+    if q_pos.numel() != rows or q_offsets.numel() != rows + 1 or work.numel() != 4 * n_work:
+        raise ValueError("q_pos, q_offsets and work must have the plan's sizes (rows, rows + 1, 4 n_work)")
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [batch, max_pages]")
+    _on_device(stream, q=q, k_pages=k_pages, v_pages=v_pages, block_table=block_table, q_pos=q_pos,
+               q_offsets=q_offsets, work=work, workspace=workspace, out=out)
     if scale is None:
         scale = d ** -0.5
     need = bi_decode_workspace_bytes(total, hq, d)
@@ -412,9 +490,12 @@ def bi_prefill_attention(q, k_pages, v_pages, block_table, q_pos, q_offsets, wor
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((rows, hq, d), dtype=out_dtype, device=q.device)
+    _out_ok(out, (rows, hq, d), (torch.float32, torch.bfloat16))
+    if not out.is_contiguous() or not workspace.is_contiguous():
+        raise ValueError("out and workspace must be contiguous")
     _check(lib.bi_prefill_attention(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), block_table.shape[1],
                                     _ptr(q_pos), _ptr(q_offsets), _ptr(work), n_work, rows, total,
                                     block_table.shape[0], hq, hkv, d, page, int(split_tokens), float(scale),
-                                    _ptr(workspace), workspace.numel(), _ptr(out), _dtype_code(out.dtype),
-                                    _stream(stream)))
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
+                                    _dtype_code(out.dtype), _stream(stream, q.device)))
     return out

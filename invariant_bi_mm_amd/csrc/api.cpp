@@ -353,6 +353,7 @@ bi_status bi_prefill_attention(const void* q, const void* k_pages, const void* v
   p.max_pages = max_pages;
   p.n_work = n_work;
   p.n_rows = n_rows;
+  p.total_splits = total_splits;
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
   p.scale = scale;

@@ -295,9 +295,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
   // The sequence owning split w: the one b with offs[b] <= w < offs[b+1]
   // (lengths are >= 1, so the offsets increase strictly). Every thread reads
   // its sequences' offsets and length with coalesced loads issued together
-  // with the count above (one memory round trip per 256 sequences), and the
-  // owner passes (b, s, L) through LDS.
-  __shared__ int sinfo[3];
+  // with the count above (one memory round trip per 256 sequences). Each
+  // wave passes the (b, s, L) its lanes found, or b = -1, through its own
+  // LDS slot; after the barrier the first slot that holds an owner is used.
+  // Offsets that name no owner for w, or a length that does not reach split
+  // w or overruns the block table's row, leave the workgroup with nothing to
+  // do (contents on the device are the caller's; this keeps every access in
+  // bounds whatever they are).
+  __shared__ int sinfo[4][3];
+  int ob = -1, os = 0, ol = 0;
   for (int base = 0; base < a.batch; base += 256) {
     const int t = base + tid;
     if (t < a.batch) {
@@ -305,18 +311,33 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
       // all three loads in flight together (not sunk into the branches below)
       asm volatile("" ::"v"(o0), "v"(o1), "v"(len));
       if (o0 <= w && w < o1) {
-        sinfo[0] = t;
-        sinfo[1] = w - o0;
-        sinfo[2] = len;
+        ob = t;
+        os = w - o0;
+        ol = len;
       }
     }
   }
   if (w >= total) return;  // uniform over the workgroup
+  {
+    const uint64_t found = __ballot(ob >= 0);
+    const int src = found ? (int)__builtin_ctzll(found) : 0;  // wave-uniform
+    const int vb = found ? __builtin_amdgcn_readlane(ob, src) : -1;
+    const int vs = __builtin_amdgcn_readlane(os, src), vl = __builtin_amdgcn_readlane(ol, src);
+    if (lane == 0) {
+      sinfo[wave][0] = vb;
+      sinfo[wave][1] = vs;
+      sinfo[wave][2] = vl;
+    }
+  }
   __syncthreads();
-  const int b = __builtin_amdgcn_readfirstlane(sinfo[0]);
-  const int s = __builtin_amdgcn_readfirstlane(sinfo[1]);
-  const int L = __builtin_amdgcn_readfirstlane(sinfo[2]);
-  const int t0 = s * SPLIT;
+  int slot = 0;
+  while (slot < 3 && sinfo[slot][0] < 0) ++slot;
+  const int b = __builtin_amdgcn_readfirstlane(sinfo[slot][0]);
+  const int s = __builtin_amdgcn_readfirstlane(sinfo[slot][1]);
+  const int L = __builtin_amdgcn_readfirstlane(sinfo[slot][2]);
+  const int64_t t0l = (int64_t)s * SPLIT;  // no overflow whatever the offsets
+  if (b < 0 || t0l >= L || (t0l + min((int64_t)SPLIT, L - t0l) + PAGE - 1) / PAGE > a.max_pages) return;  // uniform
+  const int t0 = (int)t0l;
   const int nt = min(SPLIT, L - t0);
   const int npg = (nt + PAGE - 1) / PAGE;
   const int32_t* bt = a.bt + (int64_t)b * a.max_pages + t0 / PAGE;
@@ -465,7 +486,7 @@ __global__ __launch_bounds__(256) void prefill_split_kernel(PrefillArgs a) {
 // its partials at once and takes the max from the loaded values: one memory
 // round trip. Longer rows first take the max, then fold 32 splits per trip.
 // Two waves per row keep 12 rows per CU in flight (76 VGPRs).
-__global__ __launch_bounds__(128) void decode_combine_kernel(const int32_t* __restrict__ offs,
+__global__ __launch_bounds__(128) void decode_combine_kernel(const int32_t* __restrict__ offs, int cap,
                                                               const float* __restrict__ ws_o,
                                                               const float* __restrict__ ws_ml, int hq,
                                                               void* __restrict__ out, int out_bf16) {
@@ -474,7 +495,10 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const int32_t* __re
   __shared__ float pl[2];
   const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int pg = tid >> 5, c = tid & 31, wv = tid >> 6;
-  const int w0 = offs[b], ns = offs[b + 1] - w0;
+  // The row's splits [offs[b], offs[b+1]), clamped to the workspace's cap
+  // splits so that offsets on the device can never send a read past it.
+  const int w1 = min(max(offs[b + 1], 0), cap);
+  const int w0 = min(max(offs[b], 0), w1), ns = w1 - w0;
   float l[2] = {0.0f, 0.0f};
   float4 o[2] = {make_float4(0.0f, 0.0f, 0.0f, 0.0f), make_float4(0.0f, 0.0f, 0.0f, 0.0f)};
   float M = -INFINITY;
@@ -585,7 +609,8 @@ hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)p.batch, (unsigned)p.num_q_heads), dim3(128), 0, s,
-                     p.split_offsets, p.ws_o, p.ws_ml, p.num_q_heads, p.out, p.out_bf16 ? 1 : 0);
+                     p.split_offsets, (int)p.total_splits, p.ws_o, p.ws_ml, p.num_q_heads, p.out,
+                     p.out_bf16 ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -608,7 +633,8 @@ hipError_t launch_prefill_attention(const PrefillParams& p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)p.n_rows, (unsigned)p.num_q_heads), dim3(128), 0, s,
-                     p.q_offsets, p.ws_o, p.ws_ml, p.num_q_heads, p.out, p.out_bf16 ? 1 : 0);
+                     p.q_offsets, (int)p.total_splits, p.ws_o, p.ws_ml, p.num_q_heads, p.out,
+                     p.out_bf16 ? 1 : 0);
   return hipGetLastError();
 }
 

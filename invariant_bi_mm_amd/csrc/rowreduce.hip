@@ -287,16 +287,21 @@ __global__ __launch_bounds__(LS_NT) void log_softmax_kernel(const float* __restr
       bi = j;
     }
   };
+  // While every element seen so far is -inf (a masked prefix), m is -inf
+  // and v - m would be NaN; the elements are then -inf too, so they are
+  // measured against 0 instead, which gives exp(-inf) = 0. A finite m is
+  // used as it is, so rows without -inf keep their bits.
   auto fold4 = [&](const f32x4 v, int j0) {
     const float cm = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
     if (cm > m) {
       s = s * exp_dev(m - cm);
       m = cm;
     }
-    s = s + exp_dev(v.x - m);
-    s = s + exp_dev(v.y - m);
-    s = s + exp_dev(v.z - m);
-    s = s + exp_dev(v.w - m);
+    const float mr = m == -INFINITY ? 0.0f : m;
+    s = s + exp_dev(v.x - mr);
+    s = s + exp_dev(v.y - mr);
+    s = s + exp_dev(v.z - mr);
+    s = s + exp_dev(v.w - mr);
     fold(v.x, j0);
     fold(v.y, j0 + 1);
     fold(v.z, j0 + 2);
@@ -355,7 +360,7 @@ __global__ __launch_bounds__(LS_NT) void log_softmax_kernel(const float* __restr
       s = s * exp_dev(m - v);
       m = v;
     }
-    s = s + exp_dev(v - m);
+    s = s + exp_dev(v - (m == -INFINITY ? 0.0f : m));
     fold(v, nch * 4 + tid);
   }
 

@@ -269,3 +269,43 @@ def test_binding_rejects_bad_python_args(bi):
         bi.bi_mm(torch.zeros(2, 8), torch.zeros(8, 8, dtype=torch.bfloat16))
     with pytest.raises(ValueError):
         bi.bi_mm(torch.zeros(2, 8, dtype=torch.bfloat16), torch.zeros(16, 8, dtype=torch.bfloat16))
+
+
+def test_binding_refuses_host_tensors_before_any_launch(bi):
+    """A host pointer handed to a kernel is a GPU memory fault: every wrapper
+    checks that its tensors are GPU tensors (and shapes that size the kernels'
+    reads and writes) before it launches, so these raise here, without a GPU.
+    The decode plan's split offsets come back on the host; passing them
+    unmoved is the case that matters most."""
+    bf = torch.bfloat16
+    a, w = torch.zeros(4, 64, dtype=bf), torch.zeros(64, 32, dtype=bf)
+    with pytest.raises(ValueError, match="CUDA"):
+        bi.bi_mm(a, w)
+    with pytest.raises(ValueError, match="CUDA"):
+        bi.bi_addmm(torch.zeros(32, dtype=bf), a, w)
+    with pytest.raises(ValueError, match="CUDA"):
+        bi.bi_rmsnorm(a, torch.ones(64, dtype=bf))
+    with pytest.raises(ValueError, match="CUDA"):
+        bi.bi_mean(a)
+    with pytest.raises(ValueError, match="CUDA"):
+        bi.bi_log_softmax(torch.zeros(2, 64))
+    with pytest.raises(ValueError, match="CUDA"):
+        bi.bi_add_rmsnorm(a.clone(), a, torch.ones(64, dtype=bf))
+    with pytest.raises(ValueError, match="CUDA"):
+        bi.bi_embed(torch.zeros(10, 64, dtype=bf), torch.zeros(3, dtype=torch.int64))
+    with pytest.raises(ValueError, match="CUDA"):
+        bi.bi_silu_mul(torch.zeros(2, 64, dtype=bf))
+    lens = torch.tensor([5, 300], dtype=torch.int32)
+    offs, total = bi.bi_decode_plan(lens)
+    assert offs.device.type == "cpu" and total == 3
+    q = torch.zeros(2, 32, 128, dtype=bf)
+    kp = torch.zeros(4, 8, 16, 128, dtype=bf)
+    vp = torch.zeros(4, 8, 128, 16, dtype=bf)
+    bt = torch.zeros(2, 32, dtype=torch.int32)
+    with pytest.raises(ValueError, match="CUDA"):
+        bi.bi_decode_attention(q, kp, vp, bt, lens, offs, total)
+    # shapes that size the kernels' accesses are checked too
+    with pytest.raises(ValueError, match="split_offsets"):
+        bi.bi_decode_attention(q, kp, vp, bt, lens, offs[:2], total)
+    with pytest.raises(ValueError, match="block_table"):
+        bi.bi_decode_attention(q, kp, vp, bt[:1], lens, offs, total)

@@ -284,6 +284,48 @@ def test_log_softmax_edges(lib):
     assert none is None and same_bits(y1, y[:1])
 
 
+def assert_close_masked(got, ref, what):
+    """Parity where the reference holds -inf (masked logits give -inf
+    log-probabilities): those positions must be -inf exactly, the rest meet
+    the usual tolerance."""
+    got, ref = np.asarray(got, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    neg = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(got), neg), f"{what}: -inf positions differ"
+    assert np.isfinite(got[~neg]).all(), f"{what}: non-finite values where the oracle is finite"
+    assert_close(got[~neg], ref[~neg], what)
+
+
+@pytest.mark.parametrize("n", [1003, 151936])
+def test_log_softmax_masked_rows(lib, n):
+    """Rows with -inf entries (banned tokens, a grammar mask): a masked first
+    chunk, a masked prefix longer than what a thread keeps in registers, all
+    but one entry masked, a masked tail with n % 4 != 0, and a scattered
+    mask. The fp64 oracle gives finite log-probabilities for the unmasked
+    entries and -inf for the masked ones; so must the kernel."""
+    say(f"log_softmax masked rows n={n}")
+    m = 6
+    ld = (n + 3) // 4 * 4  # rows start 16-byte aligned
+    x = S.normal_f32((m, ld), 4.0, seed=95 + n).to(DEV)[:, :n]
+    ninf = float("-inf")
+    x[0, :4] = ninf                                  # one leading 16-byte chunk
+    x[1, : min(n - 1, 70000)] = ninf                 # a long masked prefix
+    x[2, :] = ninf
+    x[2, n // 3] = 1.5                               # all but one entry masked
+    x[3, n - 3:] = ninf                              # masked tail (n % 4 != 0 for 1003)
+    g = torch.Generator().manual_seed(96)
+    x[4, torch.rand(n, generator=g) < 0.3] = ninf     # scattered
+    x[5, 4096:8192] = ninf                           # a block in the middle
+    y, am = lib.bi_log_softmax(x, out=torch.empty((m, ld), device=DEV)[:, :n])
+    xc = f32(x)
+    ref = O.log_softmax(xc)
+    assert_close_masked(f32(y), ref, f"masked log_softmax n={n}")
+    assert am.cpu().tolist() == O.argmax(xc).tolist()
+    assert float(y[2, n // 3]) == 0.0 and am[2].item() == n // 3
+    # the unmasked rows around them are untouched by the change: same bits as alone
+    y0, _ = lib.bi_log_softmax(x[4:5].contiguous())
+    assert same_bits(y0, y[4:5])
+
+
 # ------------------------------------------------------------------ decode attention
 def make_decode(lens, seed, hkv=8, hq=32, d=128, page=16):
     lens_t = torch.tensor(lens, dtype=torch.int32)
@@ -353,3 +395,33 @@ def test_decode_attention_benchmark_batch_sampled(lib):
     # the streaming hint changes how K/V are loaded, not what is computed
     out_nt = lib.bi_decode_attention(q, kp, vp, table.to(DEV), lens_t.to(DEV), offs.to(DEV), total, stream_kv=True)
     assert same_bits(out_nt, out)
+
+
+def test_decode_attention_inconsistent_device_offsets_stay_in_bounds(lib):
+    """Device-side lengths and offsets are the caller's: the host cannot read
+    them. Offsets that give one sequence a split its length does not reach
+    (and a sequence with fewer splits than its length needs) leave those
+    workgroups with nothing to do; every access stays inside the buffers and
+    the sequences whose splits are consistent keep their exact bits."""
+    lens = [300, 5, 40]
+    say("decode inconsistent offsets", lens)
+    lens_t, table, q, kp, vp = make_decode(lens, seed=130)
+    good = run_decode(lib, lens_t, table, q, kp, vp)
+    bad_offs = torch.tensor([0, 2, 4, 5], dtype=torch.int32)  # sequence 1 (5 tokens) given 2 splits
+    ws = torch.zeros(lib.bi_decode_workspace_bytes(5, 32, 128), dtype=torch.uint8, device=DEV)
+    out = lib.bi_decode_attention(q.to(DEV), kp.to(DEV), vp.to(DEV), table.to(DEV), lens_t.to(DEV),
+                                  bad_offs.to(DEV), 5, workspace=ws)
+    torch.cuda.synchronize()
+    assert same_bits(out[0], good[0]) and same_bits(out[2], good[2])
+
+
+def test_binding_checks_output_shapes(lib):
+    """A caller's output buffer must have the shape the kernel writes."""
+    a = S.normal_bf16((4, 64), 1.0, seed=140, device=DEV)
+    w = S.normal_bf16((64, 32), 1.0, seed=141, device=DEV)
+    with pytest.raises(ValueError, match="shape"):
+        lib.bi_mm(a, w, out=torch.empty((4, 16), device=DEV))
+    with pytest.raises(ValueError, match="shape"):
+        lib.bi_mean(a, out=torch.empty(3, device=DEV))
+    with pytest.raises(ValueError, match="CUDA"):
+        lib.bi_mm(a, w.cpu())
