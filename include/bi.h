@@ -119,6 +119,32 @@ bi_status bi_addmm(const void* bias, bi_dtype bias_dtype, float beta, float alph
 bi_status bi_gemm_config(int64_t m, int64_t n, int64_t k, int b_is_nk, int32_t* out4);
 
 /* ------------------------------------------------------------------------
+ * bi_gemm: bi_mm and bi_addmm with flags. bias == NULL gives
+ * C = alpha * (A @ B) (bias_dtype and beta unused); otherwise as bi_addmm.
+ * flags: 0 (the tile table of bi_gemm_config, chosen by m, n, k and the
+ * layout), or BI_GEMM_FIXED_TILE: one tile configuration per (n, k, layout)
+ * for every m, and no column split, i.e. no shape-aware tiling at all, which
+ * the pages list among the optimisations batch invariance gives up (wiki
+ * page "Thinking Machines", section on why it is not the main answer, point
+ * 3). Both modes run the same per-element chain, so they give the same
+ * bits; the fixed mode is there to measure what the table gains.
+ * Other flag bits: BI_ERR_UNSUPPORTED. Requirements as bi_mm.
+ * ------------------------------------------------------------------------ */
+#define BI_GEMM_FIXED_TILE 1
+bi_status bi_gemm(const void* bias, bi_dtype bias_dtype, float beta, float alpha,
+                  const void* a, int64_t lda, const void* b, int64_t ldb, int b_is_nk,
+                  void* c, int64_t ldc, bi_dtype c_dtype,
+                  int64_t m, int64_t n, int64_t k, int flags, hipStream_t stream);
+
+/* The launches a GEMM of these sizes makes with these flags (no device
+ * work): *count (1 or 2) entries of five int32 each in out10,
+ * {tile_m, tile_n, tile_k, waves_per_workgroup, first output column}; the
+ * second entry, when present, is the 256x128 column split of a 256x256
+ * GEMM. Unused entries are zero. BI_ERR_NULL for NULL out10 or count,
+ * BI_ERR_SHAPE for negative sizes, BI_ERR_UNSUPPORTED for unknown flags. */
+bi_status bi_gemm_plan(int64_t m, int64_t n, int64_t k, int b_is_nk, int flags, int32_t* out10, int32_t* count);
+
+/* ------------------------------------------------------------------------
  * bi_rmsnorm: y[i,j] = (x[i,j] * r_i) * w[j], r_i = 1 / sqrt(ss_i / n + eps),
  * ss_i = sum_j x[i,j]^2 (RMSNorm; readhandoff.com "What does temperature
  * zero actually guarantee?").

@@ -20,7 +20,7 @@ import torch  # noqa: F401  (must be loaded before libbi.so, see above)
 
 __all__ = [
     "BiError", "LIB_PATH", "lib",
-    "bi_mm", "bi_addmm", "bi_gemm_config", "bi_rmsnorm", "bi_mean", "bi_log_softmax",
+    "bi_mm", "bi_addmm", "bi_gemm", "bi_gemm_config", "bi_gemm_plan", "BI_GEMM_FIXED_TILE", "bi_rmsnorm", "bi_mean", "bi_log_softmax",
     "bi_decode_plan", "bi_decode_workspace_bytes", "bi_decode_attention",
     "bi_add_rmsnorm", "bi_embed", "bi_silu_mul", "bi_qknorm_rope_append",
     "bi_prefill_plan", "bi_prefill_attention", "v_pages_shape",
@@ -36,6 +36,7 @@ if not os.path.exists(LIB_PATH):
 lib = ctypes.CDLL(LIB_PATH)
 
 BI_BF16, BI_F32 = 0, 1
+BI_GEMM_FIXED_TILE = 1
 STATUS = {0: "BI_OK", 1: "BI_ERR_NULL", 2: "BI_ERR_SHAPE", 3: "BI_ERR_STRIDE", 4: "BI_ERR_ALIGN",
           5: "BI_ERR_DTYPE", 6: "BI_ERR_WORKSPACE", 7: "BI_ERR_UNSUPPORTED", 8: "BI_ERR_HIP"}
 
@@ -48,6 +49,12 @@ lib.bi_addmm.argtypes = [_vp, _i32, _f32, _f32, _vp, _i64, _vp, _i64, _i32, _vp,
 lib.bi_addmm.restype = _st
 lib.bi_gemm_config.argtypes = [_i64, _i64, _i64, _i32, ctypes.POINTER(ctypes.c_int32)]
 lib.bi_gemm_config.restype = _st
+lib.bi_gemm.argtypes = [_vp, _i32, _f32, _f32, _vp, _i64, _vp, _i64, _i32, _vp, _i64, _i32, _i64, _i64, _i64, _i32,
+                        _vp]
+lib.bi_gemm.restype = _st
+lib.bi_gemm_plan.argtypes = [_i64, _i64, _i64, _i32, _i32, ctypes.POINTER(ctypes.c_int32),
+                             ctypes.POINTER(ctypes.c_int32)]
+lib.bi_gemm_plan.restype = _st
 lib.bi_rmsnorm.argtypes = [_vp, _i64, _vp, _f32, _vp, _i64, _i32, _i64, _i64, _vp]
 lib.bi_rmsnorm.restype = _st
 lib.bi_mean.argtypes = [_vp, _i32, _i64, _vp, _i64, _i64, _vp]
@@ -203,6 +210,39 @@ def bi_addmm(bias: torch.Tensor, a: torch.Tensor, b: torch.Tensor, out: torch.Te
     _check(lib.bi_addmm(_ptr(bias), _dtype_code(bias.dtype), float(beta), float(alpha), _ptr(a), lda, _ptr(b), ldb,
                         int(b_is_nk), _ptr(out), ldc, _dtype_code(out.dtype), m, n, k, _stream(stream, a.device)))
     return out
+
+
+def bi_gemm(a: torch.Tensor, b: torch.Tensor, bias: torch.Tensor | None = None, out: torch.Tensor | None = None, *,
+            beta: float = 1.0, alpha: float = 1.0, b_is_nk: bool = False, out_dtype: torch.dtype = torch.float32,
+            fixed_tile: bool = False, stream=None) -> torch.Tensor:
+    """bi_mm (bias None) or bi_addmm, with the flags argument: fixed_tile selects
+    one tile configuration per (N, K, layout) for every M (same bits)."""
+    m, n, k = _gemm_shapes(a, b, b_is_nk)
+    if bias is not None and (bias.dim() != 1 or bias.shape[0] != n or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous [N] vector")
+    _on_device(stream, bias=bias, a=a, b=b, out=out)
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    _out_ok(out, (m, n), (torch.float32, torch.bfloat16))
+    a, lda = _mat(a, "a")
+    b, ldb = _mat(b, "b")
+    out, ldc = _mat(out, "out")
+    flags = BI_GEMM_FIXED_TILE if fixed_tile else 0
+    _check(lib.bi_gemm(_ptr(bias), _dtype_code(bias.dtype) if bias is not None else BI_F32, float(beta),
+                       float(alpha), _ptr(a), lda, _ptr(b), ldb, int(b_is_nk), _ptr(out), ldc, _dtype_code(out.dtype),
+                       m, n, k, flags, _stream(stream, a.device)))
+    return out
+
+
+def bi_gemm_plan(m: int, n: int, k: int, b_is_nk: bool = False, fixed_tile: bool = False) -> list:
+    """The launches a GEMM of these sizes makes: a list of (tile_m, tile_n,
+    tile_k, waves, first column) tuples (two when a 256x256 GEMM splits its
+    last columns onto 256x128 tiles)."""
+    out = (ctypes.c_int32 * 10)()
+    cnt = ctypes.c_int32()
+    _check(lib.bi_gemm_plan(m, n, k, int(b_is_nk), BI_GEMM_FIXED_TILE if fixed_tile else 0, out,
+                            ctypes.byref(cnt)))
+    return [tuple(out[5 * i:5 * i + 5]) for i in range(cnt.value)]
 
 
 def bi_gemm_config(m: int, n: int, k: int, b_is_nk: bool = False) -> tuple:

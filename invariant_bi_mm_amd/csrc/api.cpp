@@ -41,7 +41,8 @@ bool valid_dtype(bi_dtype d) { return d == BI_BF16 || d == BI_F32; }
 size_t dsize(bi_dtype d) { return d == BI_BF16 ? 2 : 4; }
 
 bi_status check_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, int b_is_nk, void* c,
-                     int64_t ldc, bi_dtype c_dtype, int64_t m, int64_t n, int64_t k) {
+                     int64_t ldc, bi_dtype c_dtype, int64_t m, int64_t n, int64_t k, int flags = 0) {
+  if (flags & ~BI_GEMM_FIXED_TILE) return fail(BI_ERR_UNSUPPORTED, "unknown GEMM flags 0x%x", flags);
   if (m < 0 || n < 0 || k < 0) return fail(BI_ERR_SHAPE, "negative size (m=%lld n=%lld k=%lld)", (long long)m, (long long)n, (long long)k);
   if (!valid_dtype(c_dtype)) return fail(BI_ERR_DTYPE, "c_dtype %d is not BI_BF16 or BI_F32", (int)c_dtype);
   if (m == 0 || n == 0) return BI_OK;
@@ -57,9 +58,12 @@ bi_status check_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, int
   if (k > 0 && (!aligned(a, 16) || !aligned(b, 16) || lda % 8 != 0 || ldb % 8 != 0))
     return fail(BI_ERR_ALIGN, "a/b must be 16-byte aligned with lda, ldb multiples of 8");
   if (!aligned(c, dsize(c_dtype))) return fail(BI_ERR_ALIGN, "c is not aligned to its element size");
-  const bi::GemmConfig cfg = bi::gemm_config(m, n, k, b_is_nk != 0);
-  const int64_t tiles = ((m + cfg.tile_m - 1) / cfg.tile_m) * ((n + cfg.tile_n - 1) / cfg.tile_n);
-  if (tiles > INT_MAX) return fail(BI_ERR_UNSUPPORTED, "too many output tiles");
+  const bi::GemmPlan plan = bi::gemm_plan(m, n, k, b_is_nk != 0, (flags & BI_GEMM_FIXED_TILE) != 0);
+  for (int i = 0; i < plan.count; ++i) {
+    const bi::GemmLaunch& L = plan.launch[i];
+    const int64_t tiles = ((m + L.cfg.tile_m - 1) / L.cfg.tile_m) * ((L.n_end - L.n_begin + L.cfg.tile_n - 1) / L.cfg.tile_n);
+    if (tiles > INT_MAX) return fail(BI_ERR_UNSUPPORTED, "too many output tiles");
+  }
   // the kernels address one tile's rows of A and B through 32-bit buffer
   // descriptors: a tile's byte extent must stay below 2^31. Checked for the
   // largest tile of any configuration (256 rows of A; 256 rows of B stored
@@ -73,7 +77,7 @@ bi_status check_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, int
 
 bi_status run_gemm(const void* bias, bi_dtype bias_dtype, float beta, float alpha, const void* a, int64_t lda,
                    const void* b, int64_t ldb, int b_is_nk, void* c, int64_t ldc, bi_dtype c_dtype, int64_t m,
-                   int64_t n, int64_t k, hipStream_t stream) {
+                   int64_t n, int64_t k, hipStream_t stream, int flags = 0) {
   bi::GemmParams p;
   p.a = a;
   p.b = b;
@@ -90,6 +94,7 @@ bi_status run_gemm(const void* bias, bi_dtype bias_dtype, float beta, float alph
   p.b_is_nk = b_is_nk != 0;
   p.c_bf16 = c_dtype == BI_BF16;
   p.bias_bf16 = bias_dtype == BI_BF16;
+  p.fixed_tile = (flags & BI_GEMM_FIXED_TILE) != 0;
   return hip_status(bi::launch_gemm(p, stream), "gemm launch");
 }
 
@@ -115,6 +120,41 @@ bi_status bi_addmm(const void* bias, bi_dtype bias_dtype, float beta, float alph
   if (bias == nullptr) return fail(BI_ERR_NULL, "bias is NULL");
   if (!aligned(bias, dsize(bias_dtype))) return fail(BI_ERR_ALIGN, "bias is not aligned to its element size");
   return run_gemm(bias, bias_dtype, beta, alpha, a, lda, b, ldb, b_is_nk, c, ldc, c_dtype, m, n, k, stream);
+}
+
+bi_status bi_gemm(const void* bias, bi_dtype bias_dtype, float beta, float alpha, const void* a, int64_t lda,
+                  const void* b, int64_t ldb, int b_is_nk, void* c, int64_t ldc, bi_dtype c_dtype, int64_t m,
+                  int64_t n, int64_t k, int flags, hipStream_t stream) {
+  if (bias != nullptr && !valid_dtype(bias_dtype))
+    return fail(BI_ERR_DTYPE, "bias_dtype %d is not BI_BF16 or BI_F32", (int)bias_dtype);
+  bi_status st = check_gemm(a, lda, b, ldb, b_is_nk, c, ldc, c_dtype, m, n, k, flags);
+  if (st != BI_OK) return st;
+  if (m == 0 || n == 0) return ok();
+  if (bias != nullptr && !aligned(bias, dsize(bias_dtype)))
+    return fail(BI_ERR_ALIGN, "bias is not aligned to its element size");
+  if (bias == nullptr) {  // mm: C = alpha * (A @ B)
+    bias_dtype = BI_F32;
+    beta = 0.0f;
+  }
+  return run_gemm(bias, bias_dtype, beta, alpha, a, lda, b, ldb, b_is_nk, c, ldc, c_dtype, m, n, k, stream, flags);
+}
+
+bi_status bi_gemm_plan(int64_t m, int64_t n, int64_t k, int b_is_nk, int flags, int32_t* out10, int32_t* count) {
+  if (out10 == nullptr || count == nullptr) return fail(BI_ERR_NULL, "out10 or count is NULL");
+  if (m < 0 || n < 0 || k < 0) return fail(BI_ERR_SHAPE, "negative size");
+  if (flags & ~BI_GEMM_FIXED_TILE) return fail(BI_ERR_UNSUPPORTED, "unknown GEMM flags 0x%x", flags);
+  const bi::GemmPlan plan = bi::gemm_plan(m, n, k, b_is_nk != 0, (flags & BI_GEMM_FIXED_TILE) != 0);
+  *count = plan.count;
+  for (int i = 0; i < 2; ++i) {
+    const bi::GemmLaunch& L = plan.launch[i];
+    const bool used = i < plan.count;
+    out10[5 * i + 0] = used ? L.cfg.tile_m : 0;
+    out10[5 * i + 1] = used ? L.cfg.tile_n : 0;
+    out10[5 * i + 2] = used ? L.cfg.tile_k : 0;
+    out10[5 * i + 3] = used ? L.cfg.waves : 0;
+    out10[5 * i + 4] = used ? (int32_t)L.n_begin : 0;
+  }
+  return ok();
 }
 
 bi_status bi_gemm_config(int64_t m, int64_t n, int64_t k, int b_is_nk, int32_t* out4) {

@@ -17,6 +17,21 @@ struct GemmConfig {
 // Every configuration computes each element with the same chain, so the
 // choice never changes a bit (see gemm.hip).
 GemmConfig gemm_config(int64_t m, int64_t n, int64_t k, bool b_is_nk);
+// The configuration of the fixed-tile mode (BI_GEMM_FIXED_TILE): a function
+// of (n, k, layout) only, the same for every m.
+GemmConfig gemm_config_fixed(int64_t n, int64_t k, bool b_is_nk);
+
+// The launches one GEMM call makes: up to two, each a configuration applied
+// to the output columns [n_begin, n_end).
+struct GemmLaunch {
+  GemmConfig cfg;
+  int64_t n_begin, n_end;
+};
+struct GemmPlan {
+  int count;
+  GemmLaunch launch[2];
+};
+GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k, bool b_is_nk, bool fixed_tile);
 
 struct GemmParams {
   const void* a;
@@ -29,6 +44,7 @@ struct GemmParams {
   bool b_is_nk;
   bool c_bf16;
   bool bias_bf16;
+  bool fixed_tile;  // BI_GEMM_FIXED_TILE
 };
 hipError_t launch_gemm(const GemmParams& p, hipStream_t stream);
 

@@ -770,6 +770,20 @@ GemmConfig gemm_config(int64_t m, int64_t n, int64_t k, bool b_is_nk) {
   return GemmConfig{128, 128, TK, 4};
 }
 
+// The fixed-tile mode: one configuration per (N, K, layout), whatever M is
+// -- the letter of "one tile config for all M". 256x256 (8 waves) once N
+// spans at least 16 tile columns (every projection shape and the LM head),
+// 128x128 (4 waves) for narrower N; no column split (where it splits
+// depends on M). Its bits are those of gemm_config's table, since every
+// configuration runs the same chain; it exists to measure what choosing the
+// tile by M gains.
+GemmConfig gemm_config_fixed(int64_t n, int64_t k, bool b_is_nk) {
+  (void)k;
+  (void)b_is_nk;
+  if (n >= 16 * 256 - 255) return GemmConfig{256, 256, TK, 8};
+  return GemmConfig{128, 128, TK, 4};
+}
+
 // Columns of a 256x256 GEMM left to full rounds of 256x256 tiles; the rest
 // (if any) goes to 256x128 tiles in a second launch. Whole rounds of 256 CUs
 // need tiles_m * n1 to be a multiple of 256. A round of 256x128 tiles takes
@@ -788,25 +802,47 @@ static int64_t full_round_columns(int64_t tiles_m, int64_t tiles_n, int64_t m, i
   return split < whole - 0.05 ? n1 : tiles_n;
 }
 
-hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
-  const GemmConfig cfg = gemm_config(p.m, p.n, p.k, p.b_is_nk);
+GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k, bool b_is_nk, bool fixed_tile) {
+  GemmPlan plan{};
+  const GemmConfig cfg = fixed_tile ? gemm_config_fixed(n, k, b_is_nk) : gemm_config(m, n, k, b_is_nk);
+  plan.count = 1;
+  plan.launch[0] = GemmLaunch{cfg, 0, n};
+  if (!fixed_tile && cfg.tile_m == 256 && cfg.tile_n == 256) {
+    const int64_t tiles_m = (m + 255) / 256, tiles_n = (n + 255) / 256;
+    const int64_t n1 = full_round_columns(tiles_m, tiles_n, m, n);
+    if (n1 < tiles_n) {
+      plan.count = 2;
+      plan.launch[0].n_end = n1 * 256;
+      plan.launch[1] = GemmLaunch{GemmConfig{256, 128, TK, 8}, n1 * 256, n};
+    }
+  }
+  return plan;
+}
+
+// One launch of the plan: the columns [n0, n1) of the output, with B, C and
+// the bias offset to column n0.
+static hipError_t launch_part(const GemmParams& p, const GemmLaunch& L, hipStream_t s) {
+  const GemmConfig& cfg = L.cfg;
+  const int64_t off = L.n_begin;
   GemmArgs a;
   a.a = static_cast<const uint16_t*>(p.a);
-  a.b = static_cast<const uint16_t*>(p.b);
-  a.c = p.c;
-  a.bias = p.bias;
+  a.b = p.b_is_nk ? static_cast<const uint16_t*>(p.b) + off * p.ldb : static_cast<const uint16_t*>(p.b) + off;
+  a.c = p.c_bf16 ? (void*)(static_cast<uint16_t*>(p.c) + off) : (void*)(static_cast<float*>(p.c) + off);
+  a.bias = p.bias == nullptr ? nullptr
+           : p.bias_bf16     ? (const void*)(static_cast<const uint16_t*>(p.bias) + off)
+                             : (const void*)(static_cast<const float*>(p.bias) + off);
   a.lda = p.lda;
   a.ldb = p.ldb;
   a.ldc = p.ldc;
   a.m = (int)p.m;
-  a.n = (int)p.n;
+  a.n = (int)(L.n_end - off);
   a.k = (int)p.k;
   a.alpha = p.alpha;
   a.beta = p.beta;
   a.out_bf16 = p.c_bf16 ? 1 : 0;
   a.bias_mode = p.bias == nullptr ? 0 : (p.bias_bf16 ? 1 : 2);
   a.tiles_m = (int)((p.m + cfg.tile_m - 1) / cfg.tile_m);
-  a.tiles_n = (int)((p.n + cfg.tile_n - 1) / cfg.tile_n);
+  a.tiles_n = (int)((a.n + cfg.tile_n - 1) / cfg.tile_n);
   if (cfg.tile_n == 32) {  // skinny: 16-stage ring with one consumer, 12 with two
     if (cfg.tile_m == 32)
       return p.b_is_nk ? launch_ring<1, 1, 1, 1, 2, 16, true>(a, s) : launch_ring<1, 1, 1, 1, 2, 16, false>(a, s);
@@ -818,31 +854,23 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
     return p.b_is_nk ? launch_ring<2, 2, 2, 2, 2, 4, true>(a, s) : launch_ring<2, 2, 2, 2, 2, 4, false>(a, s);
   if (cfg.tile_m == 64 && cfg.tile_n == 128)  // 1x2 consumers of 64x64, 6-stage ring
     return p.b_is_nk ? launch_ring<1, 2, 2, 2, 2, 6, true>(a, s) : launch_ring<1, 2, 2, 2, 2, 6, false>(a, s);
-  if (cfg.tile_m == 256 && cfg.tile_n == 256) {
-    const int64_t n1 = full_round_columns(a.tiles_m, a.tiles_n, p.m, p.n);
-    if (n1 < a.tiles_n) {
-      const int64_t off = n1 * 256;  // first column of the 256x128 part
-      GemmArgs a2 = a;
-      a.n = (int)off;
-      a.tiles_n = (int)n1;
-      a2.b = p.b_is_nk ? a2.b + off * p.ldb : a2.b + off;
-      a2.c = p.c_bf16 ? (void*)(static_cast<uint16_t*>(p.c) + off) : (void*)(static_cast<float*>(p.c) + off);
-      if (a2.bias_mode == 1) a2.bias = static_cast<const uint16_t*>(p.bias) + off;
-      if (a2.bias_mode == 2) a2.bias = static_cast<const float*>(p.bias) + off;
-      a2.n = (int)(p.n - off);
-      a2.tiles_n = (int)((p.n - off + 127) / 128);
-      const hipError_t e = p.b_is_nk ? launch_cfg<256, 256, 2, 4, true>(a, s) : launch_cfg<256, 256, 2, 4, false>(a, s);
-      if (e != hipSuccess) return e;
-      return p.b_is_nk ? launch_cfg<256, 128, 4, 2, true>(a2, s) : launch_cfg<256, 128, 4, 2, false>(a2, s);
-    }
-  }
 #define BI_GEMM_CASE(TM_, TN_, WM_, WN_)                                                          \
   if (cfg.tile_m == TM_ && cfg.tile_n == TN_ && cfg.waves == WM_ * WN_)                            \
     return p.b_is_nk ? launch_cfg<TM_, TN_, WM_, WN_, true>(a, s) : launch_cfg<TM_, TN_, WM_, WN_, false>(a, s);
   BI_GEMM_CASE(128, 128, 2, 2)
   BI_GEMM_CASE(256, 256, 2, 4)
+  BI_GEMM_CASE(256, 128, 4, 2)
 #undef BI_GEMM_CASE
   return hipErrorInvalidConfiguration;
+}
+
+hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
+  const GemmPlan plan = gemm_plan(p.m, p.n, p.k, p.b_is_nk, p.fixed_tile);
+  for (int i = 0; i < plan.count; ++i) {
+    const hipError_t e = launch_part(p, plan.launch[i], s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace bi

@@ -84,12 +84,21 @@ class Decoder:
                                     device=device) for _ in range(s.layers)]
         self.device = device
 
-    def _layers(self, x, positions, lens_dev, offs_dev, total, ws, block_table):
-        """The kernels of one step after the embedding; returns (logits, log-probs, greedy tokens)."""
+    def _layers(self, x, positions, lens_dev, offs_dev, total, ws, block_table, tap=None):
+        """The kernels of one step after the embedding; returns (logits, log-probs, greedy tokens).
+
+        tap: optional callable tap(layer, name, tensor), called in stream
+        order right after each stored activation is produced (names: x_in and
+        h_in of layer 0, then per layer qkv, q, att, o, x_mid, h_mid, gu, act, dn,
+        x_out, h_out; the residual x is updated in place, so a tap that keeps
+        a value must copy it). For tests that compare every step of the chain."""
         s, w = self.s, self.w
         nk = bool(w.get("b_is_nk", False))
         bsz = x.shape[0]
         h = bi_rmsnorm(x, w["w_in"][0], s.eps)
+        if tap:
+            tap(0, "x_in", x)
+            tap(0, "h_in", h)
         for l in range(s.layers):
             qkv = bi_mm(h, w["w_qkv"][l], b_is_nk=nk, out_dtype=torch.bfloat16)
             q = bi_qknorm_rope_append(qkv, w["q_norm"][l], w["k_norm"][l], w["cos"], w["sin"], positions,
@@ -99,10 +108,20 @@ class Decoder:
                                     workspace=ws, out_dtype=torch.bfloat16, split_tokens=s.split_tokens,
                                     stream_kv=True)
             o = bi_mm(a.view(bsz, s.hidden), w["w_o"][l], b_is_nk=nk, out_dtype=torch.bfloat16)
+            if tap:
+                for name, t in (("qkv", qkv), ("q", q), ("att", a.view(bsz, s.hidden)), ("o", o)):
+                    tap(l, name, t)
             h = bi_add_rmsnorm(x, o, w["w_post"][l], s.eps)
+            if tap:
+                tap(l, "x_mid", x)
+                tap(l, "h_mid", h)
             gu = bi_mm(h, w["w_gu"][l], b_is_nk=nk, out_dtype=torch.bfloat16)
-            dn = bi_mm(bi_silu_mul(gu), w["w_down"][l], b_is_nk=nk, out_dtype=torch.bfloat16)
+            act = bi_silu_mul(gu)
+            dn = bi_mm(act, w["w_down"][l], b_is_nk=nk, out_dtype=torch.bfloat16)
             h = bi_add_rmsnorm(x, dn, w["w_in"][l + 1] if l + 1 < s.layers else w["w_final"], s.eps)
+            if tap:
+                for name, t in (("gu", gu), ("act", act), ("dn", dn), ("x_out", x), ("h_out", h)):
+                    tap(l, name, t)
         logits = bi_addmm(w["b_lm"], h, w["w_lm"], b_is_nk=nk)
         logp, nxt = bi_log_softmax(logits)
         return logits, logp, nxt
@@ -112,10 +131,11 @@ class Decoder:
         for up to max_steps successive steps (see GraphStep)."""
         return GraphStep(self, batch, max_steps)
 
-    def step(self, tokens: torch.Tensor, batch: Batch):
+    def step(self, tokens: torch.Tensor, batch: Batch, tap=None):
         """Run one token per sequence. tokens: device int64 [B]. Appends the
         tokens' k, v to the cache and advances batch.lens. Returns (fp32
-        logits [B, V], fp32 log-probabilities [B, V], greedy tokens int64 [B])."""
+        logits [B, V], fp32 log-probabilities [B, V], greedy tokens int64 [B]).
+        tap: see _layers."""
         s, w = self.s, self.w
         bsz = tokens.shape[0]
         dev = self.device
@@ -129,7 +149,7 @@ class Decoder:
         ws = torch.empty(bi_decode_workspace_bytes(total, s.num_q_heads, s.head_dim), dtype=torch.uint8, device=dev)
 
         x = bi_embed(w["embed"], tokens)
-        logits, logp, nxt = self._layers(x, positions, lens_dev, offs_dev, total, ws, batch.block_table)
+        logits, logp, nxt = self._layers(x, positions, lens_dev, offs_dev, total, ws, batch.block_table, tap)
         batch.lens = lens_after
         return logits, logp, nxt
 

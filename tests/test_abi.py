@@ -309,3 +309,46 @@ def test_binding_refuses_host_tensors_before_any_launch(bi):
         bi.bi_decode_attention(q, kp, vp, bt, lens, offs[:2], total)
     with pytest.raises(ValueError, match="block_table"):
         bi.bi_decode_attention(q, kp, vp, bt[:1], lens, offs, total)
+
+
+def test_gemm_plan_and_fixed_tile_mode(bi):
+    """bi_gemm_plan reports the launches: the M-keyed table changes its tile
+    with M and splits the LM head's columns at M = 256; the fixed-tile mode
+    uses one configuration per (N, K, layout) for every M and never splits."""
+    plan = bi.bi_gemm_plan(256, 151936, 4096)
+    assert len(plan) == 2 and plan[0][:4] == (256, 256, 64, 8) and plan[1][:2] == (256, 128)
+    assert plan[0][4] == 0 and plan[1][4] % 256 == 0 and 0 < plan[1][4] < 151936
+    for n, k in ((6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288), (151936, 4096), (512, 512)):
+        for nk in (False, True):
+            table = {bi.bi_gemm_plan(m, n, k, nk)[0][:4] for m in range(1, 4097, 7)}
+            fixed = {tuple(bi.bi_gemm_plan(m, n, k, nk, fixed_tile=True)) for m in range(1, 4097, 7)}
+            assert len(fixed) == 1 and len(next(iter(fixed))) == 1, (n, k, fixed)
+            assert len(table) >= 2, (n, k, table)
+    assert bi.bi_gemm_plan(8, 512, 512, fixed_tile=True)[0][:4] == (128, 128, 64, 4)
+    # the first entry of the plan is what bi_gemm_config reports
+    for m in (1, 64, 65, 512, 4096):
+        assert bi.bi_gemm_plan(m, 6144, 4096)[0][:4] == bi.bi_gemm_config(m, 6144, 4096)
+    out, cnt = (ctypes.c_int32 * 10)(), ctypes.c_int32()
+    assert bi.lib.bi_gemm_plan(4, 512, 512, 0, 2, out, ctypes.byref(cnt)) == UNSUPPORTED
+    assert bi.lib.bi_gemm_plan(-1, 512, 512, 0, 0, out, ctypes.byref(cnt)) == SHAPE
+    assert bi.lib.bi_gemm_plan(4, 512, 512, 0, 0, None, ctypes.byref(cnt)) == NULL
+    # bi_gemm validates like bi_mm/bi_addmm, plus the flags
+    g = lambda flags=0, bias=None, m=4: bi.lib.bi_gemm(bias, 0, 1.0, 1.0, A16, 512, A16, 512, 0, A16, 512, 1,  # noqa: E731
+                                                       m, 512, 512, flags, None)
+    assert g(flags=4) == UNSUPPORTED and g(flags=1, m=-1) == SHAPE and g(bias=0x10001) == ALIGN
+    assert g(m=0) == OK and g(flags=1, m=0) == OK
+
+
+def test_qwen_shapes_walk_every_gemm_configuration(bi):
+    """Over M = 1..4096 the four Qwen3-8B projection shapes (either layout)
+    take every configuration of the tile table between them, and the 256x128
+    column split: so the every-M GPU sweep on those shapes runs them all."""
+    table = {(32, 32, 64, 3), (64, 32, 64, 4), (64, 128, 64, 4), (128, 128, 64, 6), (128, 128, 64, 4),
+             (256, 256, 64, 8)}
+    seen, split = set(), False
+    for k, n in ((4096, 6144), (4096, 4096), (4096, 24576), (12288, 4096)):
+        for m in range(1, 4097):
+            plan = bi.bi_gemm_plan(m, n, k)
+            seen |= {p[:4] for p in plan[:1]}
+            split |= len(plan) == 2 and plan[1][:4] == (256, 128, 64, 8)
+    assert seen == table and split, (seen, split)

@@ -215,6 +215,70 @@ def test_decoder_nn_linear_layout_gives_the_same_logits():
     with pytest.raises(ValueError):
         OracleDecoder(dict(w, b_is_nk=True), 2, 4, 1, 1e-6, caches).step(np.array([3, 11]))
 
+# ------------------------------------------------------------------ near-tie rounding decisions
+def test_round_at_takes_the_kernel_neighbour_only_at_near_ties():
+    from oracle.decode_step import TIE_WINDOW, round_at
+    ulp = 2.0 ** -7                       # bf16 spacing in [1, 2)
+    mid = 1.0 + ulp / 2                   # midpoint between 1 and 1 + ulp
+    w = TIE_WINDOW * ulp
+    one, up = bits(np.array([1.0])), bits(np.array([1.0 + ulp]))
+    # on the midpoint: RNE gives 1.0 (even); a kernel that stored 1 + ulp is adopted
+    got, n = round_at(np.array([mid]), up)
+    assert got[0] == 1.0 + ulp and n == 1
+    # just above the midpoint, inside the window: RNE gives 1 + ulp; the kernel's 1.0 is adopted
+    got, n = round_at(np.array([mid + w / 2]), one)
+    assert got[0] == 1.0 and n == 1
+    # outside the window the oracle's own rounding stands
+    got, n = round_at(np.array([mid + 2 * w]), one)
+    assert got[0] == 1.0 + ulp and n == 0
+    # a kernel value that is not the other neighbour is never adopted, even on a midpoint
+    got, n = round_at(np.array([mid]), bits(np.array([1.0 + 2 * ulp])))
+    assert got[0] == 1.0 and n == 0
+    got, n = round_at(np.array([mid]), bits(np.array([-(1.0 + ulp)])))
+    assert got[0] == 1.0 and n == 0
+    # agreeing values, and no kernel values at all, give plain round_bf16
+    u = np.random.default_rng(8).standard_normal(1000) * 7
+    r = O.round_bf16(u)
+    assert np.array_equal(round_at(u, O.bf16_bits_of(r))[0], r) and np.array_equal(round_at(u)[0], r)
+    # negative values: the midpoint between -1 and -(1 + ulp)
+    got, n = round_at(np.array([-mid]), bits(np.array([-(1.0 + ulp)])))
+    assert got[0] == -(1.0 + ulp) and n == 1
+
+
+def test_decoder_layer_feed_and_tie_with_its_own_values_change_nothing():
+    """Feeding a layer its own stored activations, or offering its own
+    roundings as the kernel's, reproduces the plain step bit for bit and
+    takes no decision from outside; feeding a different value changes what
+    follows (the feed is used)."""
+    from oracle.decode_step import LAYER_ROUNDINGS
+    rng = np.random.default_rng(9)
+    w = _tiny_weights(rng, layers=2, max_pos=32)
+    caches = [[(rand_bf16(rng, (L, 1, 128)), rand_bf16(rng, (L, 1, 128))) for _ in range(2)] for L in (3, 20)]
+    toks = np.array([4, 17])
+    plain = OracleDecoder(w, 2, 4, 1, 1e-6, caches)
+    ref = plain.step(toks)
+    vals = dict(plain.values)
+    own = {key: O.bf16_bits_of(O.round_bf16(v)) for key, v in vals.items() if key[1] != "v"}
+    tied = OracleDecoder(w, 2, 4, 1, 1e-6, caches)
+    assert np.array_equal(tied.step(toks, tie=own), ref) and sum(tied.ties.values()) == 0
+    assert {name for (_, name) in vals} == set(LAYER_ROUNDINGS) | {"v"}
+    # layer 1 alone from the stored layer-0 outputs, fed its own activations: same values
+    x1, h1 = own[(0, "x_out")], own[(0, "h_out")]
+    for feed in ({}, {name: b for (l, name), b in own.items() if l == 1}):
+        d = OracleDecoder(w, 2, 4, 1, 1e-6, caches)
+        d.kv = [[plain.kv[s][0], (plain.kv[s][1][0][:-1], plain.kv[s][1][1][:-1])] for s in range(2)]
+        v1, st1 = d.layer(1, x1, h1, [0, 1], feed=feed)
+        for name in LAYER_ROUNDINGS[1:]:
+            assert np.array_equal(v1[name], vals[(1, name)]), name
+    # a fed activation replaces the oracle's own downstream
+    d = OracleDecoder(w, 2, 4, 1, 1e-6, caches)
+    d.kv = [[plain.kv[s][0], (plain.kv[s][1][0][:-1], plain.kv[s][1][1][:-1])] for s in range(2)]
+    bent = own[(1, "o")].copy()
+    bent[0, 0] ^= 0x40
+    v1, _ = d.layer(1, x1, h1, [0, 1], feed={"o": bent})
+    assert not np.array_equal(v1["x_mid"], vals[(1, "x_mid")])
+
+
 # ------------------------------------------------------------------ prefill attention
 def _paged(rng, lens, hkv=1, page=16):
     pages = sum((L + page - 1) // page for L in lens)

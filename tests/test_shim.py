@@ -2,21 +2,32 @@
 
 GPU cases check that, inside ``batch_invariant_mode``, torch's own mm /
 addmm / linear / log_softmax / mean / rms_norm calls return exactly the
-bytes the C-ABI kernels return for the same operands, and that a small
-bf16 model run through unchanged torch code gives each row the same bytes
-at every batch size.
+bytes the C-ABI kernels return for the same operands and meet the fp64
+oracle's tolerances, that a small bf16 model run through unchanged torch
+code matches the oracle's composition of the same ops, and that it gives
+each row the same bytes at every batch size.
 """
+import numpy as np
 import pytest
 import torch
 import torch.nn.functional as F
 
+import oracle as O
 import synthetic as S
-from helpers import same_bits
+from helpers import ELEM_TOL, assert_close, bits, f32, same_bits
 
 DEV = "cuda"
 
 
 # ---------------------------------------------------------------- CPU: routing logic
+def close_bf16(got, ref, what):
+    """A bf16 result is one rounding of its exact value: rel-Frobenius
+    <= 2^-8 and the elementwise bound against the unrounded oracle."""
+    g = f32(got.float()).astype(np.float64).reshape(ref.shape)
+    fro, el = O.relative_frobenius(g, ref), O.elementwise_ratio(g, ref)
+    assert fro <= 2.0 ** -8 and el <= ELEM_TOL, f"{what}: rel-Frobenius {fro:.3e}, elementwise {el:.3e}"
+
+
 def test_gemm_operands_layouts():
     from invariant_bi_mm_amd.shim import gemm_operands
     a = torch.zeros(4, 64, dtype=torch.bfloat16)
@@ -69,6 +80,11 @@ def test_mm_linear_route_to_kernels(lib):
     assert same_bits(y_mm, lib.bi_mm(x[1], w_kn, out_dtype=torch.bfloat16))
     if y_mm32 is not None:
         assert same_bits(y_mm32, lib.bi_mm(x[1], w_kn))
+        assert_close(f32(y_mm32), O.mm(bits(x[1]), bits(w_kn)), "routed mm fp32 vs oracle")
+    # the routed results against the fp64 oracle
+    close_bf16(y_lin.reshape(-1, 768), O.mm(bits(x.reshape(-1, 512)), bits(w), b_is_nk=True), "routed linear")
+    close_bf16(y_lin_b, O.addmm(bits(b), bits(x[0]), bits(w), b_is_nk=True), "routed linear + bias")
+    close_bf16(y_mm, O.mm(bits(x[1]), bits(w_kn)), "routed x @ w")
 
 
 @pytest.mark.gpu
@@ -88,6 +104,12 @@ def test_reductions_route_to_kernels(lib):
     assert same_bits(mu.reshape(-1), lib.bi_mean(h.reshape(-1, 4096)).to(torch.bfloat16))
     assert mu_k.shape == (3, 7, 1) and same_bits(mu_k.reshape(-1), lib.bi_mean(h.float().reshape(-1, 4096)))
     assert same_bits(rn.reshape(-1, 4096), lib.bi_rmsnorm(h.reshape(-1, 4096), w, 1e-6))
+    # the routed results against the fp64 oracle
+    assert_close(f32(ls), O.log_softmax(f32(logits)), "routed log_softmax")
+    hb = bits(h.reshape(-1, 4096))
+    close_bf16(mu.reshape(-1), O.mean(hb), "routed mean (bf16)")
+    assert_close(f32(mu_k.reshape(-1)), O.mean(f32(h.float().reshape(-1, 4096))), "routed mean (fp32)")
+    close_bf16(rn.reshape(-1, 4096), O.rmsnorm(hb, bits(w), 1e-6), "routed rms_norm")
 
 
 @pytest.mark.gpu
@@ -118,11 +140,60 @@ class TinyLM(torch.nn.Module):
         self.n1 = torch.nn.Parameter(S.uniform_bf16((d,), 0.5, 1.5, seed=seed + 5, device=DEV), requires_grad=False)
         self.n2 = torch.nn.Parameter(S.uniform_bf16((d,), 0.5, 1.5, seed=seed + 6, device=DEV), requires_grad=False)
 
-    def forward(self, x):
-        h = F.rms_norm(x, (x.shape[-1],), weight=self.n1, eps=1e-6)
-        h = x + F.linear(F.silu(F.linear(h, self.w_up)), self.w_down)
-        h = F.rms_norm(h, (h.shape[-1],), weight=self.n2, eps=1e-6)
-        return F.log_softmax(F.linear(h, self.w_head, self.b_head).float(), dim=-1)
+    def forward(self, x, keep=None):
+        """keep: optional dict that receives each stored bf16 activation."""
+        keep = {} if keep is None else keep
+        keep["h1"] = h = F.rms_norm(x, (x.shape[-1],), weight=self.n1, eps=1e-6)
+        keep["up"] = u = F.linear(h, self.w_up)
+        keep["silu"] = a = F.silu(u)
+        keep["down"] = d = F.linear(a, self.w_down)
+        keep["res"] = r = x + d
+        keep["h2"] = h = F.rms_norm(r, (r.shape[-1],), weight=self.n2, eps=1e-6)
+        keep["logits"] = z = F.linear(h, self.w_head, self.b_head)
+        return F.log_softmax(z.float(), dim=-1)
+
+
+def oracle_tinylm(model, x_bits, tie):
+    """TinyLM's forward composed from the oracle's ops in fp64, each bf16
+    activation rounded where the model stores it. tie: the model's stored
+    bf16 values, used only at near-ties (the near-tie rule of
+    oracle.decode_step.round_at). Returns (values before rounding, fp64
+    log-probabilities)."""
+    from oracle.decode_step import round_at
+    p = {k: bits(v.detach()) for k, v in model.named_parameters()}
+    vals = {}
+
+    def keep(name, u):
+        vals[name] = u
+        return O.bf16_bits_of(round_at(u, tie[name])[0])
+
+    h = keep("h1", O.rmsnorm(x_bits, p["n1"], 1e-6))
+    u = keep("up", O.mm(h, p["w_up"], b_is_nk=True))
+    # silu alone: the gated form with an up part of ones
+    a = keep("silu", O.silu_mul(np.concatenate([u, np.full_like(u, 0x3F80)], axis=1)))
+    d = keep("down", O.mm(a, p["w_down"], b_is_nk=True))
+    r = keep("res", O.bf16_bits_to_f64(x_bits) + O.bf16_bits_to_f64(d))
+    h2 = keep("h2", O.rmsnorm(r, p["n2"], 1e-6))
+    z = keep("logits", O.addmm(p["b_head"], h2, p["w_head"], b_is_nk=True))
+    return vals, O.log_softmax(O.bf16_bits_to_f64(z).astype(np.float32))
+
+
+@pytest.mark.gpu
+def test_unchanged_model_code_matches_oracle(lib):
+    """The TinyLM's routed forward against the oracle's composition of the
+    same ops: every stored bf16 activation at the bf16 tolerance and the fp32
+    log-probabilities at 1e-3 / 4e-3."""
+    from invariant_bi_mm_amd.shim import batch_invariant_mode
+    model = TinyLM()
+    x = S.normal_bf16((64, 512), 1.0, seed=70, device=DEV)
+    acts = {}
+    with batch_invariant_mode():
+        logp = model(x, keep=acts)
+    tie = {k: bits(v) for k, v in acts.items()}
+    vals, ref = oracle_tinylm(model, bits(x), tie)
+    for name, u in vals.items():
+        close_bf16(acts[name], u, f"TinyLM {name}")
+    assert_close(f32(logp), ref, "TinyLM log-probabilities")
 
 
 @pytest.mark.gpu
