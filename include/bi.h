@@ -40,8 +40,9 @@
  *  - Alignment: base pointers 16-byte aligned, ld* a multiple of 8 for bf16
  *    and of 4 for fp32 operands (128-bit loads); otherwise BI_ERR_ALIGN.
  *  - Outputs must not overlap inputs (undefined behaviour, not checked).
- *  - The library keeps no mutable global state; calls are re-entrant and may
- *    be issued from several host threads. Error messages are thread-local.
+ *  - Calls are re-entrant and may be issued from several host threads; error
+ *    messages are thread-local. The only state the library keeps is the
+ *    scratch of bi_decode_attention_noalloc (one per GPU, see there).
  */
 #ifndef BI_H_
 #define BI_H_
@@ -255,6 +256,34 @@ bi_status bi_decode_attention(const void* q, const void* k_pages, const void* v_
                               int page_size, int split_tokens, float scale,
                               void* workspace, size_t workspace_bytes,
                               void* out, bi_dtype out_dtype, int flags, hipStream_t stream);
+
+/* bi_decode_attention_noalloc: bi_decode_attention without the workspace
+ * argument, for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * allocation. The split partials go to a scratch array the library holds in
+ * device memory (BI_DECODE_NOALLOC_MAX_BYTES per GPU it runs on, reserved
+ * when the library's code is loaded on that GPU and kept until the process
+ * ends). The call allocates nothing; the caller passes inputs and outputs
+ * as for bi_decode_attention, with the same requirements, and gets the same
+ * bits (same kernels).
+ * Limit: bi_decode_workspace_bytes(total_splits, num_q_heads, head_dim)
+ * must not exceed BI_DECODE_NOALLOC_MAX_BYTES (64 MiB: 4032 splits of 256
+ * tokens at 32 query heads, ~1M cached tokens per call); larger calls return
+ * BI_ERR_WORKSPACE and launch nothing.
+ * All calls on one GPU share the scratch: calls that overlap in time on one
+ * GPU (different streams, or host threads) race and give undefined results;
+ * calls in one stream are ordered and safe. The stream must belong to the
+ * current device (BI_ERR_UNSUPPORTED otherwise). The first call on a device
+ * looks the scratch's address up (hipGetSymbolAddress); a failure there is
+ * BI_ERR_HIP. */
+#define BI_DECODE_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+bi_status bi_decode_attention_noalloc(const void* q, const void* k_pages, const void* v_pages,
+                                      const int32_t* block_table, int64_t max_pages,
+                                      const int32_t* context_lens, const int32_t* split_offsets,
+                                      int64_t total_splits, int64_t batch,
+                                      int num_q_heads, int num_kv_heads, int head_dim,
+                                      int page_size, int split_tokens, float scale,
+                                      void* out, bi_dtype out_dtype, int flags, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Prefill / extend attention with the decode split structure.

@@ -21,7 +21,8 @@ import torch  # noqa: F401  (must be loaded before libbi.so, see above)
 __all__ = [
     "BiError", "LIB_PATH", "lib",
     "bi_mm", "bi_addmm", "bi_gemm", "bi_gemm_config", "bi_gemm_plan", "BI_GEMM_FIXED_TILE", "bi_rmsnorm", "bi_mean", "bi_log_softmax",
-    "bi_decode_plan", "bi_decode_workspace_bytes", "bi_decode_attention",
+    "bi_decode_plan", "bi_decode_workspace_bytes", "bi_decode_attention", "bi_decode_attention_noalloc",
+    "BI_DECODE_NOALLOC_MAX_BYTES",
     "bi_add_rmsnorm", "bi_embed", "bi_silu_mul", "bi_qknorm_rope_append",
     "bi_prefill_plan", "bi_prefill_attention", "v_pages_shape",
     "bi_status_string", "bi_last_error_message",
@@ -37,6 +38,7 @@ lib = ctypes.CDLL(LIB_PATH)
 
 BI_BF16, BI_F32 = 0, 1
 BI_GEMM_FIXED_TILE = 1
+BI_DECODE_NOALLOC_MAX_BYTES = 64 << 20
 STATUS = {0: "BI_OK", 1: "BI_ERR_NULL", 2: "BI_ERR_SHAPE", 3: "BI_ERR_STRIDE", 4: "BI_ERR_ALIGN",
           5: "BI_ERR_DTYPE", 6: "BI_ERR_WORKSPACE", 7: "BI_ERR_UNSUPPORTED", 8: "BI_ERR_HIP"}
 
@@ -68,6 +70,9 @@ lib.bi_decode_workspace_bytes.restype = _sz
 lib.bi_decode_attention.argtypes = [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
                                     _f32, _vp, _sz, _vp, _i32, _i32, _vp]
 lib.bi_decode_attention.restype = _st
+lib.bi_decode_attention_noalloc.argtypes = [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _i32,
+                                            _i32, _f32, _vp, _i32, _i32, _vp]
+lib.bi_decode_attention_noalloc.restype = _st
 lib.bi_add_rmsnorm.argtypes = [_vp, _i64, _vp, _i64, _vp, _f32, _vp, _i64, _i32, _i64, _i64, _vp]
 lib.bi_add_rmsnorm.restype = _st
 lib.bi_embed.argtypes = [_vp, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _vp]
@@ -378,6 +383,43 @@ def bi_decode_attention(q, k_pages, v_pages, block_table, context_lens, split_of
                                    workspace.numel() * workspace.element_size(),
                                    _ptr(out), _dtype_code(out.dtype), 1 if stream_kv else 0,
                                    _stream(stream, q.device)))
+    return out
+
+
+def bi_decode_attention_noalloc(q, k_pages, v_pages, block_table, context_lens, split_offsets, total_splits: int,
+                                out, *, scale: float | None = None, split_tokens: int = 256, stream_kv: bool = False,
+                                stream=None):
+    """bi_decode_attention with the library's own scratch for the split
+    partials instead of a workspace: nothing is allocated, `out` (bf16 or
+    fp32 [B, Hq, D], contiguous) is the caller's. Splits whose partials
+    exceed BI_DECODE_NOALLOC_MAX_BYTES are refused (BI_ERR_WORKSPACE)."""
+    _need_bf16(q, "q")
+    _need_bf16(k_pages, "k_pages")
+    _need_bf16(v_pages, "v_pages")
+    bsz, hq, d = q.shape
+    _, hkv, page, d2 = k_pages.shape
+    if d2 != d or v_pages.shape != v_pages_shape(k_pages):
+        raise ValueError("q/k/v shapes disagree (v_pages is [P, Hkv, D, page])")
+    for t, nm in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (block_table, "block_table"),
+                  (context_lens, "context_lens"), (split_offsets, "split_offsets"), (out, "out")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32 or split_offsets.dtype != torch.int32:
+        raise TypeError("block_table, context_lens, split_offsets must be int32")
+    if block_table.dim() != 2 or block_table.shape[0] != bsz:
+        raise ValueError(f"block_table must be [B={bsz}, max_pages], got {tuple(block_table.shape)}")
+    if context_lens.numel() != bsz or split_offsets.numel() != bsz + 1:
+        raise ValueError(f"context_lens must hold B={bsz} entries and split_offsets B+1={bsz + 1}")
+    _on_device(stream, q=q, k_pages=k_pages, v_pages=v_pages, block_table=block_table, context_lens=context_lens,
+               split_offsets=split_offsets, out=out)
+    _out_ok(out, (bsz, hq, d), (torch.float32, torch.bfloat16))
+    if scale is None:
+        scale = d ** -0.5
+    _check(lib.bi_decode_attention_noalloc(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                                           block_table.shape[1], _ptr(context_lens), _ptr(split_offsets),
+                                           int(total_splits), bsz, hq, hkv, d, page, int(split_tokens), float(scale),
+                                           _ptr(out), _dtype_code(out.dtype), 1 if stream_kv else 0,
+                                           _stream(stream, q.device)))
     return out
 
 

@@ -246,11 +246,18 @@ size_t bi_decode_workspace_bytes(int64_t total_splits, int num_q_heads, int head
   return (size_t)total_splits * (size_t)num_q_heads * (size_t)(head_dim + 2) * sizeof(float);
 }
 
-bi_status bi_decode_attention(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
-                              int64_t max_pages, const int32_t* context_lens, const int32_t* split_offsets,
-                              int64_t total_splits, int64_t batch, int num_q_heads, int num_kv_heads, int head_dim,
-                              int page_size, int split_tokens, float scale, void* workspace, size_t workspace_bytes,
-                              void* out, bi_dtype out_dtype, int flags, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and launch shared by bi_decode_attention (caller's workspace)
+// and bi_decode_attention_noalloc (the library's scratch, scratch == true:
+// workspace and workspace_bytes unused).
+bi_status decode_attention_impl(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                                int64_t max_pages, const int32_t* context_lens, const int32_t* split_offsets,
+                                int64_t total_splits, int64_t batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                int page_size, int split_tokens, float scale, void* workspace, size_t workspace_bytes,
+                                void* out, bi_dtype out_dtype, int flags, hipStream_t stream, bool scratch) {
   if (batch < 0 || total_splits < 0 || max_pages < 0) return fail(BI_ERR_SHAPE, "negative size");
   if ((flags & ~BI_DECODE_STREAM_KV) != 0) return fail(BI_ERR_UNSUPPORTED, "unknown flags 0x%x", (unsigned)flags);
   if (!valid_dtype(out_dtype)) return fail(BI_ERR_DTYPE, "out_dtype %d is not BI_BF16 or BI_F32", (int)out_dtype);
@@ -272,12 +279,24 @@ bi_status bi_decode_attention(const void* q, const void* k_pages, const void* v_
   if (total_splits * num_kv_heads > INT_MAX || batch > INT_MAX || num_kv_heads > 65535 || num_q_heads > 65535)
     return fail(BI_ERR_UNSUPPORTED, "grid size out of range");
   const size_t need = bi_decode_workspace_bytes(total_splits, num_q_heads, head_dim);
-  if (workspace == nullptr || workspace_bytes < need)
+  if (scratch && need > bi::decode_scratch_bytes())
+    return fail(BI_ERR_WORKSPACE,
+                "the no-allocation entry point's scratch holds %zu bytes; %lld splits of %d heads need %zu "
+                "(use bi_decode_attention with a workspace)",
+                bi::decode_scratch_bytes(), (long long)total_splits, num_q_heads, need);
+  if (!scratch && (workspace == nullptr || workspace_bytes < need))
     return fail(BI_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace_bytes);
-  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(workspace, 16) ||
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || (!scratch && !aligned(workspace, 16)) ||
       !aligned(out, dsize(out_dtype)) || !aligned(block_table, 4) || !aligned(context_lens, 4) ||
       !aligned(split_offsets, 4))
     return fail(BI_ERR_ALIGN, "q, k_pages, v_pages, workspace must be 16-byte aligned");
+  if (scratch) {
+    // every argument is valid: now the scratch of the device the stream runs on
+    const hipError_t e = bi::decode_scratch(stream, &workspace);
+    if (e == hipErrorInvalidDevice)
+      return fail(BI_ERR_UNSUPPORTED, "the stream is not on the current device (the scratch is looked up there)");
+    if (e != hipSuccess) return hip_status(e, "scratch lookup");
+  }
   bi::DecodeParams p;
   p.q = q;
   p.k_pages = k_pages;
@@ -297,6 +316,31 @@ bi_status bi_decode_attention(const void* q, const void* k_pages, const void* v_
   p.out_bf16 = out_dtype == BI_BF16;
   p.stream_kv = (flags & BI_DECODE_STREAM_KV) != 0;
   return hip_status(bi::launch_decode_attention(p, stream), "decode attention launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+bi_status bi_decode_attention(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                              int64_t max_pages, const int32_t* context_lens, const int32_t* split_offsets,
+                              int64_t total_splits, int64_t batch, int num_q_heads, int num_kv_heads, int head_dim,
+                              int page_size, int split_tokens, float scale, void* workspace, size_t workspace_bytes,
+                              void* out, bi_dtype out_dtype, int flags, hipStream_t stream) {
+  return decode_attention_impl(q, k_pages, v_pages, block_table, max_pages, context_lens, split_offsets, total_splits,
+                               batch, num_q_heads, num_kv_heads, head_dim, page_size, split_tokens, scale, workspace,
+                               workspace_bytes, out, out_dtype, flags, stream, false);
+}
+
+bi_status bi_decode_attention_noalloc(const void* q, const void* k_pages, const void* v_pages,
+                                      const int32_t* block_table, int64_t max_pages, const int32_t* context_lens,
+                                      const int32_t* split_offsets, int64_t total_splits, int64_t batch,
+                                      int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                                      int split_tokens, float scale, void* out, bi_dtype out_dtype, int flags,
+                                      hipStream_t stream) {
+  return decode_attention_impl(q, k_pages, v_pages, block_table, max_pages, context_lens, split_offsets, total_splits,
+                               batch, num_q_heads, num_kv_heads, head_dim, page_size, split_tokens, scale, nullptr, 0,
+                               out, out_dtype, flags, stream, true);
 }
 
 bi_status bi_prefill_plan(const int32_t* host_chunk_lens, const int32_t* host_ctx_before, int64_t batch,

@@ -76,6 +76,12 @@ struct DecodeParams {
   bool stream_kv;  // K/V loaded non-temporal
 };
 hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t stream);
+// The no-allocation entry point's scratch (decode_attention.hip): its size,
+// and its device address on the device `stream` runs on, which must be the
+// current device (hipErrorInvalidDevice otherwise). Looked up once per
+// device, on first use.
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(hipStream_t stream, void** ptr);
 
 struct PrefillParams {
   const void* q;

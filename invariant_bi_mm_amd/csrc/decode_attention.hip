@@ -31,9 +31,11 @@
 //   M = max_s m_s; l = sum_s 2^(m_s - M) l_s; o = sum_s 2^(m_s - M) o_s[d],
 //   each sum taken as 8 chains (splits s = r mod 8, increasing s) added in a
 //   fixed tree; out = o / l.
+#include "bi.h"
 #include "bi_internal.h"
 #include "device_common.h"
 
+#include <mutex>
 #include <type_traits>
 
 namespace bi {
@@ -585,7 +587,44 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const int32_t* __re
   }
 }
 
+// Scratch of bi_decode_attention_noalloc: the split partials (o, m, l) in a
+// file-scope device array instead of a caller's workspace, for callers that
+// cannot allocate. Every GPU the library runs on holds its own copy until
+// the process ends; all calls on one GPU share it (it keeps the last call's
+// partials; every partial a call reads is written earlier in the same call,
+// so nothing needs clearing), so calls that overlap on one GPU race. In host
+// code the array's name is not a device address: only the pointer from
+// hipGetSymbolAddress (decode_scratch) is passed to kernels.
+constexpr size_t SCRATCH_BYTES = BI_DECODE_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+
 }  // namespace
+
+size_t decode_scratch_bytes() { return SCRATCH_BYTES; }
+
+hipError_t decode_scratch(hipStream_t stream, void** ptr) {
+  static std::mutex mu;
+  static void* per_device[256] = {};
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return e;
+    if (sdev != cur) return hipErrorInvalidDevice;
+  }
+  if (cur < 0 || cur >= 256) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (per_device[cur] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with device `cur` current
+    if (e != hipSuccess) return e;
+    per_device[cur] = p;
+  }
+  *ptr = per_device[cur];
+  return hipSuccess;
+}
 
 hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t s) {
   SplitArgs a;
