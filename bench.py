@@ -235,6 +235,35 @@ def time_step_graph(torch, ops, steps, warmup, check=()):
     return e0.elapsed_time(e1) / steps
 
 
+def negative_control(torch, S, dev):
+    """The invariance harness on torch's own kernels: a fixed row at
+    position 0 inside batches of M random rows, compared bit for bit with
+    the same row alone; counts the Ms at which the row changed. Reported,
+    not asserted: it shows the check can see a batch-dependent kernel."""
+    k, n = 4096, 4096
+    w = S.normal_bf16((k, n), 0.02, seed=7, device=dev)
+    row = S.normal_bf16((1, k), 1.0, seed=11, device=dev)[0]
+    ref = torch.mm(row[None], w, out_dtype=torch.float32)[0].clone()
+    ms = (2, 8, 64, 512, 4096)
+    mm_changed = []
+    for m in ms:
+        x = S.normal_bf16((m, k), 1.0, seed=m, device=dev)
+        x[0] = row
+        if not torch.equal(torch.mm(x, w, out_dtype=torch.float32)[0].view(torch.int32), ref.view(torch.int32)):
+            mm_changed.append(m)
+    lg = S.normal_f32((1, VOCAB), 4.0, seed=3, device=dev)
+    ref_l = torch.log_softmax(lg, dim=-1)[0].clone()
+    ls_ms = (2, 64, 513)
+    ls_changed = []
+    for m in ls_ms:
+        x = S.normal_f32((m, VOCAB), 4.0, seed=m, device=dev)
+        x[0] = lg[0]
+        if not torch.equal(torch.log_softmax(x, dim=-1)[0].view(torch.int32), ref_l.view(torch.int32)):
+            ls_changed.append(m)
+    return {"torch_mm_K4096_N4096": {"M_tried": list(ms), "row_changed_at_M": mm_changed},
+            "torch_log_softmax_N151936": {"M_tried": list(ls_ms), "row_changed_at_M": ls_changed}}
+
+
 def gpu_clocks():
     """Shader and memory clocks as rocm-smi reports them (None where it is not available)."""
     import subprocess
@@ -255,9 +284,9 @@ def cpu_baseline(wl, S):
     the work ratio of each kernel."""
     import numpy as np
     import oracle as O
+    ncores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info, threadpool_limits
-        ncores = len(os.sched_getaffinity(0))
         threadpool_limits(ncores)
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
@@ -298,6 +327,7 @@ def cpu_baseline(wl, S):
     sample = ("oracle (numpy fp64) on: 128 rows x 2048 cols per projection GEMM, 32 rows x 4096 cols of the "
               "LM head, 16 rows of LM-head log_softmax, 256 rows of RMSNorm/mean, 32 rows of the 2048-row "
               "log_softmax, 3 decode sequences; each extrapolated to the full step by its work ratio")
+    cpu_baseline.cores = {"os_cpu_count": os.cpu_count(), "affinity_cores": ncores, "blas_threads": threads}
     return total, parts, threads, sample
 
 
@@ -331,15 +361,16 @@ def sweep(torch, S, bi):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n / 1e3
 
-    rows = ["| op | shape | M | bi us | bi rate | bi % roofline | torch us | tax (bi/torch) |",
-            "|---|---|---|---|---|---|---|---|"]
+    rows = ["| op | shape | M | bi us | bi rate | bi % roofline | torch us | tax (bi/torch) | fixed-tile us |",
+            "|---|---|---|---|---|---|---|---|---|"]
 
-    def line(op, shape, m, t, f, b, tt):
+    def line(op, shape, m, t, f, b, tt, tf=None):
         tm = t_min(f, b)
         bound_mfma = f / PEAK_BF16 >= b / PEAK_HBM
         rate = f"{f / t / 1e12:.1f} TFLOP/s" if bound_mfma else f"{b / t / 1e12:.2f} TB/s"
         rows.append(f"| {op} | {shape} | {m} | {t * 1e6:.1f} | {rate} | {100 * tm / t:.1f} | "
-                    f"{'' if tt is None else f'{tt * 1e6:.1f}'} | {'' if tt is None else f'{t / tt:.2f}'} |")
+                    f"{'' if tt is None else f'{tt * 1e6:.1f}'} | {'' if tt is None else f'{t / tt:.2f}'} | "
+                    f"{'' if tf is None else f'{tf * 1e6:.1f}'} |")
         log(rows[-1])
 
     dev = "cuda:0"
@@ -352,7 +383,8 @@ def sweep(torch, S, bi):
             c = torch.empty((m, n), device=dev)
             t = timed(lambda: bi.bi_mm(a, w, out=c))
             tt = timed(lambda: torch.mm(a, w, out_dtype=torch.float32))
-            line("bi_mm", f"K={k} N={n}", m, t, *gemm_work(m, n, k), tt)
+            tf = timed(lambda: bi.bi_gemm(a, w, out=c, fixed_tile=True))
+            line("bi_mm", f"K={k} N={n}", m, t, *gemm_work(m, n, k), tt, tf)
     k, n = HIDDEN, VOCAB
     w = S.normal_bf16((k, n), 0.02, seed=8, device=dev)
     bias = S.normal_bf16((n,), 0.1, seed=9, device=dev)
@@ -361,7 +393,8 @@ def sweep(torch, S, bi):
         c = torch.empty((m, n), device=dev)
         t = timed(lambda: bi.bi_addmm(bias, x, w, out=c), 10)
         tt = timed(lambda: torch.addmm(bias, x, w, out_dtype=torch.float32), 10)
-        line("bi_addmm (LM head)", f"K={k} N={n}", m, t, *gemm_work(m, n, k, bias=True), tt)
+        tf = timed(lambda: bi.bi_gemm(x, w, bias, out=c, fixed_tile=True), 10)
+        line("bi_addmm (LM head)", f"K={k} N={n}", m, t, *gemm_work(m, n, k, bias=True), tt, tf)
         lp = torch.empty_like(c)
         am = torch.empty((m,), dtype=torch.int64, device=dev)
         t = timed(lambda: bi.bi_log_softmax(c, out=lp, argmax=am))
@@ -526,6 +559,10 @@ def main():
                     help="measured HBM traffic per kernel (written from rocprofv3 FETCH_SIZE/WRITE_SIZE runs)")
     ap.add_argument("--sweep", action="store_true",
                     help="per-config sweep over the workloads' M values (markdown table), then exit")
+    ap.add_argument("--gemm-probe", action="store_true",
+                    help="only run each projection GEMM at M = 64, 512 and 4096 and the LM head at M = 256, "
+                         "3 launches each ([K,N] weights, fp32 out), for rocprofv3 counter and trace runs; "
+                         "prints which launch is which and exits")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for scaling the HBM counters) and exit")
     args = ap.parse_args()
@@ -538,6 +575,23 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 5}))
+        return
+    if args.gemm_probe:
+        import torch
+        import invariant_bi_mm_amd as bi
+        import synthetic as S
+        dev = "cuda:0"
+        cases = [(m, k, n) for (_, k, n) in GEMMS for m in (64, 512, 4096)] + [(M_LM, HIDDEN, VOCAB)]
+        for m, k, n in cases:
+            a = S.normal_bf16((m, k), 1.0, seed=m, device=dev)
+            w = S.normal_bf16((k, n), 0.02, seed=7, device=dev)
+            c = torch.empty((m, n), device=dev)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                bi.bi_mm(a, w, out=c)
+            torch.cuda.synchronize()
+            print(json.dumps({"M": m, "K": k, "N": n, "launches": bi.bi_gemm_plan(m, n, k), "reps": 3}), flush=True)
+            del a, w, c
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path (each GPU would run it "
@@ -623,14 +677,15 @@ def main():
                       "note": "torch.mm/addmm with out_dtype=float32 (hipBLASLt/rocBLAS as dispatched), F.rms_norm, torch.mean, "
                               "torch.log_softmax+argmax on the same tensors; decode attention has no torch "
                               "counterpart here"}
+        torch_base["negative_control"] = negative_control(torch, S, dev)
         log(f"torch baseline: {t_ms:.3f} ms/step (no decode); tax bi/torch on the same kernels "
-            f"{torch_base['invariance_tax']:.3f}x")
+            f"{torch_base['invariance_tax']:.3f}x; negative control {torch_base['negative_control']}")
 
     cpu = None
     if not args.no_cpu:
         t_cpu, parts, threads, sample = cpu_baseline(wl, S)
         cpu = {"value": 100.0 * sum_tmin_ms / (t_cpu * 1e3), "unit": "% of MI355X roofline (same step)",
-               "cores": threads, "kind": "oracle", "sample": sample,
+               "cores": threads, "core_counts": cpu_baseline.cores, "kind": "oracle", "sample": sample,
                "step_seconds_extrapolated": t_cpu,
                "per_kernel_seconds": {k: round(v, 3) for k, v in parts.items()}}
         log(f"cpu oracle: {t_cpu:.1f} s per step (extrapolated), threads={threads}")
