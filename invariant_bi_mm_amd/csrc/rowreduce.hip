@@ -10,11 +10,13 @@
 // actually guarantee?"; the greedy sampler "picks the highest-probability
 // token" (same section).
 //
-// Invariance: one workgroup owns one row and nothing else. The lane that
-// reads an element, the order each lane folds its elements, the butterfly
-// and the fixed-order merge of the waves' partials are all functions of n
-// (and the compiled kernel) only, so row i gets the same bits for any m and
-// any content of the other rows. No atomics, no cross-workgroup traffic.
+// Invariance: the lane that reads an element, the order each lane folds its
+// elements, the butterfly and the fixed-order merge of the waves' partials
+// are all functions of n (and the compiled kernel) only, so row i gets the
+// same bits for any m and any content of the other rows. A workgroup works
+// on one row only; for log_softmax at small m the same wave partials of a row
+// are computed by several workgroups and merged by later launches, with the
+// same arithmetic (see there). No atomics.
 #include "bi_internal.h"
 #include "device_common.h"
 
@@ -415,6 +417,157 @@ __global__ __launch_bounds__(LS_NT) void log_softmax_kernel(const float* __restr
   if (tid < tail) __builtin_nontemporal_store((xr[nch * 4 + tid] - mx) - lg, yr + nch * 4 + tid);
 }
 
+// The same row reduction for a few rows, spread over many CUs. In the kernel
+// above a row's reduction is 16 wave partials -- wave w, lane l folds the
+// units 64 w + l + 1024 u (increasing u; the n % 4 tail elements by threads
+// 0..tail-1, last) and then runs the butterfly -- merged in wave order. Those
+// 16 partials do not depend on each other, so for a small batch each gets a
+// workgroup (one wave) of its own, with all its loads in flight at once,
+// instead of sharing one CU with the other 15 (at m = 1 the one-workgroup form
+// leaves 255 CUs idle and walks ~38 memory round trips). Three launches in
+// stream order; no scratch, no atomics, no waiting between workgroups:
+//   ls_partial_kernel  the 16 wave partials of every row, each written as
+//                      {max, sum, argmax value, argmax index bits} to floats
+//                      [4 w, 4 w + 4) of the row's own output;
+//   ls_out_kernel      merges them in wave order (the arithmetic of the kernel
+//                      above) and writes every output element from float 64 on;
+//   ls_head_kernel     merges them again (same order, same bits), writes
+//                      floats 0..63 over the partials, the tail and the argmax.
+// Every row therefore gets exactly the bits of log_softmax_kernel.
+constexpr int LS_G = 40;  // units a lane of ls_partial_kernel loads at once
+
+__global__ __launch_bounds__(64) void ls_partial_kernel(const float* __restrict__ x, int64_t ldx,
+                                                         float* __restrict__ y, int64_t ldy, int n) {
+  const int row = blockIdx.x / (LS_NT / 64), w = blockIdx.x % (LS_NT / 64);
+  const int lane = threadIdx.x, tid = 64 * w + lane;  // the thread of log_softmax_kernel this lane stands for
+  const float* xr = x + (int64_t)row * ldx;
+  const f32x4* xv = reinterpret_cast<const f32x4*>(xr);
+  const int nch = n >> 2, tail = n & 3;
+  float m = -INFINITY, s = 0.0f, bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int u0 = 0; tid + u0 * LS_NT < nch; u0 += LS_G) {
+    f32x4 r[LS_G];
+#pragma unroll
+    for (int u = 0; u < LS_G; ++u) {
+      const int cc = tid + (u0 + u) * LS_NT;
+      r[u] = cc < nch ? xv[cc] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int u = 0; u < LS_G; ++u) {
+      const int cc = tid + (u0 + u) * LS_NT;
+      if (cc < nch) {
+        const f32x4 v = r[u];
+        const float cm = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+        if (cm > m) {
+          s = s * exp_dev(m - cm);
+          m = cm;
+        }
+        const float mr = m == -INFINITY ? 0.0f : m;
+        s = s + exp_dev(v.x - mr);
+        s = s + exp_dev(v.y - mr);
+        s = s + exp_dev(v.z - mr);
+        s = s + exp_dev(v.w - mr);
+        const int j0 = 4 * cc;
+        if (v.x > bv) { bv = v.x; bi = j0; }
+        if (v.y > bv) { bv = v.y; bi = j0 + 1; }
+        if (v.z > bv) { bv = v.z; bi = j0 + 2; }
+        if (v.w > bv) { bv = v.w; bi = j0 + 3; }
+      }
+    }
+  }
+  if (tid < tail) {
+    const float v = xr[nch * 4 + tid];
+    if (v > m) {
+      s = s * exp_dev(m - v);
+      m = v;
+    }
+    s = s + exp_dev(v - (m == -INFINITY ? 0.0f : m));
+    if (v > bv) {
+      bv = v;
+      bi = nch * 4 + tid;
+    }
+  }
+  MS ms{m, s};
+  AM am{bv, bi};
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    ms = ms_merge(ms, MS{xor_shfl(ms.m, d), xor_shfl(ms.s, d)});
+    am = am_merge(am, AM{xor_shfl(am.v, d), __shfl_xor(am.i, d, 64)});
+  }
+  if (lane == 0) {
+    float* slot = y + (int64_t)row * ldy + 4 * w;
+    slot[0] = ms.m;
+    slot[1] = ms.s;
+    slot[2] = am.v;
+    reinterpret_cast<int*>(slot)[3] = am.i;
+  }
+}
+
+// (max, log sum, argmax) of a row from its 16 wave partials, merged in wave
+// order as log_softmax_kernel merges them (all lanes read the same slots).
+__device__ __forceinline__ void ls_totals(const float* yr, float& mx, float& lg, AM& best) {
+  MS tot{yr[0], yr[1]};
+  best = AM{yr[2], reinterpret_cast<const int*>(yr)[3]};
+#pragma unroll
+  for (int w = 1; w < LS_NT / 64; ++w) {
+    tot = ms_merge(tot, MS{yr[4 * w], yr[4 * w + 1]});
+    best = am_merge(best, AM{yr[4 * w + 2], reinterpret_cast<const int*>(yr)[4 * w + 3]});
+  }
+  mx = tot.m;
+  lg = __builtin_amdgcn_logf(tot.s) * LN2;  // log2 -> ln
+}
+
+// Units 16 .. nch - 1 of every row (the first 16 units hold the partials
+// until ls_head_kernel): workgroup (row, slice) writes units 1024 slice ..
+// 1024 slice + 1023, four per thread, their loads in flight during the merge.
+__global__ __launch_bounds__(256) void ls_out_kernel(const float* __restrict__ x, int64_t ldx,
+                                                      float* __restrict__ y, int64_t ldy, int n) {
+  const int nch = n >> 2;
+  const int slices = (nch + 1023) / 1024;
+  const int row = blockIdx.x / slices, slice = blockIdx.x % slices;
+  const float* xr = x + (int64_t)row * ldx;
+  float* yr = y + (int64_t)row * ldy;
+  const f32x4* xv = reinterpret_cast<const f32x4*>(xr);
+  f32x4 v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int cc = 1024 * slice + threadIdx.x + 256 * j;
+    v[j] = (cc >= 16 && cc < nch) ? xv[cc] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  float mx, lg;
+  AM best;
+  ls_totals(yr, mx, lg, best);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int cc = 1024 * slice + threadIdx.x + 256 * j;
+    if (cc >= 16 && cc < nch)
+      __builtin_nontemporal_store(f32x4{(v[j].x - mx) - lg, (v[j].y - mx) - lg, (v[j].z - mx) - lg,
+                                        (v[j].w - mx) - lg},
+                                  reinterpret_cast<f32x4*>(yr) + cc);
+  }
+}
+
+// Units 0..15 of every row (over its partials), the n % 4 tail and the argmax.
+__global__ __launch_bounds__(64) void ls_head_kernel(const float* __restrict__ x, int64_t ldx,
+                                                      float* __restrict__ y, int64_t ldy,
+                                                      int64_t* __restrict__ amax, int n) {
+  const int row = blockIdx.x, lane = threadIdx.x;
+  const int nch = n >> 2, tail = n & 3;
+  const float* xr = x + (int64_t)row * ldx;
+  float* yr = y + (int64_t)row * ldy;
+  const f32x4 v = lane < 16 ? reinterpret_cast<const f32x4*>(xr)[lane] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const float t = lane < tail ? xr[nch * 4 + lane] : 0.0f;
+  float mx, lg;
+  AM best;
+  ls_totals(yr, mx, lg, best);
+  // every lane's partial reads feed mx and lg, so they precede the stores below
+  if (lane < 16)
+    __builtin_nontemporal_store(f32x4{(v.x - mx) - lg, (v.y - mx) - lg, (v.z - mx) - lg, (v.w - mx) - lg},
+                                reinterpret_cast<f32x4*>(yr) + lane);
+  if (lane < tail) __builtin_nontemporal_store((t - mx) - lg, yr + nch * 4 + lane);
+  if (lane == 0 && amax != nullptr) amax[row] = (int64_t)(best.i == 0x7fffffff ? 0 : best.i);
+}
+
 // Chunks-per-lane template choice for one-wave-per-row kernels: a function
 // of n only.
 int pick_cpt(int64_t nch) {
@@ -489,9 +642,25 @@ hipError_t launch_mean(const void* x, bool x_bf16, int64_t ldx, float* y, int64_
   return hipGetLastError();
 }
 
+// Rows up to which each row's 16 wave partials get workgroups of their own
+// (the three-launch form above); the same bits either way.
+constexpr int64_t LS_SMALL_M = 32;
+
 hipError_t launch_log_softmax(const float* x, int64_t ldx, float* y, int64_t ldy, int64_t* argmax,
                               int64_t m, int64_t n, hipStream_t s) {
-  hipLaunchKernelGGL(log_softmax_kernel, dim3((unsigned)m), dim3(LS_NT), 0, s, x, ldx, y, ldy, argmax, (int)n);
+  const int ni = (int)n;
+  if (m <= LS_SMALL_M && n >= 4096) {
+    const int slices = (ni / 4 + 1023) / 1024;
+    hipLaunchKernelGGL(ls_partial_kernel, dim3((unsigned)(m * (LS_NT / 64))), dim3(64), 0, s, x, ldx, y, ldy, ni);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(ls_out_kernel, dim3((unsigned)(m * slices)), dim3(256), 0, s, x, ldx, y, ldy, ni);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(ls_head_kernel, dim3((unsigned)m), dim3(64), 0, s, x, ldx, y, ldy, argmax, ni);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(log_softmax_kernel, dim3((unsigned)m), dim3(LS_NT), 0, s, x, ldx, y, ldy, argmax, ni);
   return hipGetLastError();
 }
 

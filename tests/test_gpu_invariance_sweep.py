@@ -138,3 +138,43 @@ def test_lm_head_every_m_up_to_256(lib, b_is_nk):
     assert not changed, f"fixed row changed at (M - 1, slot, [logits, log-probs, argmax]) {changed[:20]}"
     diff = fixed_bad.nonzero().flatten().tolist()
     assert not diff, f"fixed-tile mode differs from the table at M - 1 = {diff[:20]}"
+
+
+@pytest.mark.parametrize("n,ms", [(8203, range(1, 2049)), (151936, list(range(1, 257)) + [511, 512, 1024, 2048])],
+                         ids=["n8203_every_m", "n151936"])
+def test_log_softmax_forms_same_bits_every_m(lib, n, ms):
+    """log_softmax + argmax gives each of a row's 16 wave partials a
+    workgroup of its own for small M (three launches) and gives each row one
+    workgroup otherwise; both forms compute the same partials and merge them
+    in the same order. A fixed row at positions 0, M - 1 and p, other rows
+    fresh per M: its log-probabilities and greedy token have the bytes they
+    have at M = 1, at every M listed (n = 8203: a partial last unit)."""
+    ld = (n + 3) // 4 * 4
+    ms = list(ms)
+    mmax = max(ms)
+    rng = np.random.default_rng(n)
+    row = S.normal_f32((1, n), 4.0, seed=42000 + n, device=DEV)[0]
+    r1 = torch.zeros((1, ld), device=DEV)[:, :n]  # rows 16-byte aligned
+    r1.copy_(row[None])
+    y1, a1 = lib.bi_log_softmax(r1, out=torch.empty((1, ld), device=DEV)[:, :n])
+    ref, ref_a = as_int(y1[0].clone()), int(a1[0])
+    nblk = min(8192, 4 * mmax)
+    big = S.normal_f32((nblk + mmax, ld), 4.0, seed=42100 + n, device=DEV)
+    ybuf = torch.empty((mmax, ld), device=DEV)
+    abuf = torch.empty(mmax, dtype=torch.int64, device=DEV)
+    bad = torch.zeros((len(ms), 3, 2), dtype=torch.bool, device=DEV)
+    offs = rng.integers(0, nblk, size=len(ms)).tolist()
+    pos = torch.from_numpy(np.array([[0, m - 1, rng.integers(0, m)] for m in ms])).to(DEV)
+    say(f"log_softmax every M: n={n}, {len(ms)} values of M up to {mmax}")
+    for i, m in enumerate(ms):
+        x = big[offs[i]:offs[i] + m].clone()
+        p = pos[i]
+        x[p, :n] = row
+        y, a = lib.bi_log_softmax(x[:, :n], out=ybuf[:m, :n], argmax=abuf[:m])
+        bad[i, :, 0] = (as_int(y[p]) != ref).any(dim=1)
+        bad[i, :, 1] = a[p] != ref_a
+        if (i + 1) % 256 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    changed = bad.nonzero().tolist()
+    assert not changed, f"(index into M list, slot, [log-probs, argmax]) {changed[:20]}"

@@ -321,9 +321,15 @@ def test_log_softmax_masked_rows(lib, n):
     assert_close_masked(f32(y), ref, f"masked log_softmax n={n}")
     assert am.cpu().tolist() == O.argmax(xc).tolist()
     assert float(y[2, n // 3]) == 0.0 and am[2].item() == n // 3
-    # the unmasked rows around them are untouched by the change: same bits as alone
+    # a row has the same bits alone and in a batch, and in a batch large enough
+    # for the one-workgroup-per-row form (the six rows above use the other form)
     y0, _ = lib.bi_log_softmax(x[4:5].contiguous())
     assert same_bits(y0, y[4:5])
+    big = torch.empty((80, ld), device=DEV)
+    big[:, :n] = S.normal_f32((80, n), 4.0, seed=97).to(DEV)
+    big[70:76, :n] = x
+    yb, ab = lib.bi_log_softmax(big[:, :n], out=torch.empty((80, ld), device=DEV)[:, :n])
+    assert same_bits(yb[70:76], y) and same_bits(ab[70:76], am)
 
 
 # ------------------------------------------------------------------ decode attention
