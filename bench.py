@@ -149,17 +149,19 @@ class Workload:
 # The HIP source that defines each step's kernel (with the shared headers,
 # the input of a per-kernel digest: measured traffic stays valid until that
 # kernel's own source changes).
-KERNEL_SOURCE = {"gemm_qkv": "gemm.hip", "gemm_o": "gemm.hip", "gemm_gateup": "gemm.hip", "gemm_down": "gemm.hip",
-                 "lm_head": "gemm.hip", "lm_logsm": "rowreduce.hip", "rmsnorm": "rowreduce.hip",
-                 "mean": "rowreduce.hip", "logsm": "rowreduce.hip", "decode_attn": "decode_attention.hip"}
+_GEMM_SRC = ("gemm.hip", "gemm_plan.cpp")
+KERNEL_SOURCE = {"gemm_qkv": _GEMM_SRC, "gemm_o": _GEMM_SRC, "gemm_gateup": _GEMM_SRC, "gemm_down": _GEMM_SRC,
+                 "lm_head": _GEMM_SRC, "lm_logsm": ("rowreduce.hip",), "rmsnorm": ("rowreduce.hip",),
+                 "mean": ("rowreduce.hip",), "logsm": ("rowreduce.hip",), "decode_attn": ("decode_attention.hip",)}
 
 
 def source_digest(kernel: str) -> str:
-    """sha256 over the HIP source defining `kernel` and the shared headers."""
+    """sha256 over the sources defining `kernel` (its HIP file and, for the
+    GEMM, the tile table) and the shared headers."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "invariant_bi_mm_amd", "csrc")
-    for name in (KERNEL_SOURCE[kernel], "bi_internal.h", "device_common.h"):
+    for name in (*KERNEL_SOURCE[kernel], "bi_internal.h", "device_common.h"):
         with open(os.path.join(csrc, name), "rb") as fh:
             h.update(name.encode() + b"\0" + fh.read())
     return h.hexdigest()

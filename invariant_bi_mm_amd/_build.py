@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbi.so")
 
-SOURCES = ["api.cpp", "gemm.hip", "rowreduce.hip", "decode_attention.hip", "elementwise.hip"]
+SOURCES = ["api.cpp", "gemm_plan.cpp", "gemm.hip", "rowreduce.hip", "decode_attention.hip", "elementwise.hip"]
 
 COMMON = [
     "-O3", "-fPIC", "-std=c++17", "-Wall",

@@ -4,9 +4,10 @@
 //
 // They complete the token path the pages trace through an engine -- one
 // sequence's greedy token stream must not change with the batch around it
-// ("Defeating Nondeterminism in LLM Inference", section on the
-// completions experiment; "Batch-invariant inference kernels (Thinking
-// Machines) -- Evidence & limits", section "Evidence"). Each output element
+// (readhandoff.com, agent-run reproducibility pinning, "Where the divergence
+// showed up": completions identical for a long prefix, then forking at one
+// token; "Batch-invariant inference kernels (Thinking Machines) -- Evidence &
+// limits", section "Evidence"). Each output element
 // depends only on its own token's inputs through a fixed sequence of fp32
 // operations; the only reduction, the per-head sum of squares in the q/k
 // RMSNorm, is a fixed wave butterfly over one head. So none of them can

@@ -1,0 +1,116 @@
+// The GEMM's tile table: which configuration a call of bi_mm / bi_addmm /
+// bi_gemm runs, as a function of (m, n, k, layout) -- host code only, shared
+// by the launcher (gemm.hip) and the argument checks (api.cpp). Every
+// configuration computes each output element with the same chain (one
+// v_mfma_f32_32x32x16_bf16 per 16 k, increasing k, fp32 from 0, k padded with
+// zeros to a multiple of 64, the same epilogue), so the choice moves work
+// between workgroups without changing any bit. Batch invariance gives up
+// shape-aware tiling according to the wiki page "Thinking Machines" (section
+// on why it is not the main answer, point 3); it is kept here because it
+// never touches the reduction.
+#include "bi_internal.h"
+
+#include <numeric>
+
+namespace bi {
+
+constexpr int TK = 64;  // k per stage (the kernels' k tile)
+
+// Skinny (M <= 64): one consumer wave (32 rows) when the 32-row strips fit
+// in one round over the CUs, else two (64 rows); two producer waves either
+// way.
+static GemmConfig skinny_config(int64_t m, int64_t strips) {
+  if (m <= 32 || ((m + 31) / 32) * strips <= 256) return GemmConfig{32, 32, TK, 3};
+  return GemmConfig{64, 32, TK, 4};
+}
+
+// The configuration table. Every configuration -- skinny, 64x128, 128x128,
+// 256x256 -- computes each output element with the same chain (one 32x32x16 MFMA per
+// 16 k, increasing k, fp32, k padded to a multiple of 64, the same
+// epilogue), so the choice moves work between workgroups without changing
+// any bit, and it may depend on M: the result of a row still does not depend
+// on how many rows there are. (The batch-dependent selection the pages warn
+// about changes the reduction -- split-K, a different instruction -- and
+// nothing here does.) Measured on MI355X for the Qwen3-8B projection shapes:
+//   * skinny (32 or 64 rows x 32 columns, deep ring) for M <= 64: 2.5-3.6x
+//     faster than 128x128 (N = 4096, 6144, K = 4096 and 12288), 1.25-1.6x
+//     at N = 24576; at the 151936-wide LM head both stream at ~5.4 TB/s and
+//     128x128 is kept;
+//   * the same deep ring with a 64x128 tile (1x2 consumer waves of 64x64,
+//     6 stages) for M > 64 while 128x128 tiles would fill at most half the
+//     CUs and the 64x128 ones still fit one round: 6-14 % faster than the
+//     128x128 ring at M = 128-512 for N = 4096 (K = 4096 and 12288) and
+//     3-5 % for N = 6144 at M <= 256;
+//   * the same deep ring with a 128x128 tile (2x2 consumer waves of 64x64)
+//     for M > 64 while its tiles fit one round over the CUs: 1.15-1.35x
+//     faster than 128x128 or skinny at M = 128-1024, 1.6x than 256x256 at
+//     M = 128, N = 24576;
+//   * 256x256 (8 waves, 128x64 each) once its tiles fill the chip (M >= 192,
+//     at least 192 tiles, rounds of 256 at least 70 % full on average):
+//     1.25-1.3x faster than 128x128 at M = 4096 (N = 4096, LM head), 1.1x
+//     for the LM head at M = 256, and for the wide N of gate+up at all M;
+//   * 128x128 (4 waves, two workgroups per CU) in between.
+GemmConfig gemm_config(int64_t m, int64_t n, int64_t k, bool b_is_nk) {
+  (void)b_is_nk;
+  const int64_t strips = (n + 31) / 32;
+  if (m <= 64 && n <= 32768) return skinny_config(m, strips);
+  const int64_t t128 = ((m + 127) / 128) * ((n + 127) / 128);
+  if (m > 64 && t128 <= 128 && ((m + 63) / 64) * ((n + 127) / 128) <= 256) return GemmConfig{64, 128, TK, 4};
+  if (m > 64 && t128 <= 256) return GemmConfig{128, 128, TK, 6};
+  const int64_t t256 = ((m + 255) / 256) * ((n + 255) / 256);
+  const int64_t rounds = (t256 + 255) / 256;  // one 256x256 workgroup per CU
+  if (m >= 192 && t256 >= 192 && 10 * t256 >= 7 * rounds * 256) return GemmConfig{256, 256, TK, 8};
+  if (n >= 16384 && n <= 65536 && k <= 8192) return GemmConfig{256, 256, TK, 8};
+  return GemmConfig{128, 128, TK, 4};
+}
+
+// The fixed-tile mode: one configuration per (N, K, layout), whatever M is
+// -- the letter of "one tile config for all M". 256x256 (8 waves) once N
+// spans at least 16 tile columns (every projection shape and the LM head),
+// 128x128 (4 waves) for narrower N; no column split (where it splits
+// depends on M). Its bits are those of gemm_config's table, since every
+// configuration runs the same chain; it exists to measure what choosing the
+// tile by M gains.
+GemmConfig gemm_config_fixed(int64_t n, int64_t k, bool b_is_nk) {
+  (void)k;
+  (void)b_is_nk;
+  if (n >= 16 * 256 - 255) return GemmConfig{256, 256, TK, 8};
+  return GemmConfig{128, 128, TK, 4};
+}
+
+// Columns of a 256x256 GEMM left to full rounds of 256x256 tiles; the rest
+// (if any) goes to 256x128 tiles in a second launch. Whole rounds of 256 CUs
+// need tiles_m * n1 to be a multiple of 256. A round of 256x128 tiles takes
+// ~0.65 of a 256x256 round (measured, K = 4096); the split is taken only
+// when that predicts fewer rounds. Measured on MI355X: q+kv at M = 4096
+// (384 tiles, 1.5 rounds) 7-8 % faster, gate+up at M = 1024 4-7 %, the LM
+// head at M = 256 (594 tiles) 3-4 %. Both parts compute every element with
+// the chain above, so the bits do not change.
+static int64_t full_round_columns(int64_t tiles_m, int64_t tiles_n, int64_t m, int64_t n) {
+  const int64_t g = 256 / std::gcd(tiles_m, (int64_t)256);  // tiles_m * n1 % 256 == 0 iff g divides n1
+  const int64_t n1 = (tiles_n / g) * g;
+  if (n1 == 0 || n1 == tiles_n) return tiles_n;
+  const int64_t t_tail = ((m + 255) / 256) * ((n - n1 * 256 + 127) / 128);
+  const double split = (double)(tiles_m * n1 / 256) + 0.65 * (double)((t_tail + 255) / 256);
+  const double whole = (double)((tiles_m * tiles_n + 255) / 256);
+  return split < whole - 0.05 ? n1 : tiles_n;
+}
+
+GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k, bool b_is_nk, bool fixed_tile) {
+  GemmPlan plan{};
+  const GemmConfig cfg = fixed_tile ? gemm_config_fixed(n, k, b_is_nk) : gemm_config(m, n, k, b_is_nk);
+  plan.count = 1;
+  plan.launch[0] = GemmLaunch{cfg, 0, n};
+  if (!fixed_tile && cfg.tile_m == 256 && cfg.tile_n == 256) {
+    const int64_t tiles_m = (m + 255) / 256, tiles_n = (n + 255) / 256;
+    const int64_t n1 = full_round_columns(tiles_m, tiles_n, m, n);
+    if (n1 < tiles_n) {
+      plan.count = 2;
+      plan.launch[0].n_end = n1 * 256;
+      plan.launch[1] = GemmLaunch{GemmConfig{256, 128, TK, 8}, n1 * 256, n};
+    }
+  }
+  return plan;
+}
+
+}  // namespace bi
