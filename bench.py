@@ -561,6 +561,8 @@ def main():
                     help="measured HBM traffic per kernel (written from rocprofv3 FETCH_SIZE/WRITE_SIZE runs)")
     ap.add_argument("--sweep", action="store_true",
                     help="per-config sweep over the workloads' M values (markdown table), then exit")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only measure the prefill attention workload (4 x 2048 tokens) and print its JSON")
     ap.add_argument("--gemm-probe", action="store_true",
                     help="only run each projection GEMM at M = 64, 512 and 4096 and the LM head at M = 256, "
                          "3 launches each ([K,N] weights, fp32 out), for rocprofv3 counter and trace runs; "
@@ -607,6 +609,9 @@ def main():
     torch.cuda.set_device(0)
     if args.sweep:
         sweep(torch, S, bi)
+        return
+    if args.prefill_only:
+        print(json.dumps(prefill_measure(torch, S, bi, dev)), flush=True)
         return
     wl = Workload(torch, S, bi, dev)
     ops = wl.ops()

@@ -754,10 +754,10 @@ static hipError_t launch_part(const GemmParams& p, const GemmLaunch& L, hipStrea
       return p.b_is_nk ? launch_ring<2, 1, 1, 1, 2, 12, true>(a, s) : launch_ring<2, 1, 1, 1, 2, 12, false>(a, s);
     return hipErrorInvalidConfiguration;
   }
-  if (cfg.tile_m == 128 && cfg.tile_n == 128 && cfg.waves == 6)  // 2x2 consumers of 64x64, 4-stage ring
-    return p.b_is_nk ? launch_ring<2, 2, 2, 2, 2, 4, true>(a, s) : launch_ring<2, 2, 2, 2, 2, 4, false>(a, s);
-  if (cfg.tile_m == 64 && cfg.tile_n == 128)  // 1x2 consumers of 64x64, 6-stage ring
-    return p.b_is_nk ? launch_ring<1, 2, 2, 2, 2, 6, true>(a, s) : launch_ring<1, 2, 2, 2, 2, 6, false>(a, s);
+  if (cfg.tile_m == 128 && cfg.tile_n == 128 && cfg.waves == 10)  // 4x2 consumers of 32x64, 4-stage ring
+    return p.b_is_nk ? launch_ring<4, 2, 1, 2, 2, 4, true>(a, s) : launch_ring<4, 2, 1, 2, 2, 4, false>(a, s);
+  if (cfg.tile_m == 64 && cfg.tile_n == 128)  // 2x2 consumers of 32x64, 6-stage ring
+    return p.b_is_nk ? launch_ring<2, 2, 1, 2, 2, 6, true>(a, s) : launch_ring<2, 2, 1, 2, 2, 6, false>(a, s);
 #define BI_GEMM_CASE(TM_, TN_, WM_, WN_)                                                          \
   if (cfg.tile_m == TM_ && cfg.tile_n == TN_ && cfg.waves == WM_ * WN_)                            \
     return p.b_is_nk ? launch_cfg<TM_, TN_, WM_, WN_, true>(a, s) : launch_cfg<TM_, TN_, WM_, WN_, false>(a, s);

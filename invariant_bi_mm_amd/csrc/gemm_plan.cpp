@@ -36,15 +36,19 @@ static GemmConfig skinny_config(int64_t m, int64_t strips) {
 //     faster than 128x128 (N = 4096, 6144, K = 4096 and 12288), 1.25-1.6x
 //     at N = 24576; at the 151936-wide LM head both stream at ~5.4 TB/s and
 //     128x128 is kept;
-//   * the same deep ring with a 64x128 tile (1x2 consumer waves of 64x64,
-//     6 stages) for M > 64 while 128x128 tiles would fill at most half the
-//     CUs and the 64x128 ones still fit one round: 6-14 % faster than the
-//     128x128 ring at M = 128-512 for N = 4096 (K = 4096 and 12288) and
-//     3-5 % for N = 6144 at M <= 256;
-//   * the same deep ring with a 128x128 tile (2x2 consumer waves of 64x64)
+//   * the same deep ring with a 64x128 tile (2x2 consumer waves of 32x64,
+//     two producers, 6 stages) for M > 64 while 128x128 tiles would fill at
+//     most half the CUs and the 64x128 ones still fit one round: 6-14 %
+//     faster than the 128x128 ring at M = 128-512 for N = 4096 (K = 4096
+//     and 12288) and 3-5 % for N = 6144 at M <= 256; four consumer waves
+//     (every SIMD issuing MFMAs) instead of two of 64x64: 13-26 % faster at
+//     M = 65-512 for N = 4096 and 6144;
+//   * the same deep ring with a 128x128 tile (4x2 consumer waves of 32x64)
 //     for M > 64 while its tiles fit one round over the CUs: 1.15-1.35x
 //     faster than 128x128 or skinny at M = 128-1024, 1.6x than 256x256 at
-//     M = 128, N = 24576;
+//     M = 128, N = 24576; eight consumers instead of four of 64x64: 3-7 %
+//     faster at M = 384-1024 for N = 4096 and 6144 and at M <= 128 for
+//     N = 24576 (K = 12288 at M = 768-1024: ~5 % slower);
 //   * 256x256 (8 waves, 128x64 each) once its tiles fill the chip (M >= 192,
 //     at least 192 tiles, rounds of 256 at least 70 % full on average):
 //     1.25-1.3x faster than 128x128 at M = 4096 (N = 4096, LM head), 1.1x
@@ -55,8 +59,8 @@ GemmConfig gemm_config(int64_t m, int64_t n, int64_t k, bool b_is_nk) {
   const int64_t strips = (n + 31) / 32;
   if (m <= 64 && n <= 32768) return skinny_config(m, strips);
   const int64_t t128 = ((m + 127) / 128) * ((n + 127) / 128);
-  if (m > 64 && t128 <= 128 && ((m + 63) / 64) * ((n + 127) / 128) <= 256) return GemmConfig{64, 128, TK, 4};
-  if (m > 64 && t128 <= 256) return GemmConfig{128, 128, TK, 6};
+  if (m > 64 && t128 <= 128 && ((m + 63) / 64) * ((n + 127) / 128) <= 256) return GemmConfig{64, 128, TK, 6};
+  if (m > 64 && t128 <= 256) return GemmConfig{128, 128, TK, 10};
   const int64_t t256 = ((m + 255) / 256) * ((n + 255) / 256);
   const int64_t rounds = (t256 + 255) / 256;  // one 256x256 workgroup per CU
   if (m >= 192 && t256 >= 192 && 10 * t256 >= 7 * rounds * 256) return GemmConfig{256, 256, TK, 8};

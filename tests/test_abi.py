@@ -252,7 +252,7 @@ def test_gemm_config_table(bi):
             for nk in (False, True):
                 cfg = bi.bi_gemm_config(m, n, k, nk)
                 assert cfg == bi.bi_gemm_config(m, n, k, nk)
-                assert cfg in {(32, 32, 64, 3), (64, 32, 64, 4), (64, 128, 64, 4), (128, 128, 64, 6), (128, 128, 64, 4),
+                assert cfg in {(32, 32, 64, 3), (64, 32, 64, 4), (64, 128, 64, 6), (128, 128, 64, 10), (128, 128, 64, 4),
                                (256, 256, 64, 8)}, cfg
                 seen.add(cfg)
     assert len(seen) == 6
@@ -343,7 +343,7 @@ def test_qwen_shapes_walk_every_gemm_configuration(bi):
     """Over M = 1..4096 the four Qwen3-8B projection shapes (either layout)
     take every configuration of the tile table between them, and the 256x128
     column split: so the every-M GPU sweep on those shapes runs them all."""
-    table = {(32, 32, 64, 3), (64, 32, 64, 4), (64, 128, 64, 4), (128, 128, 64, 6), (128, 128, 64, 4),
+    table = {(32, 32, 64, 3), (64, 32, 64, 4), (64, 128, 64, 6), (128, 128, 64, 10), (128, 128, 64, 4),
              (256, 256, 64, 8)}
     seen, split = set(), False
     for k, n in ((4096, 6144), (4096, 4096), (4096, 24576), (12288, 4096)):

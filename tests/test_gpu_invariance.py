@@ -116,7 +116,7 @@ def test_mm_adversarial_other_rows(lib, fill):
             assert same_bits(lib.bi_mm(x, w)[pos], ref), (fill, m, pos)
 
 
-ALL_CONFIGS = {(32, 32, 64, 3), (64, 32, 64, 4), (64, 128, 64, 4), (128, 128, 64, 6), (128, 128, 64, 4), (256, 256, 64, 8)}
+ALL_CONFIGS = {(32, 32, 64, 3), (64, 32, 64, 4), (64, 128, 64, 6), (128, 128, 64, 10), (128, 128, 64, 4), (256, 256, 64, 8)}
 
 
 @pytest.mark.parametrize("b_is_nk", [False, True])
