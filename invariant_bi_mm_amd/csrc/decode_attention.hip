@@ -215,12 +215,17 @@ __device__ __forceinline__ void split_softmax_rows(float* const (&row)[R], int l
     l[i] = 0.0f;
     uint16_t* pb = reinterpret_cast<uint16_t*>(row[i]);
 #pragma unroll
-    for (int r = 0; r < SPLIT / 64; ++r) {
-      const float pr = __builtin_amdgcn_exp2f(v[i][r] - mx[i]);  // 2^-inf = 0 for masked slots
-      const uint32_t hb = f32_to_bf16_rne(pr);
+    for (int r = 0; r < SPLIT / 64; r += 2) {  // two keys per conversion
+      const float p0 = __builtin_amdgcn_exp2f(v[i][r] - mx[i]);  // 2^-inf = 0 for masked slots
+      const float p1 = __builtin_amdgcn_exp2f(v[i][r + 1] - mx[i]);
+      const uint32_t hb = cvt_pk_bf16(p0, p1);
+      const uint32_t lb = cvt_pk_bf16(p0 - bf16lo(hb), p1 - bf16hi(hb));
       pb[lane + 64 * r] = (uint16_t)hb;
-      pb[PLO + lane + 64 * r] = (uint16_t)f32_to_bf16_rne(pr - __uint_as_float(hb << 16));
-      l[i] = l[i] + pr;
+      pb[lane + 64 * (r + 1)] = (uint16_t)(hb >> 16);
+      pb[PLO + lane + 64 * r] = (uint16_t)lb;
+      pb[PLO + lane + 64 * (r + 1)] = (uint16_t)(lb >> 16);
+      l[i] = l[i] + p0;
+      l[i] = l[i] + p1;
     }
   }
 #pragma unroll
@@ -232,21 +237,38 @@ __device__ __forceinline__ void split_softmax_rows(float* const (&row)[R], int l
   }
 }
 
+// V of keys at or past nt is zeroed in the fragments themselves, once per
+// split: the cache past a sequence's last token may hold any bits, and
+// 0 * NaN would poison the sum. A full split (nt == SPLIT) has nothing to
+// zero.
+__device__ __forceinline__ void mask_v(u32x4 (&vf)[8][2], int nt, int lane) {
+  if (nt >= SPLIT) return;  // uniform
+  const int q4 = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const int valid = nt - (32 * ks + 8 * q4);  // keys of this lane's 8 that exist
+    u32x4 keep;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) keep[e] = (2 * e < valid ? 0xFFFFu : 0u) | (2 * e + 1 < valid ? 0xFFFF0000u : 0u);
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) vf[ks][dt] &= keep;
+  }
+}
+
 // Phase 3 on the matrix cores: the split's partial output
 //   O[r][d] = sum over its SPLIT keys of p[r][key] v[key][d]
 // for one block of 16 query rows (4 tokens x the GQA heads), by
 // v_mfma_f32_16x16x32_bf16 with A = p and B = v (fragments from
-// load_v_frags). No partial crosses waves: wave w owns columns [32 w, 32 w + 32).
-// p enters as its two bf16 parts hi + lo (written by phase 2), so the
-// products carry ~16 bits of p; the chain per element is: key steps of 32 in
-// increasing order, hi then lo in each, fp32 accumulation. V of keys at or
-// past nt is zeroed here (the cache past a sequence's last token may hold
-// any bits, and 0 * NaN would poison the sum). acc[dt] = the wave's tile dt:
-// lane l holds rows 16 rb + 4 (l / 16) + i (i = 0..3), i.e. token
-// 4 rb + l / 16 and GQA head i, column d = 32 w + 16 dt + l % 16. Rows of
-// tokens >= ntok repeat token 0's p (never stored).
+// load_v_frags, masked by mask_v). No partial crosses waves: wave w owns
+// columns [32 w, 32 w + 32). p enters as its two bf16 parts hi + lo (written
+// by phase 2), so the products carry ~16 bits of p; the chain per element
+// is: key steps of 32 in increasing order, hi then lo in each, fp32
+// accumulation. acc[dt] = the wave's tile dt: lane l holds rows
+// 16 rb + 4 (l / 16) + i (i = 0..3), i.e. token 4 rb + l / 16 and GQA head i,
+// column d = 32 w + 16 dt + l % 16. Rows of tokens >= ntok repeat token 0's
+// p (never stored).
 __device__ __forceinline__ void split_pv(const u32x4 (&vf)[8][2], const float (*S)[GQA][SROW], int rb, int ntok,
-                                         int nt, int lane, f32x4 (&acc)[2]) {
+                                         int lane, f32x4 (&acc)[2]) {
   const int r = 16 * rb + (lane & 15);  // the query row this lane feeds
   const int t = r / GQA;
   const int q4 = lane >> 4;
@@ -256,13 +278,9 @@ __device__ __forceinline__ void split_pv(const u32x4 (&vf)[8][2], const float (*
   for (int ks = 0; ks < 8; ++ks) {
     const u32x4 hi = *reinterpret_cast<const u32x4*>(prow + 32 * ks);
     const u32x4 lo = *reinterpret_cast<const u32x4*>(prow + PLO + 32 * ks);
-    const int valid = nt - (32 * ks + 8 * q4);  // keys of this lane's 8 that exist
-    u32x4 keep;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) keep[e] = (2 * e < valid ? 0xFFFFu : 0u) | (2 * e + 1 < valid ? 0xFFFF0000u : 0u);
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) {
-      const bf16x8 v = __builtin_bit_cast(bf16x8, vf[ks][dt] & keep);
+      const bf16x8 v = __builtin_bit_cast(bf16x8, vf[ks][dt]);
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi), v, acc[dt], 0, 0, 0);
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, lo), v, acc[dt], 0, 0, 0);
     }
@@ -367,7 +385,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
   }
   __syncthreads();
   f32x4 acc[2];
-  split_pv(vf, S, 0, 1, nt, lane, acc);
+  mask_v(vf, nt, lane);
+  split_pv(vf, S, 0, 1, lane, acc);
   if (lane < 16) store_pv(acc, wave, lane, a.ws_o + base * HD);  // rows 0..3: the one token
 }
 
@@ -406,7 +425,9 @@ struct PrefillArgs {
 };
 
 __global__ __launch_bounds__(256) void prefill_split_kernel(PrefillArgs a) {
-  __shared__ float S[4][GQA][SROW];  // one block of 4 tokens
+  // one block of 4 tokens, two buffers: block i writes S[i % 2], so the next
+  // block's scores need not wait for this block's p.v reads
+  __shared__ float S[2][4][GQA][SROW];
 
   const int wi = blockIdx.x / a.hkv, g = blockIdx.x % a.hkv;
   const int tid = threadIdx.x;
@@ -442,14 +463,15 @@ __global__ __launch_bounds__(256) void prefill_split_kernel(PrefillArgs a) {
   __syncthreads();                    // spos, soff
   for (int tb = 0; tb < nq; tb += 4) {  // tokens tb .. tb + 3 of the item
     const int nb = min(4, nq - tb);
+    float(*Sb)[GQA][SROW] = S[(tb >> 2) & 1];
     if (tb + 4 < nq) load_q_block(q0 + (tb + 4) * q_tok, q_tok, min(4, nq - tb - 4), lane, qn);  // next block
-    scores_block(qa, kf, nb, [&](int t) { return min(SPLIT, spos[tb + t] + 1 - t0); }, wave, lane, a.qscale, S);
+    scores_block(qa, kf, nb, [&](int t) { return min(SPLIT, spos[tb + t] + 1 - t0); }, wave, lane, a.qscale, Sb);
     __syncthreads();
     {
       // wave h: head h of the block's 4 tokens (rows of tokens >= nb hold
       // nothing of use; they are processed and never read)
       float mx[4], l[4];
-      float* const rows[4] = {S[0][wave], S[1][wave], S[2][wave], S[3][wave]};
+      float* const rows[4] = {Sb[0][wave], Sb[1][wave], Sb[2][wave], Sb[3][wave]};
       split_softmax_rows<4>(rows, lane, mx, l);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -464,13 +486,16 @@ __global__ __launch_bounds__(256) void prefill_split_kernel(PrefillArgs a) {
     }
     __syncthreads();
     f32x4 acc[2];
-    split_pv(vf, S, 0, nb, nt_max, lane, acc);
+    if (tb == 0) mask_v(vf, nt_max, lane);  // once for the item's blocks
+    split_pv(vf, Sb, 0, nb, lane, acc);
     const int t = lane >> 4;
     if (t < nb) {
       const int64_t base = part_row(tb + t);
       if (base >= 0) store_pv(acc, wave, lane, a.ws_o + base * HD);
     }
-    __syncthreads();  // the next block's scores overwrite S
+    // no barrier here: the next block writes the other score buffer, and the
+    // one after it passes two barriers that every wave reaches only after
+    // this block's p.v reads
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds) qa[ds] = qn[ds];
   }
@@ -587,6 +612,87 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const int32_t* __re
   }
 }
 
+// Combine for prefill rows: one wave per (row, query head), four query
+// heads per workgroup. The arithmetic is decode_combine_kernel's, term for
+// term -- the same 8 groups (splits s = g, g + 8, ... in increasing order,
+// each weighted by 2^(m_s - M) with M the exact max), the same tree
+// ((g0 + g1) + (g2 + g3)) + ((g4 + g5) + (g6 + g7)) and the same division --
+// so a prefilled token keeps its decode bits. Lane 32 hf + c owns
+// o[4c .. 4c + 3] of groups 4 hf .. 4 hf + 3 and adds them as
+// (g0 + g1) + (g2 + g3) in registers; the two halves' sums are then added
+// across the wave (commutative, so both halves hold the same bits). No LDS
+// and no barrier: a row of up to 8 splits (every row of a prompt of up to
+// 2048 tokens) takes one memory round trip with all its loads in flight.
+__global__ __launch_bounds__(256) void prefill_combine_kernel(const int32_t* __restrict__ offs, int cap,
+                                                               const float* __restrict__ ws_o,
+                                                               const float* __restrict__ ws_ml, int hq,
+                                                               void* __restrict__ out, int out_bf16) {
+  const int b = blockIdx.x, lane = threadIdx.x & 63;
+  const int h = 4 * blockIdx.y + (threadIdx.x >> 6);
+  const int hf = lane >> 5, c = lane & 31;
+  // the row's splits [offs[b], offs[b+1]), clamped to the workspace's cap
+  const int w1 = min(max(offs[b + 1], 0), cap);
+  const int w0 = min(max(offs[b], 0), w1), ns = w1 - w0;
+  float l[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float4 o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float M;
+  auto part = [&](int s, float2& ml, float4& ov) {
+    const int64_t ph = (int64_t)(w0 + s) * hq + h;
+    ml = *reinterpret_cast<const float2*>(ws_ml + ph * 2);
+    ov = *reinterpret_cast<const float4*>(ws_o + ph * HD + 4 * c);
+  };
+  auto fold = [&](int k, const float2 ml, const float4 ov) {
+    const float w = __builtin_amdgcn_exp2f(ml.x - M);
+    l[k] = l[k] + w * ml.y;
+    o[k].x = o[k].x + w * ov.x;
+    o[k].y = o[k].y + w * ov.y;
+    o[k].z = o[k].z + w * ov.z;
+    o[k].w = o[k].w + w * ov.w;
+  };
+  if (ns >= 1 && ns <= 8) {
+    float2 mls[4];
+    float4 ovs[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) part(min(4 * hf + k, ns - 1), mls[k], ovs[k]);
+    const float m = fmaxf(fmaxf(mls[0].x, mls[1].x), fmaxf(mls[2].x, mls[3].x));
+    M = fmaxf(m, xor_shfl(m, 32));
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (4 * hf + k < ns) fold(k, mls[k], ovs[k]);
+  } else {
+    float m = -INFINITY;
+    for (int s = lane; s < ns; s += 64) m = fmaxf(m, ws_ml[((int64_t)(w0 + s) * hq + h) * 2]);
+    M = wave_max(m);
+    for (int t0 = 0; t0 < ns; t0 += 8) {  // splits t0 .. t0 + 7: one per group, in order
+      float2 mls[4];
+      float4 ovs[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) part(min(t0 + 4 * hf + k, ns - 1), mls[k], ovs[k]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (t0 + 4 * hf + k < ns) fold(k, mls[k], ovs[k]);
+    }
+  }
+  auto add = [](float4 x, float4 y) { return make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w); };
+  const float4 t = add(add(o[0], o[1]), add(o[2], o[3]));
+  const float lt = (l[0] + l[1]) + (l[2] + l[3]);
+  const float4 os = add(t, make_float4(xor_shfl(t.x, 32), xor_shfl(t.y, 32), xor_shfl(t.z, 32), xor_shfl(t.w, 32)));
+  const float ls = lt + xor_shfl(lt, 32);
+  if (hf == 0) {
+    const float res[4] = {os.x / ls, os.y / ls, os.z / ls, os.w / ls};
+    const int64_t at = ((int64_t)b * hq + h) * HD + 4 * c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (out_bf16)
+        reinterpret_cast<uint16_t*>(out)[at + e] = (uint16_t)f32_to_bf16_rne(res[e]);
+      else
+        reinterpret_cast<float*>(out)[at + e] = res[e];
+    }
+  }
+}
+
 // Scratch of bi_decode_attention_noalloc: the split partials (o, m, l) in a
 // file-scope device array instead of a caller's workspace, for callers that
 // cannot allocate. Every GPU the library runs on holds its own copy until
@@ -671,9 +777,8 @@ hipError_t launch_prefill_attention(const PrefillParams& p, hipStream_t s) {
   hipLaunchKernelGGL(prefill_split_kernel, dim3((unsigned)(p.n_work * p.num_kv_heads)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)p.n_rows, (unsigned)p.num_q_heads), dim3(128), 0, s,
-                     p.q_offsets, (int)p.total_splits, p.ws_o, p.ws_ml, p.num_q_heads, p.out,
-                     p.out_bf16 ? 1 : 0);
+  hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)p.n_rows, (unsigned)(p.num_q_heads / GQA)), dim3(256), 0,
+                     s, p.q_offsets, (int)p.total_splits, p.ws_o, p.ws_ml, p.num_q_heads, p.out, p.out_bf16 ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -61,12 +61,15 @@ def test_prefill_parity_with_oracle(lib):
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_prefill_equals_decode_bitwise(lib, out_dtype):
-    chunk, ctx = [1, 300, 17, 600], [0, 0, 255, 1000]
+@pytest.mark.parametrize("chunk,ctx", [([1, 300, 17, 600], [0, 0, 255, 1000]),
+                                       # rows of 8 and 9 splits around position 2048, and of 17 and 33
+                                       ([40, 8, 5], [2030, 4200, 8190])],
+                         ids=["up_to_7_splits", "8_to_33_splits"])
+def test_prefill_equals_decode_bitwise(lib, out_dtype, chunk, ctx):
     table, kp, vp = cache_for([c + n for c, n in zip(ctx, chunk)], seed=6100)
     q = S.normal_bf16((sum(chunk), HQ, D), 1.0, seed=6110, device=DEV)
     out, q_pos = prefill(lib, q, kp, vp, table, chunk, ctx, out_dtype)
-    seq = np.repeat(np.arange(4), chunk)
+    seq = np.repeat(np.arange(len(chunk)), chunk)
     dec = decode_rows(lib, q, kp, vp, table, seq, q_pos, out_dtype)
     diff = [r for r in range(sum(chunk)) if not same_bits(out[r], dec[r])]
     say(f"rows differing from decode: {len(diff)} of {sum(chunk)}")
