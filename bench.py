@@ -268,9 +268,16 @@ def negative_control(torch, S, dev):
 
 def gpu_clocks():
     """Shader and memory clocks as rocm-smi reports them (None where it is not available)."""
+    import shutil
     import subprocess
+    smi = shutil.which("rocm-smi")
+    if smi is None:
+        return None
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        # rocm-smi is a Python script: run it with this interpreter rather than through its
+        # "#!/usr/bin/env python3" line, so no process replaces itself with another
+        r = subprocess.run([sys.executable, os.path.realpath(smi), "--showclocks", "--json"], capture_output=True,
+                           text=True, timeout=20)
         d = json.loads(r.stdout)
     except Exception:
         return None
