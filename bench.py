@@ -570,6 +570,8 @@ def main():
                     help="per-config sweep over the workloads' M values (markdown table), then exit")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only measure the prefill attention workload (4 x 2048 tokens) and print its JSON")
+    ap.add_argument("--e2e-only", action="store_true",
+                    help="only measure the end-to-end decode step (36 layers, batch 64) and print its JSON")
     ap.add_argument("--gemm-probe", action="store_true",
                     help="only run each projection GEMM at M = 64, 512 and 4096 and the LM head at M = 256, "
                          "3 launches each ([K,N] weights, fp32 out), for rocprofv3 counter and trace runs; "
@@ -619,6 +621,9 @@ def main():
         return
     if args.prefill_only:
         print(json.dumps(prefill_measure(torch, S, bi, dev)), flush=True)
+        return
+    if args.e2e_only:
+        print(json.dumps(e2e_decode(torch, S, bi, dev)), flush=True)
         return
     wl = Workload(torch, S, bi, dev)
     ops = wl.ops()
