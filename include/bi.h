@@ -293,7 +293,8 @@ bi_status bi_decode_attention_noalloc(const void* q, const void* k_pages, const 
  * sequence. Its reduction is cut at the same multiples of split_tokens as a
  * decode step with p + 1 cached tokens, each split is reduced with the very
  * arithmetic of bi_decode_attention's split kernel, and the partials are
- * merged by its combine. So a token's output has the same bits whether it is
+ * merged with its combine's arithmetic, term for term. So a token's output
+ * has the same bits whether it is
  * prefilled in any chunking, in any batch, or decoded -- the chunked-prefill
  * side of the batch dependence the pages trace to attention (readhandoff.com,
  * agent-run reproducibility pinning, "What does temperature zero actually
@@ -309,7 +310,7 @@ bi_status bi_decode_attention_noalloc(const void* q, const void* k_pages, const 
  *   host_q_pos      int32 [rows]       each row's position,
  *   host_q_offsets  int32 [rows + 1]   split offsets: sum over earlier rows
  *                                      of ceil((pos + 1) / split_tokens),
- *   host_work       int32 [4 n_work]   work items (first row, row count <= 8,
+ *   host_work       int32 [4 n_work]   work items (first row, row count <= 32,
  *                                      sequence, split), split-major per
  *                                      sequence.
  * Returns BI_OK or an error status (the message in bi_last_error_message). */
@@ -328,7 +329,11 @@ bi_status bi_prefill_plan(const int32_t* host_chunk_lens, const int32_t* host_ct
  *                head_dim) bytes.
  *   out          [rows, num_q_heads, head_dim], out_dtype.
  * Supported set as bi_decode_attention (BI_ERR_UNSUPPORTED otherwise). The
- * cache must hold finite values in the slots the chunk sees. */
+ * cache must hold finite values in the slots the chunk sees. The plan's
+ * arrays are read on the device only: a work item whose rows, sequence,
+ * split or pages do not fit the buffers, or a split offset past
+ * total_splits, is skipped (those rows' values are then unspecified); the
+ * kernels never access memory outside the buffers. */
 bi_status bi_prefill_attention(const void* q, const void* k_pages, const void* v_pages,
                                const int32_t* block_table, int64_t max_pages, const int32_t* q_pos,
                                const int32_t* q_offsets, const int32_t* work, int64_t n_work, int64_t n_rows,

@@ -417,7 +417,8 @@ bi_status bi_prefill_attention(const void* q, const void* k_pages, const void* v
     return fail(BI_ERR_NULL, "a required pointer is NULL");
   if (max_pages < 1 || batch < 1 || n_work < 1) return fail(BI_ERR_SHAPE, "max_pages, batch and n_work must be >= 1");
   if (total_splits < n_rows) return fail(BI_ERR_SHAPE, "total_splits < n_rows (every row has at least one split)");
-  if (n_work * num_kv_heads > INT_MAX || n_rows > INT_MAX || num_q_heads > 65535)
+  if (n_work * num_kv_heads > INT_MAX || n_rows > INT_MAX || batch > INT_MAX || total_splits > INT_MAX ||
+      num_q_heads > 65535)
     return fail(BI_ERR_UNSUPPORTED, "grid size out of range");
   const size_t need = bi_decode_workspace_bytes(total_splits, num_q_heads, head_dim);
   if (workspace == nullptr || workspace_bytes < need)
@@ -437,6 +438,7 @@ bi_status bi_prefill_attention(const void* q, const void* k_pages, const void* v
   p.max_pages = max_pages;
   p.n_work = n_work;
   p.n_rows = n_rows;
+  p.batch = batch;
   p.total_splits = total_splits;
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;

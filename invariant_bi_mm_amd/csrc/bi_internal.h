@@ -92,7 +92,7 @@ struct PrefillParams {
   const int32_t* q_offsets;
   const int32_t* work;
   int64_t max_pages;
-  int64_t n_work, n_rows, total_splits;
+  int64_t n_work, n_rows, total_splits, batch;
   int num_q_heads, num_kv_heads;
   float scale;
   float* ws_o;

@@ -35,6 +35,8 @@
 #include "bi_internal.h"
 #include "device_common.h"
 
+#include <climits>
+#include <cstdint>
 #include <mutex>
 #include <type_traits>
 
@@ -418,6 +420,7 @@ struct PrefillArgs {
   const int32_t* qoffs; // [rows + 1]
   const int32_t* work;  // [n_work, 4]: row0, n_rows, sequence, split
   int64_t max_pages;
+  int n_rows, batch, total_splits;
   int hq, hkv;
   float qscale;
   float* ws_o;
@@ -433,8 +436,17 @@ __global__ __launch_bounds__(256) void prefill_split_kernel(PrefillArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row0 = a.work[4 * wi], nq = a.work[4 * wi + 1], b = a.work[4 * wi + 2], s = a.work[4 * wi + 3];
+  // The plan's arrays are device data the host does not read: an item that
+  // does not fit the buffers (rows, sequence, split, the split's pages in
+  // the block table's row) is skipped -- uniformly, before any barrier -- so
+  // every access stays in bounds whatever they hold.
+  if (row0 < 0 || nq < 1 || nq > QB || row0 > a.n_rows - nq || b < 0 || b >= a.batch || s < 0 ||
+      s > INT32_MAX / SPLIT)
+    return;
   const int t0 = s * SPLIT;
-  const int nt_max = min(SPLIT, a.pos[row0 + nq - 1] + 1 - t0);
+  const int64_t nt_l = min((int64_t)SPLIT, (int64_t)a.pos[row0 + nq - 1] + 1 - t0);
+  if (nt_l < 1 || (t0 + nt_l + PAGE - 1) / PAGE > a.max_pages) return;
+  const int nt_max = (int)nt_l;
   const int npg = (nt_max + PAGE - 1) / PAGE;
   const int32_t* bt = a.bt + (int64_t)b * a.max_pages + t0 / PAGE;
   const int64_t head_stride = (int64_t)PAGE * HD;
@@ -452,7 +464,8 @@ __global__ __launch_bounds__(256) void prefill_split_kernel(PrefillArgs a) {
   // partial row of (chunk row row0 + t, split s, query head g GQA), or -1
   // when that row's position is before the split (it does not see it)
   auto part_row = [&](int t) -> int64_t {
-    return spos[t] + 1 - t0 > 0 ? (int64_t)(soff[t] + s) * a.hq + g * GQA : -1;
+    const int64_t slot = (int64_t)soff[t] + s;  // inside the workspace's total_splits slots, or not written
+    return spos[t] + 1 - t0 > 0 && slot >= 0 && slot < a.total_splits ? slot * a.hq + g * GQA : -1;
   };
 
   u32x4 qa[4], qn[4], kf[4][4], vf[8][2];
@@ -769,6 +782,9 @@ hipError_t launch_prefill_attention(const PrefillParams& p, hipStream_t s) {
   a.qoffs = p.q_offsets;
   a.work = p.work;
   a.max_pages = p.max_pages;
+  a.n_rows = (int)p.n_rows;
+  a.batch = (int)p.batch;
+  a.total_splits = (int)p.total_splits;
   a.hq = p.num_q_heads;
   a.hkv = p.num_kv_heads;
   a.qscale = p.scale * LOG2E;

@@ -96,3 +96,31 @@ def test_prefill_independent_of_chunking_and_batch(lib):
     tb = torch.stack([table[1], table[0], table[2]])
     ob, _ = prefill(lib, qb, kp, vp, tb, [64, 333, 50], [836, 100, 0])
     assert same_bits(ob[64:64 + 333], parts[1])
+
+
+def test_prefill_inconsistent_plan_stays_in_bounds(lib):
+    """The plan's arrays live on the device, where the host cannot check them: work items whose row
+    range, sequence, split or pages do not fit the buffers, and split offsets past the workspace, are
+    skipped by the kernels (their rows' values are then unspecified), never followed outside the buffers.
+    A correct call afterwards still gives decode's bits."""
+    chunk, ctx = [40, 9, 30], [200, 500, 700]  # 2 + 2 + 3 work items
+    table, kp, vp = cache_for([c + n for c, n in zip(ctx, chunk)], seed=6300)
+    q = S.normal_bf16((sum(chunk), HQ, D), 1.0, seed=6310, device=DEV)
+    q_pos, q_offs, work, sizes = lib.bi_prefill_plan(torch.tensor(chunk), torch.tensor(ctx))
+    rows, total, n_work = sizes
+    bad = work.clone()
+    assert n_work >= 5
+    bad[0, 0] = -5                 # row before the first
+    bad[1, 2] = 1_000_000          # sequence past the batch
+    bad[2, 1] = 1000               # more rows than an item holds
+    bad[3, 3] = 100_000            # a split no row of the item sees
+    bad[4, 0], bad[4, 1] = rows - 1, 5  # rows past the last
+    bad_offs = q_offs.clone()
+    bad_offs[3] = 1 << 30          # a row whose split slots lie past the workspace
+    out = lib.bi_prefill_attention(q, kp, vp, table.to(DEV), q_pos.to(DEV), bad_offs.to(DEV), bad.to(DEV), sizes)
+    torch.cuda.synchronize()
+    assert out.shape == (rows, HQ, D)
+    good, pos = prefill(lib, q, kp, vp, table, chunk, ctx)
+    seq = np.repeat(np.arange(len(chunk)), chunk)
+    dec = decode_rows(lib, q, kp, vp, table, seq, pos)
+    assert all(same_bits(good[r], dec[r]) for r in range(rows))
