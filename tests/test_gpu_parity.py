@@ -109,14 +109,17 @@ def test_mm_k_zero_and_empty(lib):
 QWEN = [(4096, 6144), (4096, 4096), (4096, 24576), (12288, 4096)]
 
 
+@pytest.mark.parametrize("b_is_nk", [False, True], ids=["kn", "nk"])
 @pytest.mark.parametrize("k,n", QWEN)
 @pytest.mark.parametrize("m", [1, 512, 4096])
-def test_mm_qwen_shapes_sampled(lib, k, n, m):
-    """Full-size projection GEMMs (weights ~N(0,0.02)), sampled rows."""
-    say(f"mm qwen k={k} n={n} m={m}")
+def test_mm_qwen_shapes_sampled(lib, k, n, m, b_is_nk):
+    """Full-size projection GEMMs (weights ~N(0,0.02)), sampled rows, the
+    weight stored [K,N] (the benchmark's layout) or [N,K] (the decode
+    step's)."""
+    say(f"mm qwen k={k} n={n} m={m} b_is_nk={b_is_nk}")
     a = S.normal_bf16((m, k), 1.0, seed=20 + m, device=DEV)
     w = S.normal_bf16((k, n), 0.02, seed=30 + n + k, device=DEV)
-    c = lib.bi_mm(a, w)
+    c = lib.bi_mm(a, w.t().contiguous(), b_is_nk=True) if b_is_nk else lib.bi_mm(a, w)
     rows = sorted({0, m - 1, m // 2, (m * 7) // 11})
     ref = O.mm(bits(a[rows]), bits(w))
     assert_close(f32(c[rows]), ref, f"qwen k={k} n={n} m={m}")
