@@ -397,17 +397,18 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
 // cache (which already holds them). Query row r at position p uses exactly
 // the split structure of a decode step with p + 1 cached tokens: splits
 // s = 0 .. ceil((p + 1) / SPLIT) - 1, each reduced by the functions above
-// with nt = min(SPLIT, p + 1 - s * SPLIT), merged by the decode combine
-// kernel. So a prefilled token's output has the bits a decode step would
-// give it, whatever the chunking and the batch.
+// with nt = min(SPLIT, p + 1 - s * SPLIT), merged with the decode combine's
+// arithmetic (prefill_combine_kernel). So a prefilled token's output has the
+// bits a decode step would give it, whatever the chunking and the batch.
 //
 // One workgroup per (work item, kv head); a work item is up to QB
 // consecutive query rows of one sequence and one split they see. The split's
-// K and V are loaded once into registers for all of them (keys past the last
-// row's nt read 0); the rows then go through the three phases 4 tokens (16
-// query rows) at a time, through one block-sized score array in LDS. For an
-// earlier row, the keys it must not see carry p = 0, and their products (0
-// times a finite cached value) add exact zeros.
+// K and V are loaded once into registers for all of them (V of keys past the
+// last row's nt zeroed once); the rows then go through the three phases 4
+// tokens (16 query rows) at a time, through two block-sized score arrays in
+// LDS used alternately. For an earlier row, the keys it must not see carry
+// p = 0, and their products (0 times a finite cached value) add exact
+// zeros.
 // ---------------------------------------------------------------------------
 constexpr int QB = 32;
 
