@@ -517,6 +517,53 @@ def e2e_decode(torch, S, bi, dev, steps=E2E_STEPS, warmup=1, batch_size=E2E_BATC
 PREFILL_SEQS, PREFILL_TOKENS = 4, 2048
 
 
+def cold_read(torch, S, bi, dev, reps=9):
+    """Cold reads with clean or dirty caches. A 1 GiB buffer is either read
+    (the caches then hold clean lines) or written (the Infinity Cache then
+    holds dirty lines, each evicted by a later miss with a write-back) before
+    every timed launch. Timed: a plain read of the 201 MB gate+up weight
+    (bi_mean over its 24576 rows), and bi_mm on the decode step's projections at
+    M = 1 and 64 with the weights stored [N,K]. Median of the timed launches;
+    rates in bytes of weights per second."""
+    fl = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.zeros((), device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, dirty):
+        ts = []
+        for rep in range(reps + 1):
+            if dirty:
+                fl.fill_(float(rep))
+            else:
+                sink.copy_(fl.sum())
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        ts = sorted(ts[1:])
+        return ts[len(ts) // 2]
+
+    res = {}
+    w_gu = S.normal_bf16((24576, 4096), 0.02, seed=2, device=dev)
+    means = torch.empty(24576, device=dev)
+    for dirty in (False, True):
+        key = "after_write" if dirty else "after_read"
+        t = timed(lambda: bi.bi_mean(w_gu, out=means), dirty)
+        res[f"read_201MB_{key}"] = {"us": round(t, 1), "TB/s": round(w_gu.numel() * 2 / t / 1e6, 2)}
+    for name, k, n in (("qkv", 4096, 6144), ("o", 4096, 4096), ("gate_up", 4096, 24576), ("down", 12288, 4096)):
+        w = S.normal_bf16((n, k), 0.02, seed=3, device=dev)
+        for m in (1, 64):
+            a = S.normal_bf16((m, k), 1.0, seed=4, device=dev)
+            c = torch.empty((m, n), device=dev)
+            for dirty in (False, True):
+                t = timed(lambda: bi.bi_mm(a, w, b_is_nk=True, out=c), dirty)
+                res[f"bi_mm_{name}_M{m}_{'after_write' if dirty else 'after_read'}"] = {
+                    "us": round(t, 1), "TB/s": round(2.0 * n * k / t / 1e6, 2)}
+        del w
+    return res
+
+
 def prefill_measure(torch, S, bi, dev, reps=5):
     """Causal prefill attention of PREFILL_SEQS prompts of PREFILL_TOKENS
     tokens (Qwen3-8B heads: 32 q / 8 kv, head_dim 128, one layer), with the
@@ -570,6 +617,9 @@ def main():
                     help="per-config sweep over the workloads' M values (markdown table), then exit")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only measure the prefill attention workload (4 x 2048 tokens) and print its JSON")
+    ap.add_argument("--cold-read", action="store_true",
+                    help="only time cold reads after a read-only or a write flush (a 201 MB weight and the "
+                         "decode step's small-M GEMMs) and print their JSON")
     ap.add_argument("--e2e-only", action="store_true",
                     help="only measure the end-to-end decode step (36 layers, batch 64) and print its JSON")
     ap.add_argument("--gemm-probe", action="store_true",
@@ -621,6 +671,9 @@ def main():
         return
     if args.prefill_only:
         print(json.dumps(prefill_measure(torch, S, bi, dev)), flush=True)
+        return
+    if args.cold_read:
+        print(json.dumps(cold_read(torch, S, bi, dev)), flush=True)
         return
     if args.e2e_only:
         print(json.dumps(e2e_decode(torch, S, bi, dev)), flush=True)
