@@ -143,31 +143,46 @@ __device__ __forceinline__ void load_v_frags(const uint16_t* vp, const int32_t* 
 }
 
 // Phase 1 for one block of 16 query rows (4 tokens x the GQA heads): the
-// scores S[t][h][key] of the split's SPLIT keys, t < ntok tokens of the
-// block, on the matrix cores:
+// scores S[t][h][key] of the split's SPLIT keys on the matrix cores:
 //   S = (sum_d q[r][d] k[key][d]) * qscale   (qscale = scale * log2(e)),
 // the sum taken by v_mfma_f32_16x16x32_bf16 over d in four steps of 32
 // (exact bf16 products, fp32 accumulation, increasing d), then one fp32
-// multiply; keys at or past nt_of(t) get -inf. Rows past GQA ntok are not
-// stored. The element (r, key) gets the same chain whichever row of the MFMA
-// holds r, so a token's scores do not depend on the other tokens of the block.
+// multiply; keys at or past a token's visible count get -inf. The element
+// (r, key) gets the same chain whichever row of the MFMA holds r, so a
+// token's scores do not depend on the other tokens of the block. Wave w
+// computes keys [64 w, 64 w + 64) as four 16-key tiles; lane l receives the
+// rows of token l / 16 (its 4 GQA heads) at key l % 16 of each tile.
+//
+// scores_step: one d step of the wave's four independent tile chains (FIRST:
+// the chains start here, from zeros); scores_store: tile kt's scores of the
+// lane's token into S; scores_block: the whole block, for the decode kernel
+// (rows of tokens >= ntok are not stored).
+template <bool FIRST>
+__device__ __forceinline__ void scores_step(const u32x4 (&qa)[4], const u32x4 (&kf)[4][4], int ds, f32x4 (&acc)[4]) {
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+    acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[ds]),
+                                                      __builtin_bit_cast(bf16x8, kf[kt][ds]),
+                                                      FIRST ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[kt], 0, 0, 0);
+}
+__device__ __forceinline__ void scores_store(const f32x4& acc, int kt, int t_out, int nt_t, int wave, int lane,
+                                             float qscale, float (*S)[GQA][SROW]) {
+  const int key = 64 * wave + 16 * kt + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) S[t_out][i][key] = key < nt_t ? acc[i] * qscale : -INFINITY;
+}
 template <typename NtOf>
 __device__ __forceinline__ void scores_block(const u32x4 (&qa)[4], const u32x4 (&kf)[4][4], int ntok, NtOf nt_of,
                                              int wave, int lane, float qscale, float (*S)[GQA][SROW]) {
   const int t_out = lane >> 4;  // token of the 4 rows this lane receives (GQA == 4)
-  const int nt_t = t_out < ntok ? nt_of(t_out) : 0;
+  f32x4 acc[4];
+  scores_step<true>(qa, kf, 0, acc);
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int ds = 1; ds < 4; ++ds) scores_step<false>(qa, kf, ds, acc);
+  if (t_out < ntok) {
+    const int nt_t = nt_of(t_out);
 #pragma unroll
-    for (int ds = 0; ds < 4; ++ds)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[ds]),
-                                                    __builtin_bit_cast(bf16x8, kf[kt][ds]), acc, 0, 0, 0);
-    const int key = 64 * wave + 16 * kt + (lane & 15);
-    if (t_out < ntok) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S[t_out][i][key] = key < nt_t ? acc[i] * qscale : -INFINITY;
-    }
+    for (int kt = 0; kt < 4; ++kt) scores_store(acc[kt], kt, t_out, nt_t, wave, lane, qscale, S);
   }
 }
 
@@ -239,6 +254,69 @@ __device__ __forceinline__ void split_softmax_rows(float* const (&row)[R], int l
   }
 }
 
+// Phase 2 for four rows at once, 16 lanes per row (the prefill form), in
+// stages that the prefill kernel interleaves with matrix instructions: lane
+// 16 t + j holds, of row t, the keys 4 j + i + 64 k (i, k = 0..3). The values
+// are those of split_softmax_rows, and so is every rounding: the max is exact
+// in any order; p, hi and lo are per element; and the sum is the same tree of
+// additions. In split_softmax_rows lane L (0..63) first chains keys L,
+// L + 64, L + 128, L + 192 from 0, then the lanes are paired by the bits of L
+// from the lowest up (xor 1, xor 2, xor 4, xor 8 inside each 16, then
+// (R0 + R1) + (R2 + R3) over the four 16-lane rows). Here L = 4 j + i: the
+// chains and the first two levels are in the lane, the next four are DPP
+// moves inside the 16-lane row (after the first two of them the four lanes
+// of a quad hold equal sums, so the half-mirror and mirror moves pair L's
+// bits 4 and 5). Every addition adds the same two values, and addition is
+// commutative, so the bits are equal.
+struct QuadSoftmax {
+  f32x4 v[SPLIT / 64];  // this lane's scores; group k becomes p in exp_group(k)
+  float mx;
+  float leaf[4];
+  __device__ __forceinline__ void load(const float* row, int j) {
+#pragma unroll
+    for (int k = 0; k < SPLIT / 64; ++k) v[k] = *reinterpret_cast<const f32x4*>(row + 4 * j + 64 * k);
+  }
+  __device__ __forceinline__ void max_lane() {
+    mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < SPLIT / 64; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, v[k][i]);
+  }
+  __device__ __forceinline__ void max_row() {
+    auto fmx = [](float x, float y) { return fmaxf(x, y); };
+    mx = fmx(mx, dpp_move<0xB1>(mx));   // quad_perm [1,0,3,2]
+    mx = fmx(mx, dpp_move<0x4E>(mx));   // quad_perm [2,3,0,1]
+    mx = fmx(mx, dpp_move<0x141>(mx));  // row_half_mirror
+    mx = fmx(mx, dpp_move<0x140>(mx));  // row_mirror
+  }
+  // group k: p = 2^(s - max) in place (2^-inf = 0 for masked slots)
+  __device__ __forceinline__ void exp_group(int k) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[k][i] = __builtin_amdgcn_exp2f(v[k][i] - mx);
+  }
+  // group k (groups in increasing order): p's bf16 parts written over the
+  // row (hi at u16 4 j + 64 k, lo PLO further), p added to the lane's chains
+  __device__ __forceinline__ void write_group(float* row, int j, int k) {
+    uint16_t* pb = reinterpret_cast<uint16_t*>(row);
+    const uint32_t h01 = cvt_pk_bf16(v[k][0], v[k][1]), h23 = cvt_pk_bf16(v[k][2], v[k][3]);
+    const uint32_t l01 = cvt_pk_bf16(v[k][0] - bf16lo(h01), v[k][1] - bf16hi(h01));
+    const uint32_t l23 = cvt_pk_bf16(v[k][2] - bf16lo(h23), v[k][3] - bf16hi(h23));
+    *reinterpret_cast<uint2*>(pb + 4 * j + 64 * k) = make_uint2(h01, h23);
+    *reinterpret_cast<uint2*>(pb + PLO + 4 * j + 64 * k) = make_uint2(l01, l23);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) leaf[i] = (k == 0 ? 0.0f : leaf[i]) + v[k][i];
+  }
+  __device__ __forceinline__ float sum_row() const {
+    float l = (leaf[0] + leaf[1]) + (leaf[2] + leaf[3]);
+    l = l + dpp_move<0xB1>(l);
+    l = l + dpp_move<0x4E>(l);
+    l = l + dpp_move<0x141>(l);
+    l = l + dpp_move<0x140>(l);
+    return l;
+  }
+};
+
 // V of keys at or past nt is zeroed in the fragments themselves, once per
 // split: the cache past a sequence's last token may hold any bits, and
 // 0 * NaN would poison the sum. A full split (nt == SPLIT) has nothing to
@@ -266,36 +344,61 @@ __device__ __forceinline__ void mask_v(u32x4 (&vf)[8][2], int nt, int lane) {
 // by phase 2), so the products carry ~16 bits of p; the chain per element
 // is: key steps of 32 in increasing order, hi then lo in each, fp32
 // accumulation. acc[dt] = the wave's tile dt: lane l holds rows
-// 16 rb + 4 (l / 16) + i (i = 0..3), i.e. token 4 rb + l / 16 and GQA head i,
-// column d = 32 w + 16 dt + l % 16. Rows of tokens >= ntok repeat token 0's
-// p (never stored).
-__device__ __forceinline__ void split_pv(const u32x4 (&vf)[8][2], const float (*S)[GQA][SROW], int rb, int ntok,
-                                         int lane, f32x4 (&acc)[2]) {
-  const int r = 16 * rb + (lane & 15);  // the query row this lane feeds
+// 4 (l / 16) + i (i = 0..3), i.e. token l / 16 and GQA head i, column
+// d = 32 w + 16 dt + l % 16. Rows of tokens >= ntok repeat token 0's p
+// (never stored).
+//
+// pv_row: the lane's p row (the A operand's row l % 16); pv_operands: one
+// key step's hi and lo operands from it; pv_step: that key step for both
+// column tiles, hi then lo into each chain.
+__device__ __forceinline__ const uint16_t* pv_row(const float (*S)[GQA][SROW], int ntok, int lane) {
+  const int r = lane & 15;  // the query row this lane feeds
   const int t = r / GQA;
-  const int q4 = lane >> 4;
-  const uint16_t* prow = reinterpret_cast<const uint16_t*>(S[t < ntok ? t : 0][r % GQA]) + 8 * q4;
-  acc[0] = acc[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  return reinterpret_cast<const uint16_t*>(S[t < ntok ? t : 0][r % GQA]) + 8 * (lane >> 4);
+}
+__device__ __forceinline__ void pv_operands(const uint16_t* prow, int ks, u32x4& hi, u32x4& lo) {
+  hi = *reinterpret_cast<const u32x4*>(prow + 32 * ks);
+  lo = *reinterpret_cast<const u32x4*>(prow + PLO + 32 * ks);
+}
+template <bool FIRST>
+__device__ __forceinline__ void pv_step(const u32x4 (&vf)[8][2], int ks, const u32x4& hi, const u32x4& lo,
+                                        f32x4 (&acc)[2]) {
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi),
+                                                      __builtin_bit_cast(bf16x8, vf[ks][dt]),
+                                                      FIRST ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : acc[dt], 0, 0, 0);
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, lo),
+                                                      __builtin_bit_cast(bf16x8, vf[ks][dt]), acc[dt], 0, 0, 0);
+}
+__device__ __forceinline__ void split_pv(const u32x4 (&vf)[8][2], const float (*S)[GQA][SROW], int ntok, int lane,
+                                         f32x4 (&acc)[2]) {
+  const uint16_t* prow = pv_row(S, ntok, lane);
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(prow + 32 * ks);
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(prow + PLO + 32 * ks);
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt) {
-      const bf16x8 v = __builtin_bit_cast(bf16x8, vf[ks][dt]);
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi), v, acc[dt], 0, 0, 0);
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, lo), v, acc[dt], 0, 0, 0);
-    }
+    u32x4 hi, lo;
+    pv_operands(prow, ks, hi, lo);
+    if (ks == 0) pv_step<true>(vf, ks, hi, lo, acc);
+    else pv_step<false>(vf, ks, hi, lo, acc);
   }
 }
 
 // The wave's share of a row block's partials, for the token of this lane's
-// rows: out points at that token's [GQA][HD] fp32 partial (or is null).
+// rows: out points at that token's [GQA][HD] fp32 partial. NT: non-temporal
+// stores (prefill's partials, written once and read back by the combine
+// kernel after all of them).
+template <bool NT>
 __device__ __forceinline__ void store_pv(const f32x4 (&acc)[2], int wave, int lane, float* out) {
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[i * HD + 32 * wave + 16 * dt + (lane & 15)] = acc[dt][i];
+    for (int i = 0; i < 4; ++i) {
+      float* const at = out + i * HD + 32 * wave + 16 * dt + (lane & 15);
+      if constexpr (NT) __builtin_nontemporal_store(acc[dt][i], at);
+      else *at = acc[dt][i];
+    }
 }
 
 template <bool NT>
@@ -388,8 +491,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
   __syncthreads();
   f32x4 acc[2];
   mask_v(vf, nt, lane);
-  split_pv(vf, S, 0, 1, lane, acc);
-  if (lane < 16) store_pv(acc, wave, lane, a.ws_o + base * HD);  // rows 0..3: the one token
+  split_pv(vf, S, 1, lane, acc);
+  if (lane < 16) store_pv<false>(acc, wave, lane, a.ws_o + base * HD);  // rows 0..3: the one token
 }
 
 // ---------------------------------------------------------------------------
@@ -405,12 +508,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
 // consecutive query rows of one sequence and one split they see. The split's
 // K and V are loaded once into registers for all of them (V of keys past the
 // last row's nt zeroed once); the rows then go through the three phases 4
-// tokens (16 query rows) at a time, through two block-sized score arrays in
-// LDS used alternately. For an earlier row, the keys it must not see carry
-// p = 0, and their products (0 times a finite cached value) add exact
-// zeros.
+// tokens (16 query rows) at a time, pipelined over three block-sized score
+// arrays in LDS (see the kernel). For an earlier row, the keys it must not
+// see carry p = 0, and their products (0 times a finite cached value) add
+// exact zeros. Phase 2 uses the 16-lanes-per-row form (QuadSoftmax), with
+// split_softmax_rows's bits.
 // ---------------------------------------------------------------------------
-constexpr int QB = 32;
+constexpr int QB = 64;
 
 struct PrefillArgs {
   const uint16_t* q;  // [rows, hq, HD]
@@ -428,10 +532,13 @@ struct PrefillArgs {
   float* ws_ml;
 };
 
-__global__ __launch_bounds__(256) void prefill_split_kernel(PrefillArgs a) {
-  // one block of 4 tokens, two buffers: block i writes S[i % 2], so the next
-  // block's scores need not wait for this block's p.v reads
-  __shared__ float S[2][4][GQA][SROW];
+// Two workgroups per CU (at most 256 registers per lane, half of a SIMD's),
+// so that a second wave on each SIMD fills the first one's gaps.
+__global__ __launch_bounds__(256, 2) void prefill_split_kernel(PrefillArgs a) {
+  // Three score buffers of one block (4 tokens) each, in rotation: block i
+  // uses buffer i % 3 (separate arrays, so the compiler sees that the
+  // buffers of one step never overlap).
+  __shared__ __align__(16) float S0[4][GQA][SROW], S1[4][GQA][SROW], S2[4][GQA][SROW];
 
   const int wi = blockIdx.x / a.hkv, g = blockIdx.x % a.hkv;
   const int tid = threadIdx.x;
@@ -469,49 +576,128 @@ __global__ __launch_bounds__(256) void prefill_split_kernel(PrefillArgs a) {
     return spos[t] + 1 - t0 > 0 && slot >= 0 && slot < a.total_splits ? slot * a.hq + g * GQA : -1;
   };
 
-  u32x4 qa[4], qn[4], kf[4][4], vf[8][2];
-  load_q_block(q0, q_tok, min(4, nq), lane, qa);
+  u32x4 qc[4], kf[4][4], vf[8][2];
+  load_q_block(q0, q_tok, min(4, nq), lane, qc);
   load_k_frags<false>(a.kp, bt, npg, page_stride, head_off, wave, lane, kf);
   load_v_frags<false>(a.vp, bt, npg, page_stride, head_off, wave, lane, vf);
   __builtin_amdgcn_sched_barrier(0);  // every load issued before the first MFMA waits
   __syncthreads();                    // spos, soff
-  for (int tb = 0; tb < nq; tb += 4) {  // tokens tb .. tb + 3 of the item
-    const int nb = min(4, nq - tb);
-    float(*Sb)[GQA][SROW] = S[(tb >> 2) & 1];
-    if (tb + 4 < nq) load_q_block(q0 + (tb + 4) * q_tok, q_tok, min(4, nq - tb - 4), lane, qn);  // next block
-    scores_block(qa, kf, nb, [&](int t) { return min(SPLIT, spos[tb + t] + 1 - t0); }, wave, lane, a.qscale, Sb);
-    __syncthreads();
-    {
-      // wave h: head h of the block's 4 tokens (rows of tokens >= nb hold
-      // nothing of use; they are processed and never read)
-      float mx[4], l[4];
-      float* const rows[4] = {Sb[0][wave], Sb[1][wave], Sb[2][wave], Sb[3][wave]};
-      split_softmax_rows<4>(rows, lane, mx, l);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if (t < nb) {
-          const int64_t base = part_row(tb + t);
-          if (lane == 0 && base >= 0) {
-            a.ws_ml[(base + wave) * 2 + 0] = mx[t];
-            a.ws_ml[(base + wave) * 2 + 1] = l[t];
-          }
-        }
+  const int t_lane = lane >> 4;       // the token of this lane's softmax row, scores and p.v outputs
+  const int j = lane & 15;            // the lane's place in its softmax row
+  const int nblk = (nq + 3) / 4;      // blocks of 4 tokens
+  auto nb_of = [&](int i) { return min(4, nq - 4 * i); };
+  auto row_base = [&](int i) -> int64_t { return t_lane < nb_of(i) ? part_row(4 * i + t_lane) : -1; };
+  auto qload = [&](int i) { load_q_block(q0 + 4 * i * q_tok, q_tok, nb_of(i), lane, qc); };
+  auto store_ml = [&](int i, float mx, float l) {
+    const int64_t base = row_base(i);
+    if (j == 0 && base >= 0) {
+      a.ws_ml[(base + wave) * 2 + 0] = mx;
+      a.ws_ml[(base + wave) * 2 + 1] = l;
+    }
+  };
+  auto store_o = [&](int i, const f32x4 (&acc)[2]) {
+    const int64_t base = row_base(i);
+    if (base >= 0) store_pv<true>(acc, wave, lane, a.ws_o + base * HD);
+  };
+  using Buf = float (*)[GQA][SROW];
+  int nt_min = SPLIT;  // keys seen by the item's first row (the fewest)
+  for (int t = 0; t < nq; ++t) nt_min = min(nt_min, spos[t] + 1 - t0);
+  nt_min = __builtin_amdgcn_readfirstlane(nt_min);
+
+  // The item's blocks of 4 tokens run as a pipeline with one barrier per
+  // block. Step i takes block i's softmax, block i - 1's p.v and block i + 1's
+  // scores, three different buffers (block b uses buffer b % 3). Before the
+  // barrier that ends step i, every wave has written block i + 1's scores and
+  // block i's p and has read block i - 1's p; so after it, block i + 2's
+  // scores may overwrite block i - 1's buffer. Inside a step the work is cut
+  // into chunks, each holding one group of matrix instructions (a d step of
+  // the scores or a key step of p.v) and one stage of the softmax, so that a
+  // wave's vector work sits between its matrix work (and the second wave on
+  // the SIMD can fill the gaps); scheduling barriers keep the chunks in order.
+  // Where a row of the item does not see the whole split (masked), its keys
+  // past its position get -inf scores (p = 0 exactly) and V past the last
+  // row's keys is zeroed once, so every product with an unseen key is an
+  // exact zero.
+  const bool masked = nt_min < SPLIT;  // uniform
+  {
+    // keys this lane's token of block i sees
+    auto nt_tok = [&](int i) { return t_lane < nb_of(i) ? min(SPLIT, spos[4 * i + t_lane] + 1 - t0) : 0; };
+    f32x4 sacc[4], pacc[2];
+    u32x4 phi[2], plo[2];
+    auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+    auto step = [&](int i, Buf Ssm, Buf Spv, Buf Ssc) {
+      const bool has_pv = i >= 1, has_sc = i + 1 < nblk;  // uniform
+      float* const row = Ssm[t_lane][wave];
+      const uint16_t* prow = pv_row(Spv, has_pv ? nb_of(i - 1) : 1, lane);
+      const int nt_sc = has_sc ? nt_tok(i + 1) : SPLIT;
+      QuadSoftmax sm;
+      sm.load(row, j);
+      if (has_pv) {
+        pv_operands(prow, 0, phi[0], plo[0]);
+        pv_operands(prow, 1, phi[1], plo[1]);
       }
-    }
-    __syncthreads();
-    f32x4 acc[2];
-    if (tb == 0) mask_v(vf, nt_max, lane);  // once for the item's blocks
-    split_pv(vf, Sb, 0, nb, lane, acc);
-    const int t = lane >> 4;
-    if (t < nb) {
-      const int64_t base = part_row(tb + t);
-      if (base >= 0) store_pv(acc, wave, lane, a.ws_o + base * HD);
-    }
-    // no barrier here: the next block writes the other score buffer, and the
-    // one after it passes two barriers that every wave reaches only after
-    // this block's p.v reads
+      fence();
+      if (has_sc) scores_step<true>(qc, kf, 0, sacc);
+      sm.max_lane();
+      fence();
+      if (has_sc) scores_step<false>(qc, kf, 1, sacc);
+      sm.max_row();
+      fence();
+      if (has_sc) scores_step<false>(qc, kf, 2, sacc);
+      sm.exp_group(0);
+      fence();
+      if (has_sc) {
+        scores_step<false>(qc, kf, 3, sacc);
+        qload(min(i + 2, nblk - 1));  // the next step's scores; qc is free from here on
+      }
+      sm.write_group(row, j, 0);
+      sm.exp_group(1);
+      fence();
+      // key steps 0..7 of block i - 1's p.v, the operands read two steps ahead
 #pragma unroll
-    for (int ds = 0; ds < 4; ++ds) qa[ds] = qn[ds];
+      for (int ks = 0; ks < 8; ++ks) {
+        if (has_pv) {
+          if (ks == 0) pv_step<true>(vf, ks, phi[0], plo[0], pacc);
+          else pv_step<false>(vf, ks, phi[ks & 1], plo[ks & 1], pacc);
+          if (ks + 2 < 8) pv_operands(prow, ks + 2, phi[ks & 1], plo[ks & 1]);
+        }
+        if (ks == 0) sm.write_group(row, j, 1);
+        if (ks == 1) sm.exp_group(2);
+        if (ks == 2) sm.write_group(row, j, 2);
+        if (ks == 3) sm.exp_group(3);
+        if (ks == 4) sm.write_group(row, j, 3);
+        if (has_sc && ks >= 4) scores_store(sacc[ks - 4], ks - 4, t_lane, nt_sc, wave, lane, a.qscale, Ssc);
+        fence();
+      }
+      store_ml(i, sm.mx, sm.sum_row());
+      if (has_pv) store_o(i - 1, pacc);
+      __syncthreads();
+    };
+    if (masked) mask_v(vf, nt_max, lane);
+    {  // block 0's scores
+      const int nt0 = nt_tok(0);
+      scores_step<true>(qc, kf, 0, sacc);
+#pragma unroll
+      for (int ds = 1; ds < 4; ++ds) scores_step<false>(qc, kf, ds, sacc);
+      if (nblk > 1) qload(1);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) scores_store(sacc[kt], kt, t_lane, nt0, wave, lane, a.qscale, S0);
+      __syncthreads();
+    }
+    for (int i = 0; i < nblk;) {
+      step(i, S0, S2, S1);  // i = 0 (mod 3)
+      if (++i >= nblk) break;
+      step(i, S1, S0, S2);  // i = 1 (mod 3)
+      if (++i >= nblk) break;
+      step(i, S2, S1, S0);  // i = 2 (mod 3)
+      ++i;
+    }
+    {  // the last block's p.v
+      const int i = nblk - 1;
+      f32x4 acc[2];
+      split_pv(vf, i % 3 == 0 ? S0 : i % 3 == 1 ? S1 : S2, nb_of(i), lane, acc);
+      store_o(i, acc);
+    }
   }
 }
 
