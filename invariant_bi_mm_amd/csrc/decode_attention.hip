@@ -530,10 +530,13 @@ struct PrefillArgs {
   float qscale;
   float* ws_o;
   float* ws_ml;
+  int64_t ml_off;     // ws_ml - ws_o, in floats
+  uint32_t ws_bytes;  // bytes of ws_o and ws_ml together (below 2^31 when BUFST)
 };
 
 // Two workgroups per CU (at most 256 registers per lane, half of a SIMD's),
 // so that a second wave on each SIMD fills the first one's gaps.
+template <bool BUFST>
 __global__ __launch_bounds__(256, 2) void prefill_split_kernel(PrefillArgs a) {
   // Three score buffers of one block (4 tokens) each, in rotation: block i
   // uses buffer i % 3 (separate arrays, so the compiler sees that the
@@ -588,16 +591,44 @@ __global__ __launch_bounds__(256, 2) void prefill_split_kernel(PrefillArgs a) {
   auto nb_of = [&](int i) { return min(4, nq - 4 * i); };
   auto row_base = [&](int i) -> int64_t { return t_lane < nb_of(i) ? part_row(4 * i + t_lane) : -1; };
   auto qload = [&](int i) { load_q_block(q0 + 4 * i * q_tok, q_tok, nb_of(i), lane, qc); };
+  // BUFST (the workspace is below 2 GiB): the partials go out as raw buffer
+  // stores through one resource over ws_o and ws_ml; a lane with nothing to
+  // write gets an offset past the resource's end, and the hardware drops its
+  // store. So no branch surrounds the stores, and the compiler counts a
+  // pipeline step's memory operations exactly: a wait for a load also waits
+  // for the stores issued before it, and a branch around the stores made it
+  // assume none had been issued, waiting for the previous step's stores.
+  // Otherwise, plain stores under a branch.
+  constexpr uint32_t DROP = 0x80000000u;  // past any resource of BUFST
+  const __amdgpu_buffer_rsrc_t ws_rsrc = __builtin_amdgcn_make_buffer_rsrc(a.ws_o, 0, (int)a.ws_bytes, 0x00020000);
+  constexpr int NT = 2;  // cache policy: non-temporal (written once, read back by the combine)
   auto store_ml = [&](int i, float mx, float l) {
     const int64_t base = row_base(i);
-    if (j == 0 && base >= 0) {
+    if constexpr (BUFST) {
+      const uint32_t off = j == 0 && base >= 0 ? (uint32_t)(a.ml_off + (base + wave) * 2) * 4u : DROP;
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(mx), __float_as_uint(l)}, ws_rsrc, (int)off, 0, 0);
+    } else if (j == 0 && base >= 0) {
       a.ws_ml[(base + wave) * 2 + 0] = mx;
       a.ws_ml[(base + wave) * 2 + 1] = l;
     }
   };
+  // store_o(-1, zeros) issues the same stores, all dropped (BUFST): the
+  // first step does it, so that every step of the pipeline has the same
+  // memory operations and the compiler's count at the loop's head is exact.
   auto store_o = [&](int i, const f32x4 (&acc)[2]) {
-    const int64_t base = row_base(i);
-    if (base >= 0) store_pv<true>(acc, wave, lane, a.ws_o + base * HD);
+    const int64_t base = i >= 0 ? row_base(i) : -1;
+    if constexpr (BUFST) {
+      const uint32_t off =
+          base >= 0 ? (uint32_t)(base * HD + 32 * wave + (lane & 15)) * 4u : DROP;  // + (i HD + 16 dt) 4
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[dt][h]), ws_rsrc,
+                                                (int)(off + (uint32_t)(h * HD + 16 * dt) * 4u), 0, NT);
+    } else if (base >= 0) {
+      store_pv<true>(acc, wave, lane, a.ws_o + base * HD);
+    }
   };
   using Buf = float (*)[GQA][SROW];
   int nt_min = SPLIT;  // keys seen by the item's first row (the fewest)
@@ -625,8 +656,10 @@ __global__ __launch_bounds__(256, 2) void prefill_split_kernel(PrefillArgs a) {
     f32x4 sacc[4], pacc[2];
     u32x4 phi[2], plo[2];
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
-    auto step = [&](int i, Buf Ssm, Buf Spv, Buf Ssc) {
-      const bool has_pv = i >= 1, has_sc = i + 1 < nblk;  // uniform
+    // has_pv (i >= 1) and has_sc (i + 1 < nblk) are compile-time, so that a
+    // step in the middle of the item is straight-line code
+    auto step = [&](auto pv_tag, auto sc_tag, int i, Buf Ssm, Buf Spv, Buf Ssc) {
+      constexpr bool has_pv = decltype(pv_tag)::value, has_sc = decltype(sc_tag)::value;
       float* const row = Ssm[t_lane][wave];
       const uint16_t* prow = pv_row(Spv, has_pv ? nb_of(i - 1) : 1, lane);
       const int nt_sc = has_sc ? nt_tok(i + 1) : SPLIT;
@@ -670,7 +703,12 @@ __global__ __launch_bounds__(256, 2) void prefill_split_kernel(PrefillArgs a) {
         fence();
       }
       store_ml(i, sm.mx, sm.sum_row());
-      if (has_pv) store_o(i - 1, pacc);
+      if constexpr (has_pv) {
+        store_o(i - 1, pacc);
+      } else if constexpr (BUFST) {
+        const f32x4 zeros[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+        store_o(-1, zeros);
+      }
       __syncthreads();
     };
     if (masked) mask_v(vf, nt_max, lane);
@@ -684,13 +722,29 @@ __global__ __launch_bounds__(256, 2) void prefill_split_kernel(PrefillArgs a) {
       for (int kt = 0; kt < 4; ++kt) scores_store(sacc[kt], kt, t_lane, nt0, wave, lane, a.qscale, S0);
       __syncthreads();
     }
-    for (int i = 0; i < nblk;) {
-      step(i, S0, S2, S1);  // i = 0 (mod 3)
-      if (++i >= nblk) break;
-      step(i, S1, S0, S2);  // i = 1 (mod 3)
-      if (++i >= nblk) break;
-      step(i, S2, S1, S0);  // i = 2 (mod 3)
-      ++i;
+    // V has arrived before the pipeline starts (a use here; otherwise the
+    // compiler would count V's loads as outstanding in every step)
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) asm volatile("" ::"v"(vf[ks][dt]));
+    constexpr std::true_type T{};
+    constexpr std::false_type F{};
+    if (nblk == 1) {
+      step(F, F, 0, S0, S2, S1);
+    } else {
+      step(F, T, 0, S0, S2, S1);
+      for (int i = 1; i <= nblk - 2;) {
+        step(T, T, i, S1, S0, S2);  // i = 1 (mod 3)
+        if (++i > nblk - 2) break;
+        step(T, T, i, S2, S1, S0);  // i = 2 (mod 3)
+        if (++i > nblk - 2) break;
+        step(T, T, i, S0, S2, S1);  // i = 0 (mod 3)
+        ++i;
+      }
+      const int i = nblk - 1;
+      step(T, F, i, i % 3 == 0 ? S0 : i % 3 == 1 ? S1 : S2, (i - 1) % 3 == 0 ? S0 : (i - 1) % 3 == 1 ? S1 : S2,
+           S0);
     }
     {  // the last block's p.v
       const int i = nblk - 1;
@@ -977,7 +1031,13 @@ hipError_t launch_prefill_attention(const PrefillParams& p, hipStream_t s) {
   a.qscale = p.scale * LOG2E;
   a.ws_o = p.ws_o;
   a.ws_ml = p.ws_ml;
-  hipLaunchKernelGGL(prefill_split_kernel, dim3((unsigned)(p.n_work * p.num_kv_heads)), dim3(256), 0, s, a);
+  a.ml_off = p.ws_ml - p.ws_o;
+  const int64_t ws_bytes = (a.ml_off + p.total_splits * p.num_q_heads * 2) * (int64_t)sizeof(float);
+  a.ws_bytes = (uint32_t)min(ws_bytes, (int64_t)INT32_MAX);
+  if (ws_bytes < INT32_MAX)
+    hipLaunchKernelGGL(prefill_split_kernel<true>, dim3((unsigned)(p.n_work * p.num_kv_heads)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(prefill_split_kernel<false>, dim3((unsigned)(p.n_work * p.num_kv_heads)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)p.n_rows, (unsigned)(p.num_q_heads / GQA)), dim3(256), 0,

@@ -124,3 +124,25 @@ def test_prefill_inconsistent_plan_stays_in_bounds(lib):
     seq = np.repeat(np.arange(len(chunk)), chunk)
     dec = decode_rows(lib, q, kp, vp, table, seq, pos)
     assert all(same_bits(good[r], dec[r]) for r in range(rows))
+
+
+def test_prefill_large_workspace_equals_decode_bitwise(lib):
+    """A workspace of 2 GiB or more takes the split kernel's plain-store path (smaller ones use buffer
+    stores through one 32-bit-addressed resource): 2048 chunk tokens at positions 16384.. see 65-72
+    splits each, ~140k split slots, a 2.3 GB workspace. Sampled rows have decode's bits."""
+    chunk, ctx = [2048], [16384]
+    table, kp, vp = cache_for([ctx[0] + chunk[0]], seed=6400)
+    q = S.normal_bf16((chunk[0], HQ, D), 1.0, seed=6410, device=DEV)
+    q_pos, q_offs, work, sizes = lib.bi_prefill_plan(torch.tensor(chunk), torch.tensor(ctx))
+    rows, total, n_work = sizes
+    need = lib.bi_decode_workspace_bytes(total, HQ, D)
+    say(f"split slots {total}, workspace {need / 2**30:.2f} GiB")
+    assert need >= 2 ** 31
+    out = lib.bi_prefill_attention(q, kp, vp, table.to(DEV), q_pos.to(DEV), q_offs.to(DEV), work.to(DEV), sizes)
+    rng = np.random.default_rng(6420)
+    sample = np.unique(np.concatenate([[0, 1, 255, 256, rows - 1], rng.integers(0, rows, 59)]))
+    dec = decode_rows(lib, q[sample].contiguous(), kp, vp, table, np.zeros(len(sample), dtype=np.int64),
+                      q_pos[sample])
+    diff = [int(r) for k, r in enumerate(sample) if not same_bits(out[r], dec[k])]
+    say(f"sampled rows differing from decode: {len(diff)} of {len(sample)}")
+    assert not diff
