@@ -4,6 +4,7 @@
 #include "bi.h"
 
 #include <climits>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -276,7 +277,9 @@ bi_status decode_attention_impl(const void* q, const void* k_pages, const void* 
   if (total_splits < batch || total_splits > batch * max_splits_per_seq)
     return fail(BI_ERR_SHAPE, "total_splits=%lld inconsistent with batch=%lld and max_pages=%lld",
                 (long long)total_splits, (long long)batch, (long long)max_pages);
-  if (total_splits * num_kv_heads > INT_MAX || batch > INT_MAX || num_kv_heads > 65535 || num_q_heads > 65535)
+  // each launch's work items (workgroups x threads) must fit in 32 bits
+  if (batch > INT_MAX || num_kv_heads > 65535 || num_q_heads > 65535 ||
+      total_splits * num_kv_heads * 256 > (int64_t)UINT32_MAX || batch * num_q_heads * 128 > (int64_t)UINT32_MAX)
     return fail(BI_ERR_UNSUPPORTED, "grid size out of range");
   const size_t need = bi_decode_workspace_bytes(total_splits, num_q_heads, head_dim);
   if (scratch && need > bi::decode_scratch_bytes())
@@ -417,8 +420,9 @@ bi_status bi_prefill_attention(const void* q, const void* k_pages, const void* v
     return fail(BI_ERR_NULL, "a required pointer is NULL");
   if (max_pages < 1 || batch < 1 || n_work < 1) return fail(BI_ERR_SHAPE, "max_pages, batch and n_work must be >= 1");
   if (total_splits < n_rows) return fail(BI_ERR_SHAPE, "total_splits < n_rows (every row has at least one split)");
-  if (n_work * num_kv_heads > INT_MAX || n_rows > INT_MAX || batch > INT_MAX || total_splits > INT_MAX ||
-      num_q_heads > 65535)
+  // each launch's work items (workgroups x threads) must fit in 32 bits
+  if (n_rows > INT_MAX || batch > INT_MAX || total_splits > INT_MAX || num_q_heads > 65535 ||
+      n_work * num_kv_heads * 256 > (int64_t)UINT32_MAX || n_rows * (num_q_heads / 4) * 256 > (int64_t)UINT32_MAX)
     return fail(BI_ERR_UNSUPPORTED, "grid size out of range");
   const size_t need = bi_decode_workspace_bytes(total_splits, num_q_heads, head_dim);
   if (workspace == nullptr || workspace_bytes < need)

@@ -774,7 +774,9 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const int32_t* __re
   __shared__ float red[2];
   __shared__ float4 po[2][HD / 4];
   __shared__ float pl[2];
-  const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  // the heads of one sequence are adjacent in dispatch order, so they read
+  // (and write) the sequence's contiguous partials (and output) together
+  const int b = blockIdx.x / hq, h = blockIdx.x % hq, tid = threadIdx.x;
   const int pg = tid >> 5, c = tid & 31, wv = tid >> 6;
   // The row's splits [offs[b], offs[b+1]), clamped to the workspace's cap
   // splits so that offsets on the device can never send a read past it.
@@ -881,8 +883,10 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(const int32_t* __r
                                                                const float* __restrict__ ws_o,
                                                                const float* __restrict__ ws_ml, int hq,
                                                                void* __restrict__ out, int out_bf16) {
-  const int b = blockIdx.x, lane = threadIdx.x & 63;
-  const int h = 4 * blockIdx.y + (threadIdx.x >> 6);
+  // the head groups of one row are adjacent in dispatch order, so they read
+  // (and write) the row's contiguous partials (and output) together
+  const int b = blockIdx.x / (hq / GQA), lane = threadIdx.x & 63;
+  const int h = GQA * (blockIdx.x % (hq / GQA)) + (threadIdx.x >> 6);
   const int hf = lane >> 5, c = lane & 31;
   // the row's splits [offs[b], offs[b+1]), clamped to the workspace's cap
   const int w1 = min(max(offs[b + 1], 0), cap);
@@ -1007,7 +1011,7 @@ hipError_t launch_decode_attention(const DecodeParams& p, hipStream_t s) {
     hipLaunchKernelGGL(decode_split_kernel<false>, dim3((unsigned)(p.total_splits * p.num_kv_heads)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)p.batch, (unsigned)p.num_q_heads), dim3(128), 0, s,
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(p.batch * p.num_q_heads)), dim3(128), 0, s,
                      p.split_offsets, (int)p.total_splits, p.ws_o, p.ws_ml, p.num_q_heads, p.out,
                      p.out_bf16 ? 1 : 0);
   return hipGetLastError();
@@ -1040,7 +1044,7 @@ hipError_t launch_prefill_attention(const PrefillParams& p, hipStream_t s) {
     hipLaunchKernelGGL(prefill_split_kernel<false>, dim3((unsigned)(p.n_work * p.num_kv_heads)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)p.n_rows, (unsigned)(p.num_q_heads / GQA)), dim3(256), 0,
+  hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)(p.n_rows * (p.num_q_heads / GQA))), dim3(256), 0,
                      s, p.q_offsets, (int)p.total_splits, p.ws_o, p.ws_ml, p.num_q_heads, p.out, p.out_bf16 ? 1 : 0);
   return hipGetLastError();
 }

@@ -131,6 +131,7 @@ def test_decode_validation(bi):
     assert attn(bi, flags=2) == UNSUPPORTED
     assert attn(bi, split=128) == UNSUPPORTED
     assert attn(bi, hq=16) == UNSUPPORTED
+    assert attn(bi, batch=1 << 23, total=1 << 23) == UNSUPPORTED  # work items of a launch past 2^32
     assert attn(bi, dt=3) == DTYPE
     assert attn(bi, batch=-1) == SHAPE
     assert attn(bi, q=None) == NULL
@@ -215,6 +216,7 @@ def test_prefill_attention_validation(bi):
                                            k.get("dt", 1), None)
     assert pa(rows=-1) == SHAPE and pa(dt=3) == DTYPE and pa(d=64) == UNSUPPORTED and pa(split=128) == UNSUPPORTED
     assert pa(hq=16) == UNSUPPORTED and pa(out=None) == NULL and pa(n_work=0) == SHAPE
+    assert pa(rows=1 << 22, total=1 << 22) == UNSUPPORTED  # the combine's work items past 2^32
     assert pa(total=5) == SHAPE and pa(wsb=100) == WORKSPACE and pa(ws=A2) == ALIGN and pa(rows=0, out=None) == OK
 
 
