@@ -310,7 +310,7 @@ bi_status bi_decode_attention_noalloc(const void* q, const void* k_pages, const 
  *   host_q_pos      int32 [rows]       each row's position,
  *   host_q_offsets  int32 [rows + 1]   split offsets: sum over earlier rows
  *                                      of ceil((pos + 1) / split_tokens),
- *   host_work       int32 [4 n_work]   work items (first row, row count <= 64,
+ *   host_work       int32 [4 n_work]   work items (first row, row count <= 128,
  *                                      sequence, split), split-major per
  *                                      sequence.
  * Returns BI_OK or an error status (the message in bi_last_error_message). */

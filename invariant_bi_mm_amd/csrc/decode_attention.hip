@@ -514,7 +514,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitArgs a) {
 // exact zeros. Phase 2 uses the 16-lanes-per-row form (QuadSoftmax), with
 // split_softmax_rows's bits.
 // ---------------------------------------------------------------------------
-constexpr int QB = 64;
+constexpr int QB = 128;
 
 struct PrefillArgs {
   const uint16_t* q;  // [rows, hq, HD]

@@ -42,7 +42,7 @@ hipError_t launch_decode_attention(const DecodeParams&, hipStream_t) { ++g_launc
 size_t decode_scratch_bytes() { return BI_DECODE_NOALLOC_MAX_BYTES; }
 hipError_t decode_scratch(hipStream_t, void**) { return hipErrorNoDevice; }
 hipError_t launch_prefill_attention(const PrefillParams&, hipStream_t) { ++g_launches; return hipErrorNoDevice; }
-int prefill_rows_per_item() { return 64; }
+int prefill_rows_per_item() { return 128; }
 hipError_t launch_embed(const void*, int64_t, int64_t, const int64_t*, void*, int64_t, int64_t, int64_t,
                         hipStream_t) { ++g_launches; return hipErrorNoDevice; }
 hipError_t launch_silu_mul(const void*, int64_t, void*, int64_t, int64_t, int64_t, hipStream_t) {

@@ -186,7 +186,7 @@ def test_prefill_plan_rows_offsets_and_work_cover_every_visible_split(bi):
     assert np.array_equal(np.diff(q_offs.numpy()), nsplit)
     seen = {}
     for r0, nr, b, sp in work.tolist():
-        assert 1 <= nr <= 64 and np.all(seq[r0:r0 + nr] == b)                      # one sequence per item
+        assert 1 <= nr <= 128 and np.all(seq[r0:r0 + nr] == b)                      # one sequence per item
         assert np.array_equal(want_pos[r0:r0 + nr], np.arange(want_pos[r0], want_pos[r0] + nr))
         assert want_pos[r0 + nr - 1] >= 256 * sp                                   # its last row sees the split
         for r in range(r0, r0 + nr):
