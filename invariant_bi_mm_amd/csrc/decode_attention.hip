@@ -565,31 +565,44 @@ __global__ __launch_bounds__(256, 2) void prefill_split_kernel(PrefillArgs a) {
   const int64_t head_off = (int64_t)g * head_stride;
   const int64_t q_tok = (int64_t)a.hq * HD;
   const uint16_t* q0 = a.q + ((int64_t)row0 * a.hq + g * GQA) * HD;
-  // the item's row positions and split offsets, read once into LDS (each
-  // row block needs them three times)
-  __shared__ int spos[QB], soff[QB];
-  if (tid < nq) {
-    spos[tid] = a.pos[row0 + tid];
-    soff[tid] = a.qoffs[row0 + tid];
+  // Per item row, read once into LDS (each row block needs them three
+  // times): its position, and where its partials go -- the partial row of
+  // (chunk row row0 + t, split s, query head g GQA), or -1 when the row's
+  // position is before the split (it does not see it), its split slot is
+  // outside the workspace's total_splits, or t >= nq. BUFST keeps that row
+  // as the byte offsets of its o row and its (m, l) pair in the workspace
+  // resource, past the resource's end (dropped stores) for -1.
+  constexpr uint32_t DROP = 0x80000000u;  // past any resource of BUFST
+  __shared__ int spos[QB];
+  __shared__ uint32_t s_ooff[BUFST ? QB : 1], s_moff[BUFST ? QB : 1];
+  __shared__ int64_t s_row[BUFST ? 1 : QB];
+  if (tid < QB) {
+    int64_t row = -1;
+    if (tid < nq) {
+      const int p = a.pos[row0 + tid];
+      const int64_t slot = (int64_t)a.qoffs[row0 + tid] + s;
+      spos[tid] = p;
+      if (p + 1 - t0 > 0 && slot >= 0 && slot < a.total_splits) row = slot * a.hq + g * GQA;
+    }
+    if constexpr (BUFST) {
+      // in range: the workspace, partials included, is below 2^31 bytes
+      s_ooff[tid] = row >= 0 ? (uint32_t)(row * HD) * 4u : DROP;
+      s_moff[tid] = row >= 0 ? (uint32_t)(a.ml_off + row * 2) * 4u : DROP;
+    } else {
+      s_row[tid] = row;
+    }
   }
-  // partial row of (chunk row row0 + t, split s, query head g GQA), or -1
-  // when that row's position is before the split (it does not see it)
-  auto part_row = [&](int t) -> int64_t {
-    const int64_t slot = (int64_t)soff[t] + s;  // inside the workspace's total_splits slots, or not written
-    return spos[t] + 1 - t0 > 0 && slot >= 0 && slot < a.total_splits ? slot * a.hq + g * GQA : -1;
-  };
 
   u32x4 qc[4], kf[4][4], vf[8][2];
   load_q_block(q0, q_tok, min(4, nq), lane, qc);
   load_k_frags<false>(a.kp, bt, npg, page_stride, head_off, wave, lane, kf);
   load_v_frags<false>(a.vp, bt, npg, page_stride, head_off, wave, lane, vf);
   __builtin_amdgcn_sched_barrier(0);  // every load issued before the first MFMA waits
-  __syncthreads();                    // spos, soff
+  __syncthreads();                    // the per-row tables
   const int t_lane = lane >> 4;       // the token of this lane's softmax row, scores and p.v outputs
   const int j = lane & 15;            // the lane's place in its softmax row
   const int nblk = (nq + 3) / 4;      // blocks of 4 tokens
   auto nb_of = [&](int i) { return min(4, nq - 4 * i); };
-  auto row_base = [&](int i) -> int64_t { return t_lane < nb_of(i) ? part_row(4 * i + t_lane) : -1; };
   auto qload = [&](int i) { load_q_block(q0 + 4 * i * q_tok, q_tok, nb_of(i), lane, qc); };
   // BUFST (the workspace is below 2 GiB): the partials go out as raw buffer
   // stores through one resource over ws_o and ws_ml; a lane with nothing to
@@ -599,35 +612,38 @@ __global__ __launch_bounds__(256, 2) void prefill_split_kernel(PrefillArgs a) {
   // for the stores issued before it, and a branch around the stores made it
   // assume none had been issued, waiting for the previous step's stores.
   // Otherwise, plain stores under a branch.
-  constexpr uint32_t DROP = 0x80000000u;  // past any resource of BUFST
   const __amdgpu_buffer_rsrc_t ws_rsrc = __builtin_amdgcn_make_buffer_rsrc(a.ws_o, 0, (int)a.ws_bytes, 0x00020000);
   constexpr int NT = 2;  // cache policy: non-temporal (written once, read back by the combine)
+  // block i's row of this lane (4 i + t_lane < 4 nblk <= QB; rows >= nq
+  // have nothing to write)
   auto store_ml = [&](int i, float mx, float l) {
-    const int64_t base = row_base(i);
     if constexpr (BUFST) {
-      const uint32_t off = j == 0 && base >= 0 ? (uint32_t)(a.ml_off + (base + wave) * 2) * 4u : DROP;
+      const uint32_t off = j == 0 ? s_moff[4 * i + t_lane] + 8u * wave : DROP;  // DROP + 24 is still past the end
       __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(mx), __float_as_uint(l)}, ws_rsrc, (int)off, 0, 0);
-    } else if (j == 0 && base >= 0) {
-      a.ws_ml[(base + wave) * 2 + 0] = mx;
-      a.ws_ml[(base + wave) * 2 + 1] = l;
+    } else {
+      const int64_t base = s_row[4 * i + t_lane];
+      if (j == 0 && base >= 0) {
+        a.ws_ml[(base + wave) * 2 + 0] = mx;
+        a.ws_ml[(base + wave) * 2 + 1] = l;
+      }
     }
   };
   // store_o(-1, zeros) issues the same stores, all dropped (BUFST): the
   // first step does it, so that every step of the pipeline has the same
   // memory operations and the compiler's count at the loop's head is exact.
   auto store_o = [&](int i, const f32x4 (&acc)[2]) {
-    const int64_t base = i >= 0 ? row_base(i) : -1;
     if constexpr (BUFST) {
-      const uint32_t off =
-          base >= 0 ? (uint32_t)(base * HD + 32 * wave + (lane & 15)) * 4u : DROP;  // + (i HD + 16 dt) 4
+      // + (h HD + 16 dt) 4 below; DROP plus at most 2044 is still past the end
+      const uint32_t off = (i >= 0 ? s_ooff[4 * i + t_lane] : DROP) + (uint32_t)(32 * wave + (lane & 15)) * 4u;
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
         for (int h = 0; h < 4; ++h)
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[dt][h]), ws_rsrc,
                                                 (int)(off + (uint32_t)(h * HD + 16 * dt) * 4u), 0, NT);
-    } else if (base >= 0) {
-      store_pv<true>(acc, wave, lane, a.ws_o + base * HD);
+    } else {
+      const int64_t base = i >= 0 ? s_row[4 * i + t_lane] : -1;
+      if (base >= 0) store_pv<true>(acc, wave, lane, a.ws_o + base * HD);
     }
   };
   using Buf = float (*)[GQA][SROW];
