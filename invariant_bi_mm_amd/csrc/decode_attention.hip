@@ -565,25 +565,33 @@ __global__ __launch_bounds__(256, 2) void prefill_split_kernel(PrefillArgs a) {
   const int64_t head_off = (int64_t)g * head_stride;
   const int64_t q_tok = (int64_t)a.hq * HD;
   const uint16_t* q0 = a.q + ((int64_t)row0 * a.hq + g * GQA) * HD;
-  // Per item row, read once into LDS (each row block needs them three
-  // times): its position, and where its partials go -- the partial row of
+  // Per item row t, worked out once into LDS (each row block needs them
+  // three times, and a table read has no branch): the keys of the split it
+  // sees (0 for t >= nq), and where its partials go -- the partial row of
   // (chunk row row0 + t, split s, query head g GQA), or -1 when the row's
   // position is before the split (it does not see it), its split slot is
   // outside the workspace's total_splits, or t >= nq. BUFST keeps that row
   // as the byte offsets of its o row and its (m, l) pair in the workspace
-  // resource, past the resource's end (dropped stores) for -1.
+  // resource, past the resource's end (dropped stores) for -1. Whether any
+  // row sees less than the whole split (the item is masked) is gathered by
+  // a ballot of the two waves that fill the tables.
+  static_assert(QB % 64 == 0, "the tables are filled by whole waves");
   constexpr uint32_t DROP = 0x80000000u;  // past any resource of BUFST
-  __shared__ int spos[QB];
+  __shared__ int s_nt[QB], s_short[QB / 64];
   __shared__ uint32_t s_ooff[BUFST ? QB : 1], s_moff[BUFST ? QB : 1];
   __shared__ int64_t s_row[BUFST ? 1 : QB];
-  if (tid < QB) {
+  if (tid < QB) {  // whole waves
     int64_t row = -1;
+    int nt = 0;
     if (tid < nq) {
-      const int p = a.pos[row0 + tid];
+      const int64_t seen = (int64_t)a.pos[row0 + tid] + 1 - t0;
       const int64_t slot = (int64_t)a.qoffs[row0 + tid] + s;
-      spos[tid] = p;
-      if (p + 1 - t0 > 0 && slot >= 0 && slot < a.total_splits) row = slot * a.hq + g * GQA;
+      nt = (int)max((int64_t)0, min((int64_t)SPLIT, seen));
+      if (seen > 0 && slot >= 0 && slot < a.total_splits) row = slot * a.hq + g * GQA;
     }
+    s_nt[tid] = nt;
+    const uint64_t short_rows = __ballot(tid < nq && nt < SPLIT);
+    if (lane == 0) s_short[wave] = short_rows != 0;
     if constexpr (BUFST) {
       // in range: the workspace, partials included, is below 2^31 bytes
       s_ooff[tid] = row >= 0 ? (uint32_t)(row * HD) * 4u : DROP;
@@ -647,9 +655,9 @@ __global__ __launch_bounds__(256, 2) void prefill_split_kernel(PrefillArgs a) {
     }
   };
   using Buf = float (*)[GQA][SROW];
-  int nt_min = SPLIT;  // keys seen by the item's first row (the fewest)
-  for (int t = 0; t < nq; ++t) nt_min = min(nt_min, spos[t] + 1 - t0);
-  nt_min = __builtin_amdgcn_readfirstlane(nt_min);
+  bool masked = false;  // uniform: some row sees less than the whole split
+#pragma unroll
+  for (int w = 0; w < QB / 64; ++w) masked = masked || s_short[w] != 0;
 
   // The item's blocks of 4 tokens run as a pipeline with one barrier per
   // block. Step i takes block i's softmax, block i - 1's p.v and block i + 1's
@@ -665,10 +673,9 @@ __global__ __launch_bounds__(256, 2) void prefill_split_kernel(PrefillArgs a) {
   // past its position get -inf scores (p = 0 exactly) and V past the last
   // row's keys is zeroed once, so every product with an unseen key is an
   // exact zero.
-  const bool masked = nt_min < SPLIT;  // uniform
   {
     // keys this lane's token of block i sees
-    auto nt_tok = [&](int i) { return t_lane < nb_of(i) ? min(SPLIT, spos[4 * i + t_lane] + 1 - t0) : 0; };
+    auto nt_tok = [&](int i) { return s_nt[4 * i + t_lane]; };  // 0 past the item's rows
     f32x4 sacc[4], pacc[2];
     u32x4 phi[2], plo[2];
     auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
