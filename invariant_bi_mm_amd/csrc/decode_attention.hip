@@ -778,6 +778,32 @@ __global__ __launch_bounds__(256, 2) void prefill_split_kernel(PrefillArgs a) {
   }
 }
 
+// Four consecutive output elements out[at .. at + 3] (at a multiple of 4):
+// one 16-byte (fp32) or 8-byte (bf16) store where out's alignment allows it
+// (the same for every lane), else four element stores (out need only be
+// aligned to its element size).
+__device__ __forceinline__ void store_out4(void* out, int64_t at, const float (&r)[4], int out_bf16) {
+  if (out_bf16) {
+    uint16_t* const p = reinterpret_cast<uint16_t*>(out) + at;
+    if ((reinterpret_cast<uintptr_t>(p) & 7) == 0) {
+      *reinterpret_cast<u32x2*>(p) =
+          u32x2{(uint32_t)f32_to_bf16_rne(r[0]) | ((uint32_t)f32_to_bf16_rne(r[1]) << 16),
+                (uint32_t)f32_to_bf16_rne(r[2]) | ((uint32_t)f32_to_bf16_rne(r[3]) << 16)};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = (uint16_t)f32_to_bf16_rne(r[e]);
+    }
+  } else {
+    float* const p = reinterpret_cast<float*>(out) + at;
+    if ((reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+      *reinterpret_cast<f32x4*>(p) = f32x4{r[0], r[1], r[2], r[3]};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = r[e];
+    }
+  }
+}
+
 // Combine: one workgroup of two waves per (sequence, query head). The split
 // partials are folded in 8 groups: group g takes the splits s = g, g + 8,
 // g + 16, ... in increasing order (m, l, o weighted by 2^(m_s - M), M the
@@ -879,15 +905,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const int32_t* __re
     const float4 os = add(add(ot[0], po[0][c]), add(ot[1], po[1][c]));
     const float ls = (lt[0] + pl[0]) + (lt[1] + pl[1]);
     const float res[4] = {os.x / ls, os.y / ls, os.z / ls, os.w / ls};
-    const int64_t at = ((int64_t)b * hq + h) * HD + 4 * c;
-    // element stores: out need only be aligned to its element size
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (out_bf16)
-        reinterpret_cast<uint16_t*>(out)[at + e] = (uint16_t)f32_to_bf16_rne(res[e]);
-      else
-        reinterpret_cast<float*>(out)[at + e] = res[e];
-    }
+    store_out4(out, ((int64_t)b * hq + h) * HD + 4 * c, res, out_bf16);
   }
 }
 
@@ -963,14 +981,7 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(const int32_t* __r
   const float ls = lt + xor_shfl(lt, 32);
   if (hf == 0) {
     const float res[4] = {os.x / ls, os.y / ls, os.z / ls, os.w / ls};
-    const int64_t at = ((int64_t)b * hq + h) * HD + 4 * c;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (out_bf16)
-        reinterpret_cast<uint16_t*>(out)[at + e] = (uint16_t)f32_to_bf16_rne(res[e]);
-      else
-        reinterpret_cast<float*>(out)[at + e] = res[e];
-    }
+    store_out4(out, ((int64_t)b * hq + h) * HD + 4 * c, res, out_bf16);
   }
 }
 

@@ -406,6 +406,24 @@ def test_decode_attention_benchmark_batch_sampled(lib):
     assert same_bits(out_nt, out)
 
 
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_decode_attention_unaligned_out_same_bits(lib, dt):
+    """out need only be aligned to its element size: an output that starts
+    one element past a 16-byte boundary (written element by element) gets
+    the bits of an aligned one (written as whole 4-element vectors)."""
+    lens_t, table, q, kp, vp = make_decode([1, 300, 700], seed=130)
+    say("decode unaligned out", dt)
+    aligned = run_decode(lib, lens_t, table, q, kp, vp, dt)
+    offs, total = lib.bi_decode_plan(lens_t)
+    buf = torch.full((1 + 3 * 32 * 128,), 7.0, dtype=dt, device=DEV)
+    out = buf[1:].view(3, 32, 128)
+    assert out.data_ptr() % 16 != 0
+    lib.bi_decode_attention(q.to(DEV), kp.to(DEV), vp.to(DEV), table.to(DEV), lens_t.to(DEV), offs.to(DEV), total,
+                            out=out)
+    assert same_bits(out, aligned)
+    assert buf[0].item() == 7.0
+
+
 def test_decode_attention_inconsistent_device_offsets_stay_in_bounds(lib):
     """Device-side lengths and offsets are the caller's: the host cannot read
     them. Offsets that give one sequence a split its length does not reach

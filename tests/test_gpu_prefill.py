@@ -98,6 +98,24 @@ def test_prefill_independent_of_chunking_and_batch(lib):
     assert same_bits(ob[64:64 + 333], parts[1])
 
 
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_prefill_unaligned_out_same_bits(lib, dt):
+    """An output one element past a 16-byte boundary (element stores) gets
+    the bits of an aligned one (vector stores)."""
+    chunk, ctx = [40, 9], [230, 500]
+    table, kp, vp = cache_for([c + n for c, n in zip(ctx, chunk)], seed=6200)
+    q = S.normal_bf16((sum(chunk), HQ, D), 1.0, seed=6210, device=DEV)
+    aligned, _ = prefill(lib, q, kp, vp, table, chunk, ctx, dt)
+    q_pos, q_offs, work, sizes = lib.bi_prefill_plan(torch.tensor(chunk), torch.tensor(ctx))
+    buf = torch.full((1 + sum(chunk) * HQ * D,), 7.0, dtype=dt, device=DEV)
+    out = buf[1:].view(sum(chunk), HQ, D)
+    assert out.data_ptr() % 16 != 0
+    lib.bi_prefill_attention(q, kp, vp, table.to(DEV), q_pos.to(DEV), q_offs.to(DEV), work.to(DEV), sizes, out=out)
+    say("prefill unaligned out", dt)
+    assert same_bits(out, aligned)
+    assert buf[0].item() == 7.0
+
+
 def test_prefill_inconsistent_plan_stays_in_bounds(lib):
     """The plan's arrays live on the device, where the host cannot check them: work items whose row
     range, sequence, split or pages do not fit the buffers, and split offsets past the workspace, are
