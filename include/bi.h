@@ -110,7 +110,8 @@ bi_status bi_addmm(const void* bias, bi_dtype bias_dtype, float beta, float alph
 /* Tile configuration the GEMM uses for (m, n, k, b_is_nk): writes
  * {tile_m, tile_n, tile_k, waves_per_workgroup} to out4. One of
  * {32, 32, 64, 3} and {64, 32, 64, 4} (m <= 64: 32-column strips, a deep
- * load ring), {64, 128, 64, 6} and {128, 128, 64, 10} (the same ring with a
+ * load ring), {32, 96, 64, 5} and {64, 96, 64, 8} (m <= 64, 96-column strips
+ * where those fill the CUs in one round), {64, 128, 64, 6} and {128, 128, 64, 10} (the same ring with a
  * 64x128 or 128x128 tile), {128, 128, 64, 4}, {256, 256, 64, 8}. With {256, 256, 64, 8}, when the
  * last round of tiles over the 256 CUs would be part-empty, the columns
  * past the last full round run as 256x128 tiles in a second launch. The

@@ -400,7 +400,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
 // consumer waves, each owning a (32 FM) x (32 FN) block of the tile, and P
 // producer waves that move its k tiles through an NS-stage LDS ring, up to
 // NS - 2 tiles ahead of the MFMAs. The skinny form (one 32x32 block per
-// consumer, 32 columns per workgroup) gives N / 32 workgroups for M <= 64;
+// consumer, 32 columns per workgroup) gives N / 32 workgroups for M <= 64,
+// its 96-column form (three consumers across) N / 96 where those fill the
+// CUs in one round, so a CU reads the rows of A once for 96 columns;
 // the 128x128 form (2x2 consumers of 64x64) serves medium M. The
 // per-element chain is the one of gemm_kernel: one v_mfma_f32_32x32x16_bf16
 // per 16 k, increasing k, fp32 accumulator starting at 0, the same operand
@@ -455,10 +457,10 @@ __global__ __launch_bounds__((CM * CN + P) * 64) void gemm_ring_kernel(GemmArgs 
   constexpr int TM = CM * WTM, TN = CN * WTN;
   // One stage: A as TM rows of 64 k (eight 16-byte chunks, swizzled by swz),
   // then B: [N,K] as TN rows of 64 k (swizzled likewise), or [K,N] as 64 k
-  // rows of TN columns (TN / 8 chunks; for TN >= 128 chunk c of row r stored
-  // at c ^ 4 (r % 4) as in gemm_kernel, for TN = 32 as they are).
-  static_assert(B_NK || TN == 32 || TN % 128 == 0, "[K,N] stage layout needs TN = 32 or a multiple of 128");
-  constexpr bool BSW = !B_NK && TN >= 128;
+  // rows of TN columns (TN / 8 chunks; for TN a multiple of 128 chunk c of
+  // row r stored at c ^ 4 (r % 4) as in gemm_kernel, otherwise as they are).
+  static_assert(B_NK || TN % 32 == 0, "[K,N] stage layout needs TN a multiple of 32");
+  constexpr bool BSW = !B_NK && TN % 128 == 0;
   constexpr int CPR = TN / 8;  // [K,N]: chunks per k row
   constexpr int A_CH = TM * 8, B_CH = TN * 8;
   constexpr int ST = A_CH + B_CH;                          // chunks per stage
@@ -752,6 +754,13 @@ static hipError_t launch_part(const GemmParams& p, const GemmLaunch& L, hipStrea
       return p.b_is_nk ? launch_ring<1, 1, 1, 1, 2, 16, true>(a, s) : launch_ring<1, 1, 1, 1, 2, 16, false>(a, s);
     if (cfg.tile_m == 64)
       return p.b_is_nk ? launch_ring<2, 1, 1, 1, 2, 12, true>(a, s) : launch_ring<2, 1, 1, 1, 2, 12, false>(a, s);
+    return hipErrorInvalidConfiguration;
+  }
+  if (cfg.tile_n == 96) {  // 1x3 or 2x3 consumers of 32x32, 8-stage ring
+    if (cfg.tile_m == 32)
+      return p.b_is_nk ? launch_ring<1, 3, 1, 1, 2, 8, true>(a, s) : launch_ring<1, 3, 1, 1, 2, 8, false>(a, s);
+    if (cfg.tile_m == 64)
+      return p.b_is_nk ? launch_ring<2, 3, 1, 1, 2, 8, true>(a, s) : launch_ring<2, 3, 1, 1, 2, 8, false>(a, s);
     return hipErrorInvalidConfiguration;
   }
   if (cfg.tile_m == 128 && cfg.tile_n == 128 && cfg.waves == 10)  // 4x2 consumers of 32x64, 4-stage ring

@@ -35,7 +35,8 @@ static GemmConfig skinny_config(int64_t m, int64_t strips) {
 //   * skinny (32 or 64 rows x 32 columns, deep ring) for M <= 64: 2.5-3.6x
 //     faster than 128x128 (N = 4096, 6144, K = 4096 and 12288), 1.25-1.6x
 //     at N = 24576; at the 151936-wide LM head both stream at ~5.4 TB/s and
-//     128x128 is kept;
+//     128x128 is kept; 32 or 64 rows x 96 columns (three consumers across)
+//     where that makes one round of tiles out of several (N = 24576);
 //   * the same deep ring with a 64x128 tile (2x2 consumer waves of 32x64,
 //     two producers, 6 stages) for M > 64 while 128x128 tiles would fill at
 //     most half the CUs and the 64x128 ones still fit one round: 6-14 %
@@ -57,7 +58,17 @@ static GemmConfig skinny_config(int64_t m, int64_t strips) {
 GemmConfig gemm_config(int64_t m, int64_t n, int64_t k, bool b_is_nk) {
   (void)b_is_nk;
   const int64_t strips = (n + 31) / 32;
-  if (m <= 64 && n <= 32768) return skinny_config(m, strips);
+  if (m <= 64 && n <= 32768) {
+    // 96-column skinny tiles when 32-column strips need more than one round
+    // over the CUs and the 96-column ones fill one round at least 3/4 full:
+    // a CU then reads the rows' A once for 96 columns instead of once per
+    // 32 (gate+up, N = 24576: M = 64 cold 59.8 -> 49.3 us with [N,K]
+    // weights, 81.5 -> 45.0 with [K,N]; M = 1 43.4 -> 45.2 and 60.0 -> 41.6)
+    const int64_t strips96 = (n + 95) / 96;
+    if (strips > 256 && strips96 >= 192 && strips96 <= 256)
+      return m <= 32 ? GemmConfig{32, 96, TK, 5} : GemmConfig{64, 96, TK, 8};
+    return skinny_config(m, strips);
+  }
   const int64_t t128 = ((m + 127) / 128) * ((n + 127) / 128);
   if (m > 64 && t128 <= 128 && ((m + 63) / 64) * ((n + 127) / 128) <= 256) return GemmConfig{64, 128, TK, 6};
   if (m > 64 && t128 <= 256) return GemmConfig{128, 128, TK, 10};

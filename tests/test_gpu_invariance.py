@@ -116,11 +116,12 @@ def test_mm_adversarial_other_rows(lib, fill):
             assert same_bits(lib.bi_mm(x, w)[pos], ref), (fill, m, pos)
 
 
-ALL_CONFIGS = {(32, 32, 64, 3), (64, 32, 64, 4), (64, 128, 64, 6), (128, 128, 64, 10), (128, 128, 64, 4), (256, 256, 64, 8)}
+ALL_CONFIGS = {(32, 32, 64, 3), (64, 32, 64, 4), (32, 96, 64, 5), (64, 96, 64, 8), (64, 128, 64, 6), (128, 128, 64, 10),
+               (128, 128, 64, 4), (256, 256, 64, 8)}
 
 
 @pytest.mark.parametrize("b_is_nk", [False, True])
-@pytest.mark.parametrize("n", [4096, 6144])
+@pytest.mark.parametrize("n", [4096, 6144, 24576])
 def test_mm_every_tile_configuration_same_bits(lib, b_is_nk, n):
     """A row's addmm output is the same, bit for bit, at an M of each tile
     configuration the shape takes (skinny 32 or 64 rows, the 64x128 and
@@ -152,7 +153,8 @@ def test_mm_every_tile_configuration_same_bits(lib, b_is_nk, n):
 
 def test_every_tile_configuration_is_exercised(lib):
     """The shapes of the test above take every configuration of the table between them."""
-    seen = {lib.bi_gemm_config(m, n, 1032, nk) for n in (4096, 6144) for nk in (False, True) for m in range(1, 4097)}
+    seen = {lib.bi_gemm_config(m, n, 1032, nk) for n in (4096, 6144, 24576) for nk in (False, True)
+            for m in range(1, 4097)}
     assert seen == ALL_CONFIGS, seen
 
 
