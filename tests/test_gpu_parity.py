@@ -58,6 +58,27 @@ def test_mm_ragged_tiles(lib, m, n, k, b_is_nk):
     assert_close(f32(c), O.mm(bits(a), bits(b), b_is_nk=b_is_nk), "mm ragged")
 
 
+@pytest.mark.parametrize("b_is_nk", [False, True])
+def test_mm_wide_skinny_tiles_ragged(lib, b_is_nk):
+    """The 96-column skinny tiles on a width that is not a multiple of 96 (or
+    32) and a ragged K: against the oracle, and bit for bit against the
+    fixed-tile mode (256x256 tiles) for the same rows."""
+    n, k = 20008, 1032
+    w = S.normal_bf16((n, k) if b_is_nk else (k, n), 1.0 / k, seed=81, device=DEV)
+    for m in (1, 33, 64):
+        cfg = lib.bi_gemm_config(m, n, k, b_is_nk)
+        say(f"wide skinny m={m} n={n} k={k} nk={b_is_nk} cfg={cfg}")
+        assert cfg[1] == 96, cfg
+        a = S.normal_bf16((m, k), 1.0, seed=82 + m, device=DEV)
+        c = lib.bi_mm(a, w, b_is_nk=b_is_nk)
+        cols = np.r_[0:40, n // 2 - 20:n // 2 + 20, n - 72:n]
+        wb = bits(w)
+        ref = O.mm(bits(a), wb[cols] if b_is_nk else wb[:, cols], b_is_nk=b_is_nk)
+        assert_close(f32(c)[:, cols], ref, "wide skinny vs oracle")
+        fixed = lib.bi_gemm(a, w, b_is_nk=b_is_nk, fixed_tile=True)
+        assert same_bits(c, fixed)
+
+
 def test_mm_layouts_agree_bitwise(lib):
     """B stored [K,N] and the same B stored [N,K] give identical bits: the
     layout changes only how B reaches LDS, not the arithmetic."""
