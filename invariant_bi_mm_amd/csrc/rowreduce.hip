@@ -643,8 +643,10 @@ hipError_t launch_mean(const void* x, bool x_bf16, int64_t ldx, float* y, int64_
 }
 
 // Rows up to which each row's 16 wave partials get workgroups of their own
-// (the three-launch form above); the same bits either way.
-constexpr int64_t LS_SMALL_M = 32;
+// (the three-launch form above); the same bits either way. Measured at
+// n = 151936: M = 33 27.3 -> 20.3 us, M = 48 27.7 -> 24.2 us, even at
+// M = 64 (28.3 / 28.8 us), slower beyond (M = 96 31.3 / 42.6 us).
+constexpr int64_t LS_SMALL_M = 48;
 
 hipError_t launch_log_softmax(const float* x, int64_t ldx, float* y, int64_t ldy, int64_t* argmax,
                               int64_t m, int64_t n, hipStream_t s) {
