@@ -86,7 +86,7 @@ typedef enum { BI_BF16 = 0, BI_F32 = 1 } bi_dtype;
  * runs that same chain with the same operands, so a row of C has the same
  * bits whatever m is and wherever the row sits.
  * Requirements: k % 8 == 0; with b_is_nk == 0 also n % 8 == 0;
- * 256 * lda * 2 and (b_is_nk ? 256 : 64) * ldb * 2 below 2^31 bytes (the
+ * 256 * lda * 2 and (b_is_nk ? 384 : 64) * ldb * 2 below 2^31 bytes (the
  * largest tile's byte range; BI_ERR_UNSUPPORTED otherwise).
  * k == 0 with m, n > 0: C = beta * bias (addmm) or zeros (mm).
  * ------------------------------------------------------------------------ */
@@ -112,7 +112,9 @@ bi_status bi_addmm(const void* bias, bi_dtype bias_dtype, float beta, float alph
  * {32, 32, 64, 3} and {64, 32, 64, 4} (m <= 64: 32-column strips, a deep
  * load ring), {32, 96, 64, 5} and {64, 96, 64, 8} (m <= 64, 96-column strips
  * where those fill the CUs in one round), {64, 128, 64, 6} and {128, 128, 64, 10} (the same ring with a
- * 64x128 or 128x128 tile), {128, 128, 64, 4}, {256, 256, 64, 8}. With {256, 256, 64, 8}, when the
+ * 64x128 or 128x128 tile), {128, 128, 64, 4}, {256, 256, 64, 8},
+ * {256, 384, 64, 8} (only where k % 64 == 0, n % 384 == 0 and its tiles
+ * make whole rounds over the 256 CUs). With {256, 256, 64, 8}, when the
  * last round of tiles over the 256 CUs would be part-empty, the columns
  * past the last full round run as 256x128 tiles in a second launch. The
  * choice changes which workgroup computes an element, never how (see

@@ -67,11 +67,11 @@ bi_status check_gemm(const void* a, int64_t lda, const void* b, int64_t ldb, int
   }
   // the kernels address one tile's rows of A and B through 32-bit buffer
   // descriptors: a tile's byte extent must stay below 2^31. Checked for the
-  // largest tile of any configuration (256 rows of A; 256 rows of B stored
+  // largest tile of any configuration (256 rows of A; 384 rows of B stored
   // [n, k], 64 k-rows stored [k, n]), so whether a call is accepted does not
   // depend on m.
   const int64_t lim = int64_t(1) << 31;
-  if (2 * 256 * lda >= lim || 2 * (b_is_nk ? 256 : 64) * ldb >= lim)
+  if (2 * 256 * lda >= lim || 2 * (b_is_nk ? 384 : 64) * ldb >= lim)
     return fail(BI_ERR_UNSUPPORTED, "leading dimension too large for one tile's 32-bit byte range");
   return BI_OK;
 }

@@ -20,10 +20,10 @@
 //   stream-K or atomic anywhere.
 //
 // Which tile configuration runs is chosen from (M, N, K) -- a skinny kernel
-// for small M (below), 128x128 or 256x256 otherwise, the last with its
-// leftover columns on 256x128 tiles when its final round over the CUs would
-// be part-empty -- and, because every configuration runs the chain above,
-// that choice never changes a bit.
+// for small M (below), 128x128, 256x256 or 256x384 otherwise, 256x256 with
+// its leftover columns on 256x128 tiles when its final round over the CUs
+// would be part-empty -- and, because every configuration runs the chain
+// above, that choice never changes a bit.
 //
 // Structure (one workgroup per TM x TN output tile)
 //   * global -> LDS directly (buffer_load ... lds, 16 bytes per lane): no
@@ -135,6 +135,11 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
   static_assert(A_I * 64 * NW == TM * 8 && B_I * 64 * NW == TN * 8, "tile not evenly split across waves");
   static_assert(FM >= 1 && FN >= 1, "wave tile smaller than one MFMA");
   static_assert(B_NK || TN % 128 == 0, "[K,N] swizzle needs at least 16 chunks per row");
+  // FULL (the 256x384 tile): K is a multiple of TK and N of TN, so no load
+  // needs a k or n mask; its fragment addresses are recomputed per read and
+  // rows past M are multiplied as zeros rather than skipped, which keeps its
+  // 192 accumulators and the rest within 256 registers
+  constexpr bool FULL = TN == 384;
 
   // two stages, each its own LDS object
   __shared__ u32x4 As0[TM * 8], As1[TM * 8];
@@ -190,11 +195,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
     const int k0 = t * TK;
 #pragma unroll
     for (int i = 0; i < A_I; ++i)
-      lds_load16(a_rsrc, &as[(i * NW + wave) * 64], (k0 + a_k[i] < K) ? a_off[i] + (uint32_t)k0 * 2u : OOB);
+      lds_load16(a_rsrc, &as[(i * NW + wave) * 64],
+                 (FULL || k0 + a_k[i] < K) ? a_off[i] + (uint32_t)k0 * 2u : OOB);
     if constexpr (B_NK) {
 #pragma unroll
       for (int i = 0; i < B_I; ++i)
-        lds_load16(bnk_rsrc, &bs[(i * NW + wave) * 64], (k0 + b_k[i] < K) ? b_off[i] + (uint32_t)k0 * 2u : OOB);
+        lds_load16(bnk_rsrc, &bs[(i * NW + wave) * 64],
+                   (FULL || k0 + b_k[i] < K) ? b_off[i] + (uint32_t)k0 * 2u : OOB);
     } else {
       // rows of this k tile only: rows past K lie past the descriptor. The
       // base and size are workgroup-uniform; readfirstlane lets the compiler
@@ -208,7 +215,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
           make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), nbytes);
 #pragma unroll
       for (int i = 0; i < B_I; ++i)
-        lds_load16(r, &bs[(i * NW + wave) * 64], (n0 + b_k[i] < N) ? b_off[i] : OOB);
+        lds_load16(r, &bs[(i * NW + wave) * 64], (FULL || n0 + b_k[i] < N) ? b_off[i] : OOB);
     }
   };
 
@@ -241,11 +248,16 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
   // LDS reads of step kk+1 are in flight while the MFMAs of step kk run.
   auto frags = [&](auto FMV, int kk, const u32x4* as, const u32x4* bs, bf16x8* af, bf16x8* bfr) {
     constexpr int fmv = decltype(FMV)::value;
+    // FULL: the swizzled addresses are worked out at each read instead of
+    // being kept in registers over the loop (an opaque copy of the row index
+    // keeps the compiler from hoisting them)
+    int ar0 = arow0, br0 = brow0;
+    if constexpr (FULL) asm volatile("" : "+v"(ar0), "+v"(br0));
 #pragma unroll
-    for (int i = 0; i < fmv; ++i) af[i] = __builtin_bit_cast(bf16x8, as[swz(arow0 + i * 32, kk * 2 + khalf)]);
+    for (int i = 0; i < fmv; ++i) af[i] = __builtin_bit_cast(bf16x8, as[swz(ar0 + i * 32, kk * 2 + khalf)]);
     if constexpr (B_NK) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = __builtin_bit_cast(bf16x8, bs[swz(brow0 + j * 32, kk * 2 + khalf)]);
+      for (int j = 0; j < FN; ++j) bfr[j] = __builtin_bit_cast(bf16x8, bs[swz(br0 + j * 32, kk * 2 + khalf)]);
     } else {
       typedef short s16x4 __attribute__((ext_vector_type(4)));
       typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -314,7 +326,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_kernel(GemmArgs g) {
   };
   const int wave_rows = M - m0 - wm * WTM;  // wave-uniform
   const int fmv = wave_rows <= 0 ? 0 : min(FM, (wave_rows + 31) / 32);
-  if (fmv == FM) {
+  if constexpr (FULL) {
+    kloop(std::integral_constant<int, FM>{});
+  } else if (fmv == FM) {
     kloop(std::integral_constant<int, FM>{});
   } else {
     static_for<0, FM>([&](auto I) {
@@ -774,6 +788,12 @@ static hipError_t launch_part(const GemmParams& p, const GemmLaunch& L, hipStrea
   BI_GEMM_CASE(256, 256, 2, 4)
   BI_GEMM_CASE(256, 128, 4, 2)
 #undef BI_GEMM_CASE
+  // 256x384 assumes whole k tiles and tile columns (no masks); the table
+  // picks it only then
+  if (cfg.tile_m == 256 && cfg.tile_n == 384 && cfg.waves == 8) {
+    if (p.k % 64 != 0 || a.n % 384 != 0) return hipErrorInvalidConfiguration;
+    return p.b_is_nk ? launch_cfg<256, 384, 2, 4, true>(a, s) : launch_cfg<256, 384, 2, 4, false>(a, s);
+  }
   return hipErrorInvalidConfiguration;
 }
 

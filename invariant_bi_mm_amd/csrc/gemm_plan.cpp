@@ -25,7 +25,7 @@ static GemmConfig skinny_config(int64_t m, int64_t strips) {
 }
 
 // The configuration table. Every configuration -- skinny, 64x128, 128x128,
-// 256x256 -- computes each output element with the same chain (one 32x32x16 MFMA per
+// 256x256, 256x384 -- computes each output element with the same chain (one 32x32x16 MFMA per
 // 16 k, increasing k, fp32, k padded to a multiple of 64, the same
 // epilogue), so the choice moves work between workgroups without changing
 // any bit, and it may depend on M: the result of a row still does not depend
@@ -50,6 +50,8 @@ static GemmConfig skinny_config(int64_t m, int64_t strips) {
 //     M = 128, N = 24576; eight consumers instead of four of 64x64: 3-7 %
 //     faster at M = 384-1024 for N = 4096 and 6144 and at M <= 128 for
 //     N = 24576 (K = 12288 at M = 768-1024: ~5 % slower);
+//   * 256x384 (8 waves, 128x96 each) where K and N are whole tiles and its
+//     tiles make whole rounds over the CUs (gate+up and q+kv at M = 4096);
 //   * 256x256 (8 waves, 128x64 each) once its tiles fill the chip (M >= 192,
 //     at least 192 tiles, rounds of 256 at least 70 % full on average):
 //     1.25-1.3x faster than 128x128 at M = 4096 (N = 4096, LM head), 1.1x
@@ -72,6 +74,19 @@ GemmConfig gemm_config(int64_t m, int64_t n, int64_t k, bool b_is_nk) {
   const int64_t t128 = ((m + 127) / 128) * ((n + 127) / 128);
   if (m > 64 && t128 <= 128 && ((m + 63) / 64) * ((n + 127) / 128) <= 256) return GemmConfig{64, 128, TK, 6};
   if (m > 64 && t128 <= 256) return GemmConfig{128, 128, TK, 10};
+  // 256x384 (8 waves of 128x96) where K is a whole number of k tiles, N of
+  // tile columns, and its tiles make whole rounds over the CUs: per flop it
+  // reads a fifth fewer LDS bytes than 256x256 and fills LDS with a sixth
+  // fewer. Measured against 256x256 (with its column split where taken),
+  // warm, [K,N] / [N,K] weights: gate+up (N = 24576) at M = 1024 208 -> 180 /
+  // 211 -> 186 us, M = 2048 363 -> 354 / 363 -> 358, M = 3072 556 -> 520 /
+  // 566 -> 532, M = 4096 691 -> 671 / 702 -> 687; q+kv (N = 6144) at
+  // M = 4096, one round of 256 tiles where 256x256 needs 1.5, 184 -> 167 /
+  // 184 -> 169 us.
+  if (n % 384 == 0 && k % TK == 0) {
+    const int64_t t384 = ((m + 255) / 256) * (n / 384);
+    if (t384 >= 256 && t384 % 256 == 0) return GemmConfig{256, 384, TK, 8};
+  }
   const int64_t t256 = ((m + 255) / 256) * ((n + 255) / 256);
   const int64_t rounds = (t256 + 255) / 256;  // one 256x256 workgroup per CU
   if (m >= 192 && t256 >= 192 && 10 * t256 >= 7 * rounds * 256) return GemmConfig{256, 256, TK, 8};

@@ -255,13 +255,17 @@ def test_gemm_config_table(bi):
                 cfg = bi.bi_gemm_config(m, n, k, nk)
                 assert cfg == bi.bi_gemm_config(m, n, k, nk)
                 assert cfg in {(32, 32, 64, 3), (64, 32, 64, 4), (32, 96, 64, 5), (64, 96, 64, 8), (64, 128, 64, 6),
-                               (128, 128, 64, 10), (128, 128, 64, 4), (256, 256, 64, 8)}, cfg
+                               (128, 128, 64, 10), (128, 128, 64, 4), (256, 256, 64, 8), (256, 384, 64, 8)}, cfg
                 seen.add(cfg)
-    assert len(seen) == 8
+    assert len(seen) == 9
     # small batches of the projection shapes take the skinny tiles, M = 4096 a full-width one
     assert bi.bi_gemm_config(1, 4096, 4096)[1] == 32 and bi.bi_gemm_config(64, 4096, 12288)[1] == 32
     assert bi.bi_gemm_config(1, 24576, 4096) == (32, 96, 64, 5) and bi.bi_gemm_config(64, 24576, 4096) == (64, 96, 64, 8)
     assert bi.bi_gemm_config(4096, 4096, 4096)[1] == 256 and bi.bi_gemm_config(1, 151936, 4096)[1] == 128
+    # 256x384 only where K and N are whole tiles and its tiles make whole rounds of 256
+    assert bi.bi_gemm_config(4096, 24576, 4096)[1] == 384 and bi.bi_gemm_config(4096, 6144, 4096)[1] == 384
+    assert bi.bi_gemm_config(1024, 24576, 4096)[1] == 384 and bi.bi_gemm_config(1280, 24576, 4096)[1] == 256
+    assert bi.bi_gemm_config(4096, 6144, 4104)[1] != 384 and bi.bi_gemm_config(3840, 6144, 4096)[1] != 384
     with pytest.raises(bi.BiError):
         bi.bi_gemm_config(-1, 4, 4, False)
     assert bi.lib.bi_gemm_config(1, 4, 4, 0, None) == NULL
@@ -344,14 +348,17 @@ def test_gemm_plan_and_fixed_tile_mode(bi):
 
 def test_qwen_shapes_walk_every_gemm_configuration(bi):
     """Over M = 1..4096 the four Qwen3-8B projection shapes (either layout)
-    take every configuration of the tile table between them, and the 256x128
-    column split: so the every-M GPU sweep on those shapes runs them all."""
+    take every configuration of the tile table between them, and the LM head
+    over M = 1..256 the 256x128 column split: so the every-M GPU sweeps on
+    those shapes run them all."""
     table = {(32, 32, 64, 3), (64, 32, 64, 4), (32, 96, 64, 5), (64, 96, 64, 8), (64, 128, 64, 6), (128, 128, 64, 10),
-             (128, 128, 64, 4), (256, 256, 64, 8)}
+             (128, 128, 64, 4), (256, 256, 64, 8), (256, 384, 64, 8)}
     seen, split = set(), False
     for k, n in ((4096, 6144), (4096, 4096), (4096, 24576), (12288, 4096)):
         for m in range(1, 4097):
             plan = bi.bi_gemm_plan(m, n, k)
             seen |= {p[:4] for p in plan[:1]}
-            split |= len(plan) == 2 and plan[1][:4] == (256, 128, 64, 8)
+    for m in range(1, 257):
+        plan = bi.bi_gemm_plan(m, 151936, 4096)
+        split |= len(plan) == 2 and plan[1][:4] == (256, 128, 64, 8)
     assert seen == table and split, (seen, split)

@@ -117,17 +117,20 @@ def test_mm_adversarial_other_rows(lib, fill):
 
 
 ALL_CONFIGS = {(32, 32, 64, 3), (64, 32, 64, 4), (32, 96, 64, 5), (64, 96, 64, 8), (64, 128, 64, 6), (128, 128, 64, 10),
-               (128, 128, 64, 4), (256, 256, 64, 8)}
+               (128, 128, 64, 4), (256, 256, 64, 8), (256, 384, 64, 8)}
+# (n, k): a ragged K (a 64-tail) on three widths, and whole k tiles where the
+# 256x384 tile (K a multiple of 64, N of 384) can be chosen
+CONFIG_SHAPES = [(4096, 1032), (6144, 1032), (24576, 1032), (6144, 1024), (24576, 1024)]
 
 
 @pytest.mark.parametrize("b_is_nk", [False, True])
-@pytest.mark.parametrize("n", [4096, 6144, 24576])
-def test_mm_every_tile_configuration_same_bits(lib, b_is_nk, n):
+@pytest.mark.parametrize("n,k", CONFIG_SHAPES)
+def test_mm_every_tile_configuration_same_bits(lib, b_is_nk, n, k):
     """A row's addmm output is the same, bit for bit, at an M of each tile
     configuration the shape takes (skinny 32 or 64 rows, the 64x128 and
-    128x128 rings, 128x128, 256x256), at the first and last row, for fp32 and bf16
-    outputs and a ragged K (a 64-tail) -- and it matches the oracle."""
-    k = 1032
+    128x128 rings, 128x128, 256x256, 256x384), at the first and last row, for
+    fp32 and bf16 outputs, with a ragged K (a 64-tail) or whole k tiles -- and
+    it matches the oracle."""
     first = {}
     for m in range(1, 4097):
         first.setdefault(lib.bi_gemm_config(m, n, k, b_is_nk), m)
@@ -153,7 +156,7 @@ def test_mm_every_tile_configuration_same_bits(lib, b_is_nk, n):
 
 def test_every_tile_configuration_is_exercised(lib):
     """The shapes of the test above take every configuration of the table between them."""
-    seen = {lib.bi_gemm_config(m, n, 1032, nk) for n in (4096, 6144, 24576) for nk in (False, True)
+    seen = {lib.bi_gemm_config(m, n, k, nk) for n, k in CONFIG_SHAPES for nk in (False, True)
             for m in range(1, 4097)}
     assert seen == ALL_CONFIGS, seen
 

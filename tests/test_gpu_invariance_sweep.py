@@ -8,9 +8,9 @@ guarantee?"); the property wanted is outputs that do not depend on the batch
 size ("Batch-invariant inference kernels (Thinking Machines) -- Evidence &
 limits", "Rubric assessment"). The GEMM picks its tile configuration from
 (M, N, K), and on the Qwen3-8B projection shapes that choice changes up to
-six times between M = 1 and 4096 (and splits the last columns onto 256x128
-tiles at some M). So every M = 1..4096 is run on each of those shapes, both
-weight layouts, fp32 and bf16 outputs:
+eight times between M = 1 and 4096 (the LM head's also splits its last
+columns onto 256x128 tiles from M = 192). So every M = 1..4096 is run on each
+of the projection shapes, both weight layouts, fp32 and bf16 outputs:
 
 * a fixed row, placed at positions 0, M - 1 and a seeded p, must have the
   bytes it has at M = 1;
