@@ -167,6 +167,113 @@ def source_digest(kernel: str) -> str:
     return h.hexdigest()
 
 
+COUNTER_COMMANDS = [
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/fetch -o run -- python3 bench.py --steps 2 --warmup 1 "
+    "--no-cpu --no-torch --no-e2e",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/write -o run -- python3 bench.py --steps 2 --warmup 1 "
+    "--no-cpu --no-torch --no-e2e",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/cal_fetch -o run -- python3 bench.py --copy-calibration",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/cal_write -o run -- python3 bench.py --copy-calibration",
+    "python3 bench.py --summarize-counters <dir>",
+]
+COPY_BYTES = 256 << 20  # the --copy-calibration copy
+
+
+def step_algorithmic_bytes(S):
+    """Algorithmic bytes per launch group of a step (the Workload's figures,
+    without a GPU: the decode lengths come from the same seeded draw)."""
+    out = {name: gemm_work(M_GEMM, n, k)[1] for name, k, n in GEMMS}
+    out["lm_head"] = gemm_work(M_LM, VOCAB, HIDDEN, bias=True)[1]
+    out["lm_logsm"] = 8.0 * M_LM * VOCAB + 8 * M_LM
+    out["rmsnorm"] = 4.0 * M_ROWS * HIDDEN + 2 * HIDDEN
+    out["mean"] = 2.0 * M_ROWS * HIDDEN + 4 * M_ROWS
+    out["logsm"] = 8.0 * M_ROWS * VOCAB + 8 * M_ROWS
+    lens = S.context_lens(B_DECODE, seed=5000)
+    out["decode_attn"] = (4096.0 * float(lens.sum()) + B_DECODE * 32 * 128 * (2 + 4)
+                          + 4.0 * float(((lens + 15) // 16).sum()))
+    return out
+
+
+def summarize_counters(root: str, out_json: str) -> None:
+    """HBM traffic per launch group from the rocprofv3 FETCH_SIZE and
+    WRITE_SIZE runs under `root` (subfolders fetch, write, cal_fetch,
+    cal_write, as in COUNTER_COMMANDS): every complete step the runs
+    dispatched (the step's kernels in their order, found by name) is averaged
+    per op, scaled by what the same counter reads for a plain copy of
+    COPY_BYTES, and written to `out_json` with each op's source digest; the
+    markdown table goes to stdout."""
+    import csv
+    import glob
+    import statistics
+    import invariant_bi_mm_amd as bi
+    import synthetic as S
+
+    def rows(sub):
+        files = glob.glob(os.path.join(root, sub, "**", "*counter_collection.csv"), recursive=True)
+        if len(files) != 1:
+            raise SystemExit(f"expected one counter_collection.csv under {os.path.join(root, sub)}, found {files}")
+        with open(files[0], newline="") as fh:
+            got = [(int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])) for r in csv.DictReader(fh)]
+        return sorted(got)
+
+    def kib_of_copy(sub):
+        vals = [v for _, name, v in rows(sub) if "copyBuffer" in name]
+        if not vals:
+            raise SystemExit(f"no copy kernel in {sub}")
+        return statistics.median(vals)
+
+    cal = {"copy_kernel": "__amd_rocclr_copyBuffer", "copy_bytes": COPY_BYTES,
+           "copy_FETCH_SIZE_KiB": kib_of_copy("cal_fetch"), "copy_WRITE_SIZE_KiB": kib_of_copy("cal_write")}
+    cal["fetch_scale"] = COPY_BYTES / (cal["copy_FETCH_SIZE_KiB"] * 1024.0)
+    cal["write_scale"] = COPY_BYTES / (cal["copy_WRITE_SIZE_KiB"] * 1024.0)
+
+    # the step's dispatches in order: (op, kernel name fragment)
+    seq = []
+    for name, k, n in GEMMS:
+        seq += [(name, f"gemm_kernel<{p[0]}, {p[1]},") for p in bi.bi_gemm_plan(M_GEMM, n, k)]
+    seq += [("lm_head", f"gemm_kernel<{p[0]}, {p[1]},") for p in bi.bi_gemm_plan(M_LM, VOCAB, HIDDEN)]
+    seq += [("lm_logsm", "log_softmax_kernel"), ("rmsnorm", "rmsnorm_kernel"), ("mean", "mean_kernel"),
+            ("logsm", "log_softmax_kernel"), ("decode_attn", "decode_split_kernel"),
+            ("decode_attn", "decode_combine_kernel")]
+
+    def per_op(sub):
+        ours = [(name, v) for _, name, v in rows(sub) if "bi::" in name]
+        sums, steps, i = {}, 0, 0
+        while i + len(seq) <= len(ours):
+            if all(frag in ours[i + j][0] for j, (_, frag) in enumerate(seq)):
+                for j, (op, _) in enumerate(seq):
+                    sums[op] = sums.get(op, 0.0) + ours[i + j][1]
+                steps += 1
+                i += len(seq)
+            else:
+                i += 1
+        if steps == 0:
+            raise SystemExit(f"no complete step found in {sub}")
+        return {op: v / steps for op, v in sums.items()}, steps
+
+    fetch, nf = per_op("fetch")
+    write, nw = per_op("write")
+    alg = step_algorithmic_bytes(S)
+    kernels = {}
+    print("| op | kernels | fetch MB | write MB | total MB | algorithmic MB | ratio |")
+    print("|---|---|---|---|---|---|---|")
+    for op in dict.fromkeys(o for o, _ in seq):
+        fb = fetch[op] * 1024.0 * cal["fetch_scale"]
+        wb = write[op] * 1024.0 * cal["write_scale"]
+        frags = list(dict.fromkeys(f for o, f in seq if o == op))
+        kernels[op] = {"hbm_fetch_bytes_per_launch": int(round(fb)), "hbm_write_bytes_per_launch": int(round(wb)),
+                       "kernels": frags, "hbm_bytes_per_launch": int(round(fb + wb)),
+                       "source_sha256": source_digest(op), "source": list(KERNEL_SOURCE[op])}
+        print(f"| {op} | {', '.join('`' + f + '`' for f in frags)} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | "
+              f"{(fb + wb) / 1e6:.1f} | {alg[op] / 1e6:.1f} | {(fb + wb) / alg[op]:.2f} |")
+    with open(out_json, "w") as fh:
+        json.dump({"commands": COUNTER_COMMANDS, "calibration": cal, "steps_averaged": {"fetch": nf, "write": nw},
+                   "kernels": kernels}, fh, indent=1)
+        fh.write("\n")
+    log(f"wrote {out_json}: {nf} / {nw} steps averaged; fetch scale {cal['fetch_scale']:.4f}, "
+        f"write scale {cal['write_scale']:.4f}")
+
+
 def time_step(torch, ops, steps, warmup):
     """Run `warmup` untimed steps, then `steps` timed steps bracketed by
     synchronize; every launch group is also bracketed by HIP events on the
@@ -628,7 +735,13 @@ def main():
                          "prints which launch is which and exits")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for scaling the HBM counters) and exit")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="no GPU: turn the rocprofv3 FETCH_SIZE/WRITE_SIZE runs under DIR (fetch/, write/, "
+                         "cal_fetch/, cal_write/) into the --traffic JSON and print the per-op table")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.traffic)
+        return
     if args.copy_calibration:
         import torch
         nbytes = 256 << 20
