@@ -791,7 +791,7 @@ static hipError_t launch_part(const GemmParams& p, const GemmLaunch& L, hipStrea
   // 256x384 assumes whole k tiles and tile columns (no masks); the table
   // picks it only then
   if (cfg.tile_m == 256 && cfg.tile_n == 384 && cfg.waves == 8) {
-    if (p.k % 64 != 0 || a.n % 384 != 0) return hipErrorInvalidConfiguration;
+    if (p.k <= 0 || p.k % 64 != 0 || a.n % 384 != 0) return hipErrorInvalidConfiguration;
     return p.b_is_nk ? launch_cfg<256, 384, 2, 4, true>(a, s) : launch_cfg<256, 384, 2, 4, false>(a, s);
   }
   return hipErrorInvalidConfiguration;

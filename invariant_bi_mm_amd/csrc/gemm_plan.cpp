@@ -83,7 +83,7 @@ GemmConfig gemm_config(int64_t m, int64_t n, int64_t k, bool b_is_nk) {
   // 566 -> 532, M = 4096 691 -> 671 / 702 -> 687; q+kv (N = 6144) at
   // M = 4096, one round of 256 tiles where 256x256 needs 1.5, 184 -> 167 /
   // 184 -> 169 us.
-  if (n % 384 == 0 && k % TK == 0) {
+  if (k > 0 && n % 384 == 0 && k % TK == 0) {  // its loads have no k mask: k == 0 (A, B may be NULL) excluded
     const int64_t t384 = ((m + 255) / 256) * (n / 384);
     if (t384 >= 256 && t384 % 256 == 0) return GemmConfig{256, 384, TK, 8};
   }

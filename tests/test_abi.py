@@ -266,6 +266,8 @@ def test_gemm_config_table(bi):
     assert bi.bi_gemm_config(4096, 24576, 4096)[1] == 384 and bi.bi_gemm_config(4096, 6144, 4096)[1] == 384
     assert bi.bi_gemm_config(1024, 24576, 4096)[1] == 384 and bi.bi_gemm_config(1280, 24576, 4096)[1] == 256
     assert bi.bi_gemm_config(4096, 6144, 4104)[1] != 384 and bi.bi_gemm_config(3840, 6144, 4096)[1] != 384
+    # its loads carry no k mask, so never for k == 0 (where A and B may be NULL)
+    assert bi.bi_gemm_config(4096, 24576, 0)[1] != 384
     with pytest.raises(bi.BiError):
         bi.bi_gemm_config(-1, 4, 4, False)
     assert bi.lib.bi_gemm_config(1, 4, 4, 0, None) == NULL

@@ -125,6 +125,16 @@ def test_mm_k_zero_and_empty(lib):
     e = lib.bi_mm(torch.empty((0, 64), dtype=torch.bfloat16, device=DEV),
                   torch.ones((64, 8), dtype=torch.bfloat16, device=DEV))
     assert e.shape == (0, 8)
+    # k == 0 at a size whose k > 0 form takes the 256x384 tile (no k mask in
+    # its loads): the table must keep such a call on a masked kernel
+    for nk in (False, True):
+        m, n = 1024, 24576
+        assert lib.bi_gemm_config(m, n, 0, nk)[1] != 384 and lib.bi_gemm_config(m, n, 64, nk)[1] == 384
+        a = torch.empty((m, 0), dtype=torch.bfloat16, device=DEV)
+        b = torch.empty((n, 0) if nk else (0, n), dtype=torch.bfloat16, device=DEV)
+        c = torch.full((m, n), 3.0, device=DEV)
+        lib.bi_mm(a, b, out=c, b_is_nk=nk)
+        assert torch.all(c == 0)
 
 
 QWEN = [(4096, 6144), (4096, 4096), (4096, 24576), (12288, 4096)]
