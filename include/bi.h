@@ -114,9 +114,12 @@ bi_status bi_addmm(const void* bias, bi_dtype bias_dtype, float beta, float alph
  * where those fill the CUs in one round), {64, 128, 64, 6} and {128, 128, 64, 10} (the same ring with a
  * 64x128 or 128x128 tile), {128, 128, 64, 4}, {256, 256, 64, 8},
  * {256, 384, 64, 8} (only where k % 64 == 0, n % 384 == 0 and its tiles
- * make whole rounds over the 256 CUs). With {256, 256, 64, 8}, when the
- * last round of tiles over the 256 CUs would be part-empty, the columns
- * past the last full round run as 256x128 tiles in a second launch. The
+ * make whole rounds over the 256 CUs). This is the tile table's entry;
+ * bi_gemm_plan reports the launches: with {256, 256, 64, 8}, when the last
+ * round of tiles over the 256 CUs would be part-empty, either the columns
+ * past the last full round run as 256x128 tiles in a second launch, or
+ * (wide N, e.g. the LM head) the first columns run as 256x384 tiles in
+ * whole rounds and the rest as 256x256 tiles, whichever takes fewer rounds. The
  * choice changes which workgroup computes an element, never how (see
  * bi_mm). Returns BI_ERR_NULL
  * if out4 is NULL, BI_ERR_SHAPE for negative sizes. */
@@ -142,9 +145,10 @@ bi_status bi_gemm(const void* bias, bi_dtype bias_dtype, float beta, float alpha
 
 /* The launches a GEMM of these sizes makes with these flags (no device
  * work): *count (1 or 2) entries of five int32 each in out10,
- * {tile_m, tile_n, tile_k, waves_per_workgroup, first output column}; the
- * second entry, when present, is the 256x128 column split of a 256x256
- * GEMM. Unused entries are zero. BI_ERR_NULL for NULL out10 or count,
+ * {tile_m, tile_n, tile_k, waves_per_workgroup, first output column}; two
+ * entries when a 256x256 GEMM is split over its columns (256x256 then
+ * 256x128, or 256x384 then 256x256; see bi_gemm_config). Unused entries
+ * are zero. BI_ERR_NULL for NULL out10 or count,
  * BI_ERR_SHAPE for negative sizes, BI_ERR_UNSUPPORTED for unknown flags. */
 bi_status bi_gemm_plan(int64_t m, int64_t n, int64_t k, int b_is_nk, int flags, int32_t* out10, int32_t* count);
 

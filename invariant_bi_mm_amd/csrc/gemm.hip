@@ -20,9 +20,10 @@
 //   stream-K or atomic anywhere.
 //
 // Which tile configuration runs is chosen from (M, N, K) -- a skinny kernel
-// for small M (below), 128x128, 256x256 or 256x384 otherwise, 256x256 with
-// its leftover columns on 256x128 tiles when its final round over the CUs
-// would be part-empty -- and, because every configuration runs the chain
+// for small M (below), 128x128, 256x256 or 256x384 otherwise; where a
+// 256x256 GEMM's final round over the CUs would be part-empty, its leftover
+// columns go to 256x128 tiles, or (wide N) its first columns to 256x384
+// tiles in whole rounds -- and, because every configuration runs the chain
 // above, that choice never changes a bit.
 //
 // Structure (one workgroup per TM x TN output tile)

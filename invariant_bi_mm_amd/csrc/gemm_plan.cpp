@@ -126,6 +126,41 @@ static int64_t full_round_columns(int64_t tiles_m, int64_t tiles_n, int64_t m, i
   return split < whole - 0.05 ? n1 : tiles_n;
 }
 
+// Columns of a 256x256 GEMM better taken first by 256x384 tiles, in whole
+// rounds over the CUs, the rest staying on 256x256 tiles (a second launch):
+// a round of 256x384 tiles takes ~1.45 rounds of 256x256 (measured at
+// K = 4096), so for wide N it can cover the columns past the last full
+// 256x256 round for less than a part-empty round costs. Returns 0 (no such
+// split) or the first launch's width, a multiple of 384 that leaves columns
+// to the second; chosen to minimise the predicted rounds, and taken only
+// where that beats the 256x256 plan (`cost_256`, in 256x256 rounds) by more
+// than 0.05. The 256x384 tile's loads have no k mask, so k must be a
+// positive multiple of 64. Only where the last row of tiles is at least 3/4
+// full: 256x256 tiles skip the MFMAs of row blocks past M, the 256x384 ones
+// multiply them as zeros, so with a sparse last row the round count above
+// overstates the 256x256 plan (the LM head at M = 300 508 -> 546 us). Measured
+// on MI355X, the LM head (N = 151936, K = 4096), warm, [K,N] weights: M = 200
+// 352 -> 321 us, 224 356 -> 329, 256 377 -> 350 ([N,K] 377 -> 361; after a
+// read-only flush 372 -> 330), 1000 1150 -> 1117, 1024 1157 -> 1111, 2048
+// 2212 -> 2150, 4096 4317 -> 4180; M = 512 even.
+static int64_t wide_384_columns(int64_t m, int64_t n, int64_t k, double cost_256) {
+  if (k <= 0 || k % TK != 0) return 0;
+  const int64_t tiles_m = (m + 255) / 256;
+  if (m - (tiles_m - 1) * 256 < 192) return 0;
+  const int64_t g = 256 / std::gcd(tiles_m, (int64_t)256);  // tiles_m * c % 256 == 0 iff g divides c
+  int64_t best = 0;
+  double best_cost = cost_256 - 0.05;
+  for (int64_t c = g; 384 * c < n; c += g) {
+    const int64_t rest_tiles = tiles_m * ((n - 384 * c + 255) / 256);
+    const double cost = 1.45 * (double)(tiles_m * c / 256) + (double)((rest_tiles + 255) / 256);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = 384 * c;
+    }
+  }
+  return best;
+}
+
 GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k, bool b_is_nk, bool fixed_tile) {
   GemmPlan plan{};
   const GemmConfig cfg = fixed_tile ? gemm_config_fixed(n, k, b_is_nk) : gemm_config(m, n, k, b_is_nk);
@@ -134,7 +169,15 @@ GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k, bool b_is_nk, bool fixed_til
   if (!fixed_tile && cfg.tile_m == 256 && cfg.tile_n == 256) {
     const int64_t tiles_m = (m + 255) / 256, tiles_n = (n + 255) / 256;
     const int64_t n1 = full_round_columns(tiles_m, tiles_n, m, n);
-    if (n1 < tiles_n) {
+    const double whole = (double)((tiles_m * tiles_n + 255) / 256);
+    const double split = (double)(tiles_m * n1 / 256) +
+                         0.65 * (double)((((m + 255) / 256) * ((n - n1 * 256 + 127) / 128) + 255) / 256);
+    const int64_t w384 = wide_384_columns(m, n, k, n1 < tiles_n ? split : whole);
+    if (w384 > 0) {
+      plan.count = 2;
+      plan.launch[0] = GemmLaunch{GemmConfig{256, 384, TK, 8}, 0, w384};
+      plan.launch[1] = GemmLaunch{cfg, w384, n};
+    } else if (n1 < tiles_n) {
       plan.count = 2;
       plan.launch[0].n_end = n1 * 256;
       plan.launch[1] = GemmLaunch{GemmConfig{256, 128, TK, 8}, n1 * 256, n};

@@ -324,9 +324,15 @@ def test_gemm_plan_and_fixed_tile_mode(bi):
     """bi_gemm_plan reports the launches: the M-keyed table changes its tile
     with M and splits the LM head's columns at M = 256; the fixed-tile mode
     uses one configuration per (N, K, layout) for every M and never splits."""
-    plan = bi.bi_gemm_plan(256, 151936, 4096)
+    plan = bi.bi_gemm_plan(769, 151936, 4096)
     assert len(plan) == 2 and plan[0][:4] == (256, 256, 64, 8) and plan[1][:2] == (256, 128)
     assert plan[0][4] == 0 and plan[1][4] % 256 == 0 and 0 < plan[1][4] < 151936
+    # the LM head at M = 256: 256x384 tiles in one whole round over the CUs, the rest on 256x256
+    plan = bi.bi_gemm_plan(256, 151936, 4096)
+    assert len(plan) == 2 and plan[0][:4] == (256, 384, 64, 8) and plan[1][:4] == (256, 256, 64, 8)
+    assert plan[1][4] == 256 * 384
+    # not with a sparse last row of tiles (256x256 skips rows past M, 256x384 multiplies them)
+    assert len(bi.bi_gemm_plan(300, 151936, 4096)) == 1
     for n, k in ((6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288), (151936, 4096), (512, 512)):
         for nk in (False, True):
             table = {bi.bi_gemm_plan(m, n, k, nk)[0][:4] for m in range(1, 4097, 7)}
@@ -351,8 +357,9 @@ def test_gemm_plan_and_fixed_tile_mode(bi):
 def test_qwen_shapes_walk_every_gemm_configuration(bi):
     """Over M = 1..4096 the four Qwen3-8B projection shapes (either layout)
     take every configuration of the tile table between them, and the LM head
-    over M = 1..256 the 256x128 column split: so the every-M GPU sweeps on
-    those shapes run them all."""
+    over M = 1..256 the split into 256x384 and 256x256 launches: so the
+    every-M GPU sweeps on those shapes run them all. (The 256x128 column
+    split has its own GPU test, test_mm_column_split_same_bits.)"""
     table = {(32, 32, 64, 3), (64, 32, 64, 4), (32, 96, 64, 5), (64, 96, 64, 8), (64, 128, 64, 6), (128, 128, 64, 10),
              (128, 128, 64, 4), (256, 256, 64, 8), (256, 384, 64, 8)}
     seen, split = set(), False
@@ -362,5 +369,5 @@ def test_qwen_shapes_walk_every_gemm_configuration(bi):
             seen |= {p[:4] for p in plan[:1]}
     for m in range(1, 257):
         plan = bi.bi_gemm_plan(m, 151936, 4096)
-        split |= len(plan) == 2 and plan[1][:4] == (256, 128, 64, 8)
+        split |= len(plan) == 2 and plan[0][:2] == (256, 384) and plan[1][:2] == (256, 256)
     assert seen == table and split, (seen, split)

@@ -161,31 +161,20 @@ def test_every_tile_configuration_is_exercised(lib):
     assert seen == ALL_CONFIGS, seen
 
 
-def full_round_columns(m, n):
-    """256-wide tile columns the library leaves to full rounds of 256x256
-    tiles before it covers the rest with 256x128 tiles (the rule in
-    gemm.hip, restated so the test can pick shapes that split)."""
-    import math
-    tm, tn = (m + 255) // 256, (n + 255) // 256
-    g = 256 // math.gcd(tm, 256)
-    n1 = tn // g * g
-    if n1 in (0, tn):
-        return tn
-    tail = (m + 255) // 256 * ((n - n1 * 256 + 127) // 128)
-    split = tm * n1 // 256 + 0.65 * ((tail + 255) // 256)
-    return n1 if split < (tm * tn + 255) // 256 - 0.05 else tn
-
-
 @pytest.mark.parametrize("b_is_nk", [False, True])
-@pytest.mark.parametrize("m,k,n,slab", [(4096, 1032, 6144, 2048), (4096, 1032, 6136, 2048), (256, 4096, 151936, 131072)])
-def test_mm_column_split_same_bits(lib, b_is_nk, m, k, n, slab):
-    """A 256x256 GEMM whose last round over the CUs would be part-empty runs
-    its leftover columns as 256x128 tiles (N = 6136: the last of them ragged,
-    120 columns). Each column block of its output must have the bits of the
-    same block computed on its own (no split), for fp32 and bf16 outputs with
-    a bias, and sampled rows match the oracle."""
-    assert lib.bi_gemm_config(m, n, k, b_is_nk)[:2] == (256, 256)
-    assert full_round_columns(m, n) * 256 < n, "shape does not split"
+@pytest.mark.parametrize("m,k,n,slab,second", [(4096, 1032, 6144, 2048, 128), (4096, 1032, 6136, 2048, 128),
+                                                (769, 4096, 151936, 131072, 128), (256, 4096, 151936, 131072, 256)])
+def test_mm_column_split_same_bits(lib, b_is_nk, m, k, n, slab, second):
+    """A GEMM in two launches over its columns: a 256x256 GEMM whose last
+    round over the CUs would be part-empty runs its leftover columns as
+    256x128 tiles (N = 6136: the last of them ragged, 120 columns), and a wide
+    one (the LM head at M = 256) its first columns as 256x384 tiles in whole
+    rounds and the rest as 256x256 tiles. Each column block of its output
+    must have the bits of the same block computed on its own (other plans),
+    for fp32 and bf16 outputs with a bias, and sampled rows of the second
+    launch's columns match the oracle."""
+    plan = lib.bi_gemm_plan(m, n, k, b_is_nk)
+    assert len(plan) == 2 and plan[1][:2] == (256, second), plan
     w = S.normal_bf16((n, k) if b_is_nk else (k, n), 1 / k, seed=81, device=DEV)
     bias = S.normal_bf16((n,), 0.1, seed=82, device=DEV)
     a = S.normal_bf16((m, k), 1.0, seed=83, device=DEV)
@@ -196,8 +185,8 @@ def test_mm_column_split_same_bits(lib, b_is_nk, m, k, n, slab):
             ws = w[c0:c1] if b_is_nk else w[:, c0:c1]
             part = lib.bi_addmm(bias[c0:c1], a, ws, b_is_nk=b_is_nk, out_dtype=od, beta=0.5, alpha=1.5)
             assert same_bits(full[:, c0:c1], part), (od, c0)
-        if od == torch.float32:  # sampled rows of the 256x128 part against the oracle
-            rows, ct = [0, m // 2 + 1, m - 1], full_round_columns(m, n) * 256
+        if od == torch.float32:  # sampled rows of the second launch's columns against the oracle
+            rows, ct = [0, m // 2 + 1, m - 1], plan[1][4]
             wt = w[ct:] if b_is_nk else w[:, ct:]
             want = 0.5 * O.bf16_bits_to_f64(bits(bias[ct:]))[None] + 1.5 * O.mm(bits(a[rows]), bits(wt), b_is_nk=b_is_nk)
             assert_close(f32(full[rows][:, ct:]), want, "split addmm rows vs oracle")
