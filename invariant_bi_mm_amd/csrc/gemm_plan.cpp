@@ -51,7 +51,8 @@ static GemmConfig skinny_config(int64_t m, int64_t strips) {
 //     faster at M = 384-1024 for N = 4096 and 6144 and at M <= 128 for
 //     N = 24576 (K = 12288 at M = 768-1024: ~5 % slower);
 //   * 256x384 (8 waves, 128x96 each) where K and N are whole tiles and its
-//     tiles make whole rounds over the CUs (gate+up and q+kv at M = 4096);
+//     tiles make whole rounds over the CUs (gate+up at M in 769..1024,
+//     1793..2048, 2817..3072 and 3841..4096; q+kv at M > 3840);
 //   * 256x256 (8 waves, 128x64 each) once its tiles fill the chip (M >= 192,
 //     at least 192 tiles, rounds of 256 at least 70 % full on average):
 //     1.25-1.3x faster than 128x128 at M = 4096 (N = 4096, LM head), 1.1x
@@ -82,7 +83,9 @@ GemmConfig gemm_config(int64_t m, int64_t n, int64_t k, bool b_is_nk) {
   // 211 -> 186 us, M = 2048 363 -> 354 / 363 -> 358, M = 3072 556 -> 520 /
   // 566 -> 532, M = 4096 691 -> 671 / 702 -> 687; q+kv (N = 6144) at
   // M = 4096, one round of 256 tiles where 256x256 needs 1.5, 184 -> 167 /
-  // 184 -> 169 us.
+  // 184 -> 169 us. Also with a sparse last row of tiles, whose rows past M
+  // it multiplies as zeros: gate+up at M = 769 180 -> 169 us, 832 187 -> 170,
+  // 960 190 -> 177; q+kv at M = 3841 185 -> 166 us.
   if (k > 0 && n % 384 == 0 && k % TK == 0) {  // its loads have no k mask: k == 0 (A, B may be NULL) excluded
     const int64_t t384 = ((m + 255) / 256) * (n / 384);
     if (t384 >= 256 && t384 % 256 == 0) return GemmConfig{256, 384, TK, 8};
@@ -116,14 +119,18 @@ GemmConfig gemm_config_fixed(int64_t n, int64_t k, bool b_is_nk) {
 // (384 tiles, 1.5 rounds) 7-8 % faster, gate+up at M = 1024 4-7 %, the LM
 // head at M = 256 (594 tiles) 3-4 %. Both parts compute every element with
 // the chain above, so the bits do not change.
-static int64_t full_round_columns(int64_t tiles_m, int64_t tiles_n, int64_t m, int64_t n) {
+// Also gives the plan's predicted time in 256x256 rounds (*cost).
+static int64_t full_round_columns(int64_t tiles_m, int64_t tiles_n, int64_t n, double* cost) {
+  const double whole = (double)((tiles_m * tiles_n + 255) / 256);
+  *cost = whole;
   const int64_t g = 256 / std::gcd(tiles_m, (int64_t)256);  // tiles_m * n1 % 256 == 0 iff g divides n1
   const int64_t n1 = (tiles_n / g) * g;
   if (n1 == 0 || n1 == tiles_n) return tiles_n;
-  const int64_t t_tail = ((m + 255) / 256) * ((n - n1 * 256 + 127) / 128);
+  const int64_t t_tail = tiles_m * ((n - n1 * 256 + 127) / 128);
   const double split = (double)(tiles_m * n1 / 256) + 0.65 * (double)((t_tail + 255) / 256);
-  const double whole = (double)((tiles_m * tiles_n + 255) / 256);
-  return split < whole - 0.05 ? n1 : tiles_n;
+  if (split >= whole - 0.05) return tiles_n;
+  *cost = split;
+  return n1;
 }
 
 // Columns of a 256x256 GEMM better taken first by 256x384 tiles, in whole
@@ -168,11 +175,9 @@ GemmPlan gemm_plan(int64_t m, int64_t n, int64_t k, bool b_is_nk, bool fixed_til
   plan.launch[0] = GemmLaunch{cfg, 0, n};
   if (!fixed_tile && cfg.tile_m == 256 && cfg.tile_n == 256) {
     const int64_t tiles_m = (m + 255) / 256, tiles_n = (n + 255) / 256;
-    const int64_t n1 = full_round_columns(tiles_m, tiles_n, m, n);
-    const double whole = (double)((tiles_m * tiles_n + 255) / 256);
-    const double split = (double)(tiles_m * n1 / 256) +
-                         0.65 * (double)((((m + 255) / 256) * ((n - n1 * 256 + 127) / 128) + 255) / 256);
-    const int64_t w384 = wide_384_columns(m, n, k, n1 < tiles_n ? split : whole);
+    double cost_256 = 0.0;
+    const int64_t n1 = full_round_columns(tiles_m, tiles_n, n, &cost_256);
+    const int64_t w384 = wide_384_columns(m, n, k, cost_256);
     if (w384 > 0) {
       plan.count = 2;
       plan.launch[0] = GemmLaunch{GemmConfig{256, 384, TK, 8}, 0, w384};
