@@ -157,7 +157,12 @@ static int64_t wide_384_columns(int64_t m, int64_t n, int64_t k, double cost_256
   const int64_t g = 256 / std::gcd(tiles_m, (int64_t)256);  // tiles_m * c % 256 == 0 iff g divides c
   int64_t best = 0;
   double best_cost = cost_256 - 0.05;
-  for (int64_t c = g; 384 * c < n; c += g) {
+  // widths c * 384 with c a multiple of g leaving columns to the second
+  // launch; each step of g adds ~1.45 * tiles_m * g / 256 rounds of 256x384
+  // and removes ~1.5 times as many of 256x256, so the best lies near the
+  // widest: the 64 widest are tried (all of them for every shape here)
+  const int64_t c_max = ((n - 1) / 384 / g) * g;
+  for (int64_t c = c_max; c >= g && c > c_max - 64 * g; c -= g) {
     const int64_t rest_tiles = tiles_m * ((n - 384 * c + 255) / 256);
     const double cost = 1.45 * (double)(tiles_m * c / 256) + (double)((rest_tiles + 255) / 256);
     if (cost < best_cost) {
